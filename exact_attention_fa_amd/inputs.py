@@ -1,0 +1,77 @@
+"""Seeded synthetic inputs shared by the GPU path's tests, the oracle's tests and the benchmark.
+
+This module holds no attention arithmetic. It only draws numbers and rounds them to bfloat16,
+so that the oracle and the HIP kernels consume the very same bf16 values.
+
+Recipe (one stream per slice, so any single head can be regenerated on its own):
+    Generator(PCG64(SeedSequence([seed, tensor_id, b, h]))).standard_normal((N, d), float32)
+then fp32 -> bf16 by round-to-nearest-even on the bit pattern. Tensor ids: Q=0, K=1, V=2, dO=3.
+The values are iid N(0,1), the distribution every workload on the attention pages assumes for
+its synthetic inputs.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+from numpy.random import PCG64, Generator, SeedSequence
+
+TENSOR_ID = {"q": 0, "k": 1, "v": 2, "do": 3}
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """fp32 array -> bf16 bit patterns (uint16), round to nearest, ties to even.
+
+    Finite inputs only (the generators below never draw a non-finite value).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_to_f32(u: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact fp32 values."""
+    u = np.ascontiguousarray(u, dtype=np.uint16)
+    return (u.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_to_f64(u: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact fp64 values."""
+    return bf16_to_f32(u).astype(np.float64)
+
+
+def slice_bf16(seed: int, tensor: str, b: int, h: int, n: int, d: int) -> np.ndarray:
+    """One (b, h) slice [n, d] of a tensor as bf16 bit patterns."""
+    g = Generator(PCG64(SeedSequence([seed, TENSOR_ID[tensor], b, h])))
+    return bf16_round(g.standard_normal((n, d), dtype=np.float32))
+
+
+def tensor_bf16(seed: int, tensor: str, B: int, H: int, n: int, d: int,
+                threads: int | None = None) -> np.ndarray:
+    """The whole [B, H, n, d] tensor as bf16 bit patterns, drawn slice by slice."""
+    out = np.empty((B, H, n, d), dtype=np.uint16)
+
+    def fill(bh: int) -> None:
+        b, h = divmod(bh, H)
+        out[b, h] = slice_bf16(seed, tensor, b, h, n, d)
+
+    nthreads = threads or min(16, os.cpu_count() or 1)
+    if B * H == 1 or nthreads == 1:
+        for bh in range(B * H):
+            fill(bh)
+    else:
+        with ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(fill, range(B * H)))
+    return out
+
+
+def qkv_bf16(seed: int, B: int, H: int, n_q: int, n_k: int, d: int, with_do: bool = False):
+    """Q [B,H,n_q,d], K and V [B,H,n_k,d] (and dO [B,H,n_q,d]) as bf16 bit patterns."""
+    q = tensor_bf16(seed, "q", B, H, n_q, d)
+    k = tensor_bf16(seed, "k", B, H, n_k, d)
+    v = tensor_bf16(seed, "v", B, H, n_k, d)
+    if with_do:
+        return q, k, v, tensor_bf16(seed, "do", B, H, n_q, d)
+    return q, k, v

@@ -1,0 +1,166 @@
+"""Plain CPU fp64 oracle for exact scaled-dot-product attention (forward, backward, decode).
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or execute this module;
+only the tests, the package's smoke check and the benchmark's CPU-baseline leg use it. It shares
+no code with the HIP kernels: it takes plain float arrays and returns fp64 arrays.
+
+Sources. Five web pages on FlashAttention; the arithmetic below follows
+  [MW]  "Bellek Duvarının Fiziği: Standart Attention'dan FlashAttention'a" (webturing Principia):
+        "Attention'ın Cebiri" (the definition S = QK^T/sqrt(d_k), P = row softmax(S), O = PV),
+        "Softmax'ın Kalesi" (softmax with the row maximum subtracted),
+        "O(N²) Çıkmazı" (the standard implementation materialises S and P),
+        "Maskeleme ve Dropout" (causal: query i sees keys j <= i, masked entries are -inf before
+        the row maximum),
+        "Geri Yayılım" (the stored per-row log-sum-exp L, P = exp(S - L), and the softmax
+        gradient identity dsoftmax = p * (dp - <dp>)),
+        "Decode Aşaması: Flash-Decoding" (decode is the same function with one query row).
+  [EN]  "FlashAttention'ı Anlamak Bölüm 1", section 0.2 (notation: Q in R^{N_q x d},
+        K, V in R^{N_k x d}, optional mask/bias added to the scores).
+
+Because FlashAttention computes exact attention (it differs from the textbook only in rounding
+order, [MW] "Online Softmax"), this oracle is the textbook definition written out, not the tiled
+algorithm: it materialises the full score matrix S and probability matrix P of every head, one
+head at a time, in fp64.
+
+Readings where the pages are silent (each also listed in the design notes):
+  * the scale is a caller argument (the pages use 1/sqrt(d_k));
+  * for N_q != N_k the causal mask is aligned bottom-right: key j is visible to query i iff
+    j <= i + N_k - N_q (identical to "j <= i" when N_q == N_k); N_q > N_k is rejected so that
+    no row is empty;
+  * the stored statistic is the natural-log log-sum-exp of the scaled, masked scores,
+    L_i = ln sum_j exp(S_ij);
+  * d_v = d.
+
+Every function here is pinned by tests that do not reuse its formulas: brute-force per-row
+softmax in pure Python, rows of P summing to one, bitwise causal invariance to future keys,
+central finite differences of the gradients, closed forms (Q = 0, one key, first causal row),
+shift and permutation invariances, gradient sum rules, and agreement with PyTorch's CPU
+scaled_dot_product_attention and autograd in float64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Rows of one head processed together. Rows are independent, so splitting them changes no
+# arithmetic on any row; it only bounds host memory for long sequences (N_q * N_k large).
+_ROW_BLOCK_ELEMS = 1 << 26
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def visible(n_q: int, n_k: int, causal: bool) -> np.ndarray:
+    """Boolean [n_q, n_k]: True where key j may be attended by query i.
+
+    [MW] "Maskeleme ve Dropout": under the causal mask query i sees only keys j <= i.
+    With N_q < N_k the queries are taken to be the last N_q positions (bottom-right).
+    """
+    if causal and n_q > n_k:
+        raise ValueError("causal attention needs n_q <= n_k")
+    if not causal:
+        return np.ones((n_q, n_k), dtype=bool)
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    return j <= i + (n_k - n_q)
+
+
+def scores(q, k, scale: float, causal: bool, rows=None) -> np.ndarray:
+    """S = scale * Q K^T with masked entries set to -inf, for one head ([MW] "Attention'ın Cebiri").
+
+    q: [n_q, d], k: [n_k, d]. `rows` selects a subset of query rows (default: all).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    n_q, n_k = q.shape[0], k.shape[0]
+    rows = np.arange(n_q) if rows is None else np.asarray(rows)
+    s = scale * (q[rows] @ k.T)
+    mask = visible(n_q, n_k, causal)[rows]
+    s[~mask] = -np.inf
+    return s
+
+
+def softmax_rows(s: np.ndarray):
+    """Row softmax with the row maximum subtracted ([MW] "Softmax'ın Kalesi").
+
+    Returns (P, L) with P_ij = exp(S_ij - m_i) / sum_j exp(S_ij - m_i) and the log-sum-exp
+    L_i = m_i + ln sum_j exp(S_ij - m_i) ([MW] "Geri Yayılım"). Every row must hold at least
+    one finite score.
+    """
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = np.sum(e, axis=1, keepdims=True)
+    p = e / z
+    lse = (m + np.log(z))[:, 0]
+    return p, lse
+
+
+def forward_head(q, k, v, scale: float, causal: bool, rows=None):
+    """O = P V and L for one head; q [n_q, d], k/v [n_k, d]. Returns (o [r, d], lse [r])."""
+    v = _f64(v)
+    n_q, n_k = np.shape(q)[0], np.shape(k)[0]
+    rows = np.arange(n_q) if rows is None else np.asarray(rows)
+    block = max(1, _ROW_BLOCK_ELEMS // max(1, n_k))
+    o = np.empty((len(rows), v.shape[1]), dtype=np.float64)
+    lse = np.empty(len(rows), dtype=np.float64)
+    for r0 in range(0, len(rows), block):
+        sel = rows[r0:r0 + block]
+        p, l_ = softmax_rows(scores(q, k, scale, causal, sel))
+        o[r0:r0 + len(sel)] = p @ v
+        lse[r0:r0 + len(sel)] = l_
+    return o, lse
+
+
+def forward(q, k, v, scale: float, causal: bool):
+    """Batched forward: q [B,H,n_q,d], k/v [B,H,n_k,d] -> (o [B,H,n_q,d], lse [B,H,n_q])."""
+    B, H, n_q, d = np.shape(q)
+    o = np.empty((B, H, n_q, np.shape(v)[3]), dtype=np.float64)
+    lse = np.empty((B, H, n_q), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h], v[b, h], scale, causal)
+    return o, lse
+
+
+def backward_head(q, k, v, do, scale: float, causal: bool):
+    """Gradients of O with respect to Q, K, V for one head, by the textbook chain rule.
+
+    [MW] "Geri Yayılım": with P materialised, dV = P^T dO; dP = dO V^T; the softmax gradient
+    identity gives dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik); and since S = scale * Q K^T,
+    dQ = scale * dS K and dK = scale * dS^T Q. The row term is taken from P and dP here, not
+    from rowsum(dO * O), so that it is independent of the GPU's preprocess.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    p, _ = softmax_rows(scores(q, k, scale, causal))
+    dv = p.T @ do
+    dp = do @ v.T
+    row = np.sum(p * dp, axis=1, keepdims=True)
+    ds = p * (dp - row)
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def backward(q, k, v, do, scale: float, causal: bool):
+    """Batched backward: returns (dq, dk, dv) shaped like (q, k, v), fp64."""
+    B, H = np.shape(q)[:2]
+    dq = np.empty(np.shape(q), dtype=np.float64)
+    dk = np.empty(np.shape(k), dtype=np.float64)
+    dv = np.empty(np.shape(v), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            dq[b, h], dk[b, h], dv[b, h] = backward_head(q[b, h], k[b, h], v[b, h], do[b, h],
+                                                         scale, causal)
+    return dq, dk, dv
+
+
+def decode(q, k, v, scale: float):
+    """Decode step: one query row per (b, h) against the whole KV cache.
+
+    [MW] "Decode Aşaması: Flash-Decoding": the split-KV scheme computes the same function as
+    the forward pass with a single query, so the oracle is the forward with n_q = 1 and no split.
+    q [B,H,1,d], k/v [B,H,n_k,d] -> (o [B,H,1,d], lse [B,H,1]).
+    """
+    if np.shape(q)[2] != 1:
+        raise ValueError("decode takes exactly one query row per (b, h)")
+    return forward(q, k, v, scale, causal=False)

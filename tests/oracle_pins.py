@@ -1,0 +1,252 @@
+"""Pins for the CPU oracle: checks that tie it to something other than itself.
+
+Each pin reads the oracle through the module object at call time, so a test can plant a
+mistake in the oracle (monkeypatching one of its functions) and confirm that some pin fails.
+
+Page: "Bellek Duvarının Fiziği" (webturing Principia). Sections used: "Attention'ın Cebiri"
+(definition), "Softmax'ın Kalesi" (stable softmax), "Maskeleme ve Dropout" (causal mask),
+"Geri Yayılım" (LSE and gradients), "Decode Aşaması: Flash-Decoding" (split and combine).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle.attention as A
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _head(rng, n_q, n_k, d):
+    return (rng.standard_normal((n_q, d)), rng.standard_normal((n_k, d)),
+            rng.standard_normal((n_k, d)))
+
+
+TINY_SHAPES = [(1, 1, 4), (3, 3, 4), (5, 5, 8), (8, 8, 8), (3, 7, 4), (2, 9, 8)]
+
+
+def pin_brute_force_rows():
+    """Per-row softmax written as direct loops with math.exp (spec check (i))."""
+    rng = _rng(1)
+    for n_q, n_k, d in TINY_SHAPES:
+        for causal in (False, True):
+            q, k, v = _head(rng, n_q, n_k, d)
+            scale = 1.0 / math.sqrt(d)
+            o, lse = A.forward_head(q, k, v, scale, causal)
+            for i in range(n_q):
+                horizon = i + n_k - n_q if causal else n_k - 1
+                s = [scale * sum(q[i, t] * k[j, t] for t in range(d)) for j in range(horizon + 1)]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                z = sum(w)
+                for t in range(d):
+                    ref = sum(w[j] * v[j, t] for j in range(len(w))) / z
+                    assert abs(o[i, t] - ref) <= 1e-12 * (1 + abs(ref)), (n_q, n_k, d, causal, i, t)
+                assert abs(lse[i] - (mx + math.log(z))) <= 1e-12 * (1 + abs(lse[i]))
+
+
+def pin_rows_sum_to_one():
+    """Rows of P sum to 1 and P = exp(S - L) (spec check (ii), and the backward's
+    recomputation identity)."""
+    rng = _rng(2)
+    for n_q, n_k, d in TINY_SHAPES + [(64, 64, 16), (17, 40, 8)]:
+        for causal in (False, True):
+            q, k, _ = _head(rng, n_q, n_k, d)
+            s = A.scores(q, k, 0.3, causal)
+            p, lse = A.softmax_rows(s)
+            assert np.all(np.abs(p.sum(axis=1) - 1.0) <= 1e-14)
+            assert np.all(p >= 0)
+            np.testing.assert_allclose(np.exp(s - lse[:, None]), p, rtol=1e-12, atol=1e-15)
+            # masked entries carry zero probability
+            assert np.all(p[~A.visible(n_q, n_k, causal)] == 0.0)
+
+
+def pin_causal_future_invariance():
+    """Redrawing K_j, V_j beyond row i's horizon leaves O_i and L_i bitwise unchanged
+    (spec check (iii)); also the first causal row has a closed form."""
+    rng = _rng(3)
+    for n_q, n_k, d in [(6, 6, 4), (5, 9, 8), (16, 16, 8)]:
+        q, k, v = _head(rng, n_q, n_k, d)
+        o, lse = A.forward_head(q, k, v, 0.5, True)
+        for i in range(n_q):
+            horizon = i + n_k - n_q
+            k2, v2 = k.copy(), v.copy()
+            k2[horizon + 1:] = rng.standard_normal(k2[horizon + 1:].shape) * 7.0
+            v2[horizon + 1:] = rng.standard_normal(v2[horizon + 1:].shape) * 7.0
+            o2, lse2 = A.forward_head(q, k2, v2, 0.5, True)
+            assert np.array_equal(o2[i], o[i]) and lse2[i] == lse[i], (n_q, n_k, i)
+        # square causal: row 0 sees key 0 only
+        if n_q == n_k:
+            np.testing.assert_allclose(o[0], v[0], rtol=0, atol=1e-15)
+            assert abs(lse[0] - 0.5 * float(q[0] @ k[0])) <= 1e-14
+
+
+def _f(q, k, v, do, scale, causal):
+    o, _ = A.forward_head(q, k, v, scale, causal)
+    return float(np.sum(do * o))
+
+
+def pin_finite_differences():
+    """Central differences of f = sum(dO * O) against dQ, dK, dV (spec check (iv))."""
+    rng = _rng(4)
+    h = 1e-6
+    for n_q, n_k, d, causal in [(3, 3, 4, False), (4, 4, 3, True), (3, 5, 2, True), (2, 4, 3, False)]:
+        q, k, v = _head(rng, n_q, n_k, d)
+        do = rng.standard_normal((n_q, d))
+        scale = 0.7
+        dq, dk, dv = A.backward_head(q, k, v, do, scale, causal)
+        for x, g in ((q, dq), (k, dk), (v, dv)):
+            num = np.empty_like(x)
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + h
+                fp = _f(q, k, v, do, scale, causal)
+                x[idx] = old - h
+                fm = _f(q, k, v, do, scale, causal)
+                x[idx] = old
+                num[idx] = (fp - fm) / (2 * h)
+            err = np.linalg.norm(num - g) / max(np.linalg.norm(num), 1e-300)
+            assert err <= 1e-6, (n_q, n_k, d, causal, err)
+
+
+def pin_closed_forms():
+    """Q = 0: uniform weights over the visible keys, L = ln(#visible). One key: O = V_0 and
+    L = scale * q.k_0. All V rows equal: every O row equals that row."""
+    rng = _rng(5)
+    for n_q, n_k, d in [(4, 4, 8), (3, 7, 4), (16, 16, 16)]:
+        for causal in (False, True):
+            _, k, v = _head(rng, n_q, n_k, d)
+            q = np.zeros((n_q, d))
+            o, lse = A.forward_head(q, k, v, 0.25, causal)
+            vis = A.visible(n_q, n_k, causal)
+            for i in range(n_q):
+                cnt = int(vis[i].sum())
+                np.testing.assert_allclose(o[i], v[vis[i]].mean(axis=0), rtol=1e-12, atol=1e-13)
+                assert abs(lse[i] - math.log(cnt)) <= 1e-13
+    for n_q, d in [(1, 4), (5, 8)]:
+        q, k, v = _head(rng, n_q, 1, d)
+        o, lse = A.forward_head(q, k, v, 0.3, False)
+        np.testing.assert_allclose(o, np.repeat(v, n_q, axis=0), rtol=0, atol=1e-15)
+        np.testing.assert_allclose(lse, 0.3 * (q @ k[0]), rtol=1e-14, atol=1e-15)
+    q, k, _ = _head(rng, 9, 9, 4)
+    v = np.tile(rng.standard_normal((1, 4)), (9, 1))
+    o, _ = A.forward_head(q, k, v, 1.0, True)
+    np.testing.assert_allclose(o, v, rtol=1e-13, atol=1e-14)
+
+
+def pin_invariances():
+    """Shifting every key by u leaves O unchanged and adds scale * q_i.u to L_i; permuting keys
+    and values together leaves O and L unchanged (non-causal); scaling V scales O."""
+    rng = _rng(6)
+    for n_q, n_k, d in [(5, 5, 4), (4, 11, 8)]:
+        q, k, v = _head(rng, n_q, n_k, d)
+        scale = 0.4
+        for causal in (False, True):
+            o, lse = A.forward_head(q, k, v, scale, causal)
+            u = rng.standard_normal(d)
+            o2, lse2 = A.forward_head(q, k + u, v, scale, causal)
+            np.testing.assert_allclose(o2, o, rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(lse2, lse + scale * (q @ u), rtol=1e-11, atol=1e-12)
+            o3, _ = A.forward_head(q, k, 3.0 * v, scale, causal)
+            np.testing.assert_allclose(o3, 3.0 * o, rtol=1e-12, atol=1e-12)
+        perm = rng.permutation(n_k)
+        o, lse = A.forward_head(q, k, v, scale, False)
+        o2, lse2 = A.forward_head(q, k[perm], v[perm], scale, False)
+        np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse2, lse, rtol=1e-12, atol=1e-13)
+
+
+def pin_gradient_sum_rules():
+    """Every row of dS sums to zero, so sum_j dK_j = 0; rows of P sum to one, so
+    sum_j dV_j = sum_i dO_i; dO = 0 gives zero gradients; and rowsum(P * dP) equals
+    rowsum(dO * O), the D the GPU backward uses."""
+    rng = _rng(7)
+    for n_q, n_k, d in [(6, 6, 4), (4, 9, 8), (32, 32, 16)]:
+        for causal in (False, True):
+            q, k, v = _head(rng, n_q, n_k, d)
+            do = rng.standard_normal((n_q, d))
+            dq, dk, dv = A.backward_head(q, k, v, do, 0.5, causal)
+            scale_k = np.linalg.norm(dk) + 1.0
+            assert np.linalg.norm(dk.sum(axis=0)) <= 1e-12 * scale_k * n_k
+            np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), rtol=1e-12, atol=1e-12)
+            z = A.backward_head(q, k, v, np.zeros_like(do), 0.5, causal)
+            assert all(np.all(g == 0) for g in z)
+            o, _ = A.forward_head(q, k, v, 0.5, causal)
+            p, _ = A.softmax_rows(A.scores(q, k, 0.5, causal))
+            np.testing.assert_allclose(np.sum(p * (do @ v.T), axis=1), np.sum(do * o, axis=1),
+                                       rtol=1e-12, atol=1e-12)
+
+
+def pin_torch_sdpa():
+    """Agreement with PyTorch's CPU scaled_dot_product_attention and its autograd in float64,
+    an implementation written independently of this oracle; the log-sum-exp against
+    torch.logsumexp of the masked scores."""
+    import torch
+    rng = _rng(8)
+    for n_q, n_k, d in [(7, 7, 8), (5, 12, 16), (33, 33, 8)]:
+        for causal in (False, True):
+            q, k, v = _head(rng, n_q, n_k, d)
+            do = rng.standard_normal((n_q, d))
+            scale = 1.0 / math.sqrt(d)
+            tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+            mask = torch.tensor(np.tril(np.ones((n_q, n_k), dtype=bool), k=n_k - n_q)) if causal else None
+            to = torch.nn.functional.scaled_dot_product_attention(
+                tq[None], tk[None], tv[None], attn_mask=mask, scale=scale)[0]
+            to.backward(torch.tensor(do))
+            o, lse = A.forward_head(q, k, v, scale, causal)
+            np.testing.assert_allclose(o, to.detach().numpy(), rtol=1e-12, atol=1e-13)
+            s = (tq.detach() @ tk.detach().T) * scale
+            if causal:
+                s = s.masked_fill(~mask, float("-inf"))
+            np.testing.assert_allclose(lse, torch.logsumexp(s, dim=1).numpy(), rtol=1e-13, atol=1e-13)
+            dq, dk, dv = A.backward_head(q, k, v, do, scale, causal)
+            np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def pin_hand_examples():
+    """Values derived by hand from the definition, stored under tests/golden."""
+    with open(os.path.join(GOLDEN, "hand_examples.json")) as f:
+        fx = json.load(f)
+    for c in fx["cases"]:
+        q, k, v, do = (np.array(c[x], dtype=np.float64) for x in ("q", "k", "v", "do"))
+        o, lse = A.forward_head(q, k, v, c["scale"], c["causal"])
+        np.testing.assert_allclose(o, c["o"], rtol=1e-14, atol=1e-14, err_msg=c["name"])
+        np.testing.assert_allclose(lse, c["lse"], rtol=1e-14, atol=1e-14, err_msg=c["name"])
+        dq, dk, dv = A.backward_head(q, k, v, do, c["scale"], c["causal"])
+        for got, key in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+            np.testing.assert_allclose(got, c[key], rtol=1e-13, atol=1e-14, err_msg=c["name"] + key)
+
+
+def pin_decode_split_combine():
+    """Decode equals the forward with one query row, and combining per-chunk results with the
+    Flash-Decoding reduction (L = ln sum_c e^{L_c}, O = sum_c e^{L_c - L} O_c) equals the whole."""
+    rng = _rng(9)
+    B, H, n_k, d = 2, 3, 37, 8
+    q = rng.standard_normal((B, H, 1, d))
+    k = rng.standard_normal((B, H, n_k, d))
+    v = rng.standard_normal((B, H, n_k, d))
+    o, lse = A.decode(q, k, v, 0.35)
+    of, lsef = A.forward(q, k, v, 0.35, False)
+    assert np.array_equal(o, of) and np.array_equal(lse, lsef)
+    for chunks in ([0, 37], [0, 10, 37], [0, 1, 2, 20, 36, 37]):
+        parts = [A.forward(q, k[:, :, a:b], v[:, :, a:b], 0.35, False) for a, b in zip(chunks, chunks[1:])]
+        ls = np.stack([p[1][..., 0] for p in parts])
+        m = ls.max(axis=0)
+        L = m + np.log(np.sum(np.exp(ls - m), axis=0))
+        O = sum(np.exp(p[1][..., 0] - L)[..., None, None] * p[0] for p in parts)
+        np.testing.assert_allclose(O, o, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(L, lse[..., 0], rtol=1e-14, atol=1e-14)
+
+
+ALL_PINS = [pin_brute_force_rows, pin_rows_sum_to_one, pin_causal_future_invariance,
+            pin_finite_differences, pin_closed_forms, pin_invariances, pin_gradient_sum_rules,
+            pin_torch_sdpa, pin_hand_examples, pin_decode_split_combine]

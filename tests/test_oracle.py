@@ -1,0 +1,156 @@
+"""The CPU oracle against its pins, and planted mistakes in the oracle that the pins must catch."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as A
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+def test_batched_matches_per_head():
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((2, 3, 9, 8))
+    k = rng.standard_normal((2, 3, 13, 8))
+    v = rng.standard_normal((2, 3, 13, 8))
+    do = rng.standard_normal((2, 3, 9, 8))
+    o, lse = oracle.forward(q, k, v, 0.3, True)
+    dq, dk, dv = oracle.backward(q, k, v, do, 0.3, True)
+    for b in range(2):
+        for h in range(3):
+            oh, lh = oracle.forward_head(q[b, h], k[b, h], v[b, h], 0.3, True)
+            assert np.array_equal(oh, o[b, h]) and np.array_equal(lh, lse[b, h])
+            gh = oracle.backward_head(q[b, h], k[b, h], v[b, h], do[b, h], 0.3, True)
+            for x, y in zip(gh, (dq[b, h], dk[b, h], dv[b, h])):
+                assert np.array_equal(x, y)
+
+
+def test_row_subset_and_row_blocks(monkeypatch):
+    """Rows computed alone, or in small row blocks, agree with the whole head."""
+    rng = np.random.default_rng(12)
+    q, k, v = (rng.standard_normal((40, 8)), rng.standard_normal((50, 8)), rng.standard_normal((50, 8)))
+    o, lse = oracle.forward_head(q, k, v, 0.4, True)
+    rows = np.array([0, 7, 39])
+    o2, lse2 = oracle.forward_head(q, k, v, 0.4, True, rows=rows)
+    np.testing.assert_allclose(o2, o[rows], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lse2, lse[rows], rtol=1e-14, atol=1e-15)
+    monkeypatch.setattr(A, "_ROW_BLOCK_ELEMS", 3 * 50)
+    o3, lse3 = oracle.forward_head(q, k, v, 0.4, True)
+    np.testing.assert_allclose(o3, o, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lse3, lse, rtol=1e-14, atol=1e-15)
+
+
+def test_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        oracle.visible(5, 4, True)
+    with pytest.raises(ValueError):
+        oracle.decode(np.zeros((1, 1, 2, 4)), np.zeros((1, 1, 3, 4)), np.zeros((1, 1, 3, 4)), 1.0)
+
+
+# ---- planted mistakes (in the oracle, on the CPU): each one must make some pin fail ----------
+
+_orig_scores = A.scores
+_orig_softmax = A.softmax_rows
+_orig_visible = A.visible
+
+
+def _scores_no_scale(q, k, scale, causal, rows=None):
+    return _orig_scores(q, k, 1.0, causal, rows)
+
+
+def _scores_transposed(q, k, scale, causal, rows=None):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    s = scale * (k @ q.T)
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    s = s[rows]
+    s[~_orig_visible(q.shape[0], k.shape[0], causal)[rows]] = -np.inf
+    return s
+
+
+def _visible_off_by_one(n_q, n_k, causal):
+    if not causal:
+        return np.ones((n_q, n_k), dtype=bool)
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    return j <= i + (n_k - n_q) + 1
+
+
+def _visible_top_left(n_q, n_k, causal):
+    if not causal:
+        return np.ones((n_q, n_k), dtype=bool)
+    return np.arange(n_k)[None, :] <= np.arange(n_q)[:, None]
+
+
+def _softmax_lse_without_max(s):
+    p, lse = _orig_softmax(s)
+    m = np.max(s, axis=1)
+    return p, lse - m
+
+
+def _softmax_columns(s):
+    m = np.max(s, axis=0, keepdims=True)
+    e = np.exp(s - m)
+    z = np.sum(e, axis=0, keepdims=True)
+    return e / z, (m + np.log(z))[0, : s.shape[0]] if s.shape[0] <= s.shape[1] else np.zeros(s.shape[0])
+
+
+def _bwd_factory(variant):
+    def bwd(q, k, v, do, scale, causal):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        p, _ = A.softmax_rows(A.scores(q, k, scale, causal))
+        dv = p.T @ do
+        dp = do @ v.T
+        row = np.sum(p * dp, axis=1, keepdims=True)
+        ds = p * (dp - row)
+        dq = scale * (ds @ k)
+        dk = scale * (ds.T @ q)
+        if variant == "no_row_term":
+            ds = p * dp
+            dq, dk = scale * (ds @ k), scale * (ds.T @ q)
+        elif variant == "sign":
+            ds = p * (row - dp)
+            dq, dk = scale * (ds @ k), scale * (ds.T @ q)
+        elif variant == "dk_no_scale":
+            dk = ds.T @ q
+        elif variant == "dv_no_transpose":
+            dv = (p @ do) if p.shape[0] == p.shape[1] else dv * 0.5
+        elif variant == "dq_uses_v":
+            dq = scale * (ds @ v)
+        return dq, dk, dv
+    return bwd
+
+
+MUTANTS = {
+    "scores_no_scale": ("scores", _scores_no_scale),
+    "scores_transposed": ("scores", _scores_transposed),
+    "mask_off_by_one": ("visible", _visible_off_by_one),
+    "mask_top_left": ("visible", _visible_top_left),
+    "lse_without_max": ("softmax_rows", _softmax_lse_without_max),
+    "softmax_over_columns": ("softmax_rows", _softmax_columns),
+    "bwd_no_row_term": ("backward_head", _bwd_factory("no_row_term")),
+    "bwd_sign": ("backward_head", _bwd_factory("sign")),
+    "bwd_dk_no_scale": ("backward_head", _bwd_factory("dk_no_scale")),
+    "bwd_dv_no_transpose": ("backward_head", _bwd_factory("dv_no_transpose")),
+    "bwd_dq_uses_v": ("backward_head", _bwd_factory("dq_uses_v")),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(A, attr, fn)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except Exception:  # an assertion, or the mistake breaking a shape
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
