@@ -1,0 +1,163 @@
+"""ctypes binding of libfa.so (the C ABI declared in include/fa.h).
+
+Argument marshalling only: torch provides device memory and the current HIP stream, and every
+step of the computation runs in the library's kernels. There is no fallback: if the library is
+missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_ALIGN",
+          5: "FA_ERR_CAUSAL", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_SCALE", 8: "FA_ERR_ARG",
+          9: "FA_ERR_HIP"}
+
+# Every entry point include/fa.h declares: name -> (restype, argtypes)
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "fa_status_string": (ctypes.c_char_p, [_I]),
+    "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_decode_num_splits": (_I, [_I, _I, _I, _I]),
+    "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m exact_attention_fa_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise FaError(fn, status)
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t, name: str, shape, dtype) -> None:
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on a GPU")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _scale(scale, d: int) -> float:
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None):
+    """O and LSE of exact attention. q [B,H,Nq,d], k/v [B,H,Nk,d] bf16 -> (o bf16, lse fp32)."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _need(q, "q", (B, H, Nq, d), torch.bfloat16)
+    _need(k, "k", (B, H, Nk, d), torch.bfloat16)
+    _need(v, "v", (B, H, Nk, d), torch.bfloat16)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _need(o, "o", (B, H, Nq, d), torch.bfloat16)
+        _need(lse, "lse", (B, H, Nq), torch.float32)
+    st = load().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       B, H, Nq, Nk, d, _scale(scale, d), int(bool(causal)), _stream(q))
+    _check("fa_fwd", st)
+    return o, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load().fa_bwd_workspace_bytes(B, H, Nq, Nk, d))
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+        workspace=None, out=None):
+    """Gradients (dq, dk, dv) of exact attention by recomputation from the stored LSE."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for t, n, shp in ((q, "q", (B, H, Nq, d)), (k, "k", (B, H, Nk, d)), (v, "v", (B, H, Nk, d)),
+                      (o, "o", (B, H, Nq, d)), (dout, "dout", (B, H, Nq, d))):
+        _need(t, n, shp, torch.bfloat16)
+    _need(lse, "lse", (B, H, Nq), torch.float32)
+    nbytes = bwd_workspace_bytes(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    st = load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                       B, H, Nq, Nk, d, _scale(scale, d), int(bool(causal)), _stream(q))
+    _check("fa_bwd", st)
+    return dq, dk, dv
+
+
+def decode_num_splits(B: int, H: int, Nk: int, d: int) -> int:
+    return int(load().fa_decode_num_splits(B, H, Nk, d))
+
+
+def decode_workspace_bytes(B: int, H: int, Nk: int, d: int, num_splits: int = 0) -> int:
+    return int(load().fa_decode_workspace_bytes(B, H, Nk, d, num_splits))
+
+
+def decode(q, k, v, scale: float | None = None, num_splits: int = 0, workspace=None, out=None):
+    """One decode step: q [B,H,1,d] against k/v [B,H,Nk,d] -> (o [B,H,1,d] bf16, lse [B,H,1])."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _need(q, "q", (B, H, Nq, d), torch.bfloat16)
+    _need(k, "k", (B, H, Nk, d), torch.bfloat16)
+    _need(v, "v", (B, H, Nk, d), torch.bfloat16)
+    nbytes = decode_workspace_bytes(B, H, Nk, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    st = load().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          B, H, Nq, Nk, d, _scale(scale, d), 0, int(num_splits), _stream(q))
+    _check("fa_decode", st)
+    return o, lse

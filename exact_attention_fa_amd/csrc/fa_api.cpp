@@ -1,0 +1,122 @@
+// C ABI of the attention library: argument validation, workspace sizing and dispatch.
+// Every check runs before anything is enqueued, so an error leaves the outputs untouched.
+#include "fa.h"
+
+#include <math.h>
+
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+fa_status check_common(int B, int H, int Nq, int Nk, int d, float scale, int causal) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  const long long bh = (long long)B * H;
+  if (bh * Nq >= (1LL << 31) || bh * Nk >= (1LL << 31)) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (causal && Nq > Nk) return FA_ERR_CAUSAL;
+  return FA_OK;
+}
+
+fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+const __bf16* bf(const fa_bf16* p) { return reinterpret_cast<const __bf16*>(p); }
+__bf16* bf(fa_bf16* p) { return reinterpret_cast<__bf16*>(p); }
+
+size_t round_up16(size_t n) { return (n + 15) & ~size_t(15); }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: a size is < 1 or an index range is too large";
+    case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension must be 64 or 128";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: pointers must be 16-byte aligned";
+    case FA_ERR_CAUSAL: return "FA_ERR_CAUSAL: causal attention needs N_q <= N_k";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case FA_ERR_ARG: return "FA_ERR_ARG: argument out of range";
+    case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+fa_status fa_fwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+                 int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                 hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status s = check_common(B, H, N_q, N_k, d, scale, causal);
+  if (s != FA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a{bf(q), bf(k), bf(v), bf(o), lse, B, H, N_q, N_k, d, scale, causal != 0, stream};
+  return from_hip(fa::launch_fwd(a));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d) {
+  (void)N_k;
+  (void)d;
+  if (B < 1 || H < 1 || N_q < 1) return 0;
+  return round_up16((size_t)B * H * N_q * sizeof(float));
+}
+
+fa_status fa_bwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                 const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+                 void* workspace, size_t workspace_bytes, int B, int H, int N_q, int N_k, int d,
+                 float scale, int causal, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  fa_status s = check_common(B, H, N_q, N_k, d, scale, causal);
+  if (s != FA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, N_q, N_k, d))
+    return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  fa::BwdArgs a{bf(q), bf(k), bf(v), bf(o), lse, bf(dout), bf(dq), bf(dk), bf(dv),
+                static_cast<float*>(workspace), B, H, N_q, N_k, d, scale, causal != 0, stream};
+  return from_hip(fa::launch_bwd(a));
+}
+
+int fa_decode_num_splits(int B, int H, int N_k, int d) {
+  if (B < 1 || H < 1 || N_k < 1) return 1;
+  return fa::decode_auto_splits(B, H, N_k, d);
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int N_k, int d, int num_splits) {
+  if (B < 1 || H < 1 || N_k < 1 || (d != 64 && d != 128) || num_splits < 0) return 0;
+  const int c = num_splits == 0 ? fa_decode_num_splits(B, H, N_k, d) : num_splits;
+  const size_t rows = (size_t)B * H * c;
+  return round_up16(rows * d * sizeof(float)) + round_up16(rows * sizeof(float));
+}
+
+fa_status fa_decode(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+                    void* workspace, size_t workspace_bytes, int B, int H, int N_q, int N_k,
+                    int d, float scale, int causal, int num_splits, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status s = check_common(B, H, N_q, N_k, d, scale, causal);
+  if (s != FA_OK) return s;
+  if (N_q != 1) return FA_ERR_ARG;
+  if (num_splits < 0 || num_splits > 1024 || num_splits > N_k) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const int c = num_splits == 0 ? fa_decode_num_splits(B, H, N_k, d) : num_splits;
+  if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, H, N_k, d, c))
+    return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  const size_t rows = (size_t)B * H * c;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             round_up16(rows * d * sizeof(float)));
+  fa::DecodeArgs a{bf(q), bf(k), bf(v), bf(o), lse, part_o, part_lse, B, H, N_k, d, c, scale,
+                   stream};
+  return from_hip(fa::launch_decode(a));
+}
+
+}  // extern "C"

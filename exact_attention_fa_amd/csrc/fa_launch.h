@@ -1,0 +1,58 @@
+// Host-side launch entry points of the attention kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float* lse;
+  int B, H, Nq, Nk, d;
+  float scale;
+  bool causal;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* o;
+  const float* lse;
+  const __bf16* dout;
+  __bf16* dq;
+  __bf16* dk;
+  __bf16* dv;
+  float* delta;  // workspace: D = rowsum(dO * O), [B, H, Nq]
+  int B, H, Nq, Nk, d;
+  float scale;
+  bool causal;
+  hipStream_t stream;
+};
+
+struct DecodeArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float* lse;
+  float* part_o;    // workspace: [B, H, splits, d]
+  float* part_lse;  // workspace: [B, H, splits]
+  int B, H, Nk, d, splits;
+  float scale;
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
+
+// Split count used by the decode when the caller passes 0.
+int decode_auto_splits(int B, int H, int Nk, int d);
+
+}  // namespace fa

@@ -1,0 +1,122 @@
+/*
+ * fa.h - C ABI of an MI355X (gfx950) exact-attention library: fused forward, backward by
+ * recomputation, and split-KV decoding, for bfloat16 tensors on one GPU.
+ *
+ * What is computed (page "Bellek Duvarının Fiziği: Standart Attention'dan FlashAttention'a",
+ * section "Attention'ın Cebiri"; notation of "FlashAttention'ı Anlamak Bölüm 1", section 0.2):
+ *     S = scale * Q K^T + M,   P = row-softmax(S),   O = P V,
+ * with M_ij = 0 where key j is visible to query i and -inf elsewhere. Without `causal` every key
+ * is visible. With `causal`, key j is visible to query i iff j <= i + (N_k - N_q): the page's
+ * "query i sees keys j <= i" (section "Maskeleme ve Dropout"), aligned so that the queries are
+ * the last N_q positions of the key sequence when N_q < N_k.
+ *
+ * Layout. Every tensor is a device pointer to a contiguous row-major array:
+ *     q, o, dout, dq      [B, H, N_q, d]   bf16
+ *     k, v, dk, dv        [B, H, N_k, d]   bf16
+ *     lse                 [B, H, N_q]      fp32, natural log: lse_i = ln sum_j exp(S_ij)
+ * bf16 values are passed as their 16-bit patterns (fa_bf16). d_v = d.
+ *
+ * Ownership. The caller owns every buffer. The library never allocates, frees or synchronises
+ * and keeps no mutable global state, so calls are reentrant. Inputs are read only; outputs are
+ * fully overwritten; outputs must not alias inputs or each other.
+ *
+ * Streams. Every call only enqueues kernels on `stream` (0 = the null stream) and returns.
+ *
+ * Errors. All arguments are validated before anything is enqueued; on any error nothing is
+ * enqueued and no output is touched. A failed launch returns FA_ERR_HIP. Faults during kernel
+ * execution surface at the caller's next synchronisation of the stream.
+ *
+ * Common constraints: B, H, N_q, N_k >= 1; d in {64, 128}; B*H*N_q and B*H*N_k below 2^31;
+ * pointers 16-byte aligned; scale finite and > 0; causal requires N_q <= N_k (so no row is empty).
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t fa_bf16; /* bfloat16 bit pattern */
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,     /* a size < 1, or an index range too large */
+  FA_ERR_HEADDIM = 3,   /* d not in {64, 128} */
+  FA_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
+  FA_ERR_CAUSAL = 5,    /* causal with N_q > N_k */
+  FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than the queried size */
+  FA_ERR_SCALE = 7,     /* scale not finite or not > 0 */
+  FA_ERR_ARG = 8,       /* another argument out of range (decode: N_q != 1, bad split count) */
+  FA_ERR_HIP = 9        /* a kernel launch failed */
+} fa_status;
+
+/* Human-readable name of a status code; never NULL. */
+const char* fa_status_string(fa_status s);
+
+/*
+ * Forward pass: O and the per-row log-sum-exp L.
+ * Page "Bellek Duvarının Fiziği", sections "Online Softmax" and "Forward geçişin iskeleti":
+ * Q is split into row blocks, K/V are streamed block by block through on-chip memory, the row
+ * maximum and sum are kept as running statistics, and the N_q x N_k score and probability
+ * matrices are never written to HBM. Section "Geri Yayılım": L is the one statistic per row that
+ * the backward pass needs to rebuild P.
+ *   q [B,H,N_q,d], k/v [B,H,N_k,d] in; o [B,H,N_q,d] bf16 and lse [B,H,N_q] fp32 out.
+ */
+fa_status fa_fwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+                 int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                 hipStream_t stream);
+
+/* Bytes of device workspace fa_bwd needs (the fp32 row vector D = rowsum(dO * O)). */
+size_t fa_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d);
+
+/*
+ * Backward pass by recomputation: gradients of O with respect to Q, K, V given dO.
+ * Page "Bellek Duvarının Fiziği", section "Geri Yayılım": P is rebuilt block by block as
+ * exp(S - L) from the stored L, D = rowsum(dO * O) is taken from the forward output, and the
+ * softmax gradient identity dS = P * (dP - D) gives dQ = scale dS K, dK = scale dS^T Q,
+ * dV = P^T dO.
+ *   q, k, v, o (forward output), lse (forward output), dout = dO in;
+ *   dq [B,H,N_q,d], dk, dv [B,H,N_k,d] bf16 out.
+ *   workspace: device memory of at least fa_bwd_workspace_bytes(...) bytes, 16-byte aligned,
+ *   owned by the caller, clobbered by the call.
+ */
+fa_status fa_bwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                 const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                 hipStream_t stream);
+
+/* The split count fa_decode uses when called with num_splits = 0. */
+int fa_decode_num_splits(int B, int H, int N_k, int d);
+
+/* Bytes of device workspace fa_decode needs for a split count (0 = the automatic choice):
+ * per (b, h, split) one fp32 partial output row of d values and one fp32 log-sum-exp. */
+size_t fa_decode_workspace_bytes(int B, int H, int N_k, int d, int num_splits);
+
+/*
+ * Decode step (Flash-Decoding): one query row per (b, h) against a long KV cache.
+ * Page "Bellek Duvarının Fiziği", section "Decode Aşaması: Flash-Decoding": the keys are split
+ * into C chunks processed in parallel, each producing its own local (max, sum, output) triple,
+ * and one reduction merges them with the online-softmax rescaling identity.
+ *   q [B,H,1,d], k/v [B,H,N_k,d] in; o [B,H,1,d] bf16 and lse [B,H,1] fp32 out.
+ *   N_q must be 1. With one query row the bottom-right causal mask hides nothing, so `causal`
+ *   is accepted and changes nothing. num_splits: 0 = automatic, else 1..min(N_k, 1024).
+ *   workspace: at least fa_decode_workspace_bytes(B, H, N_k, d, num_splits) bytes, 16-byte
+ *   aligned, owned by the caller, clobbered by the call.
+ */
+fa_status fa_decode(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+                    void* workspace, size_t workspace_bytes,
+                    int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                    int num_splits, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

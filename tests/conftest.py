@@ -20,4 +20,5 @@ def gpu():
     if not torch.cuda.is_available():
         pytest.fail("GPU test collected on a machine with no GPU")
     from exact_attention_fa_amd import _lib
-    return _lib.load()
+    _lib.load()
+    return _lib

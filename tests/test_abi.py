@@ -1,0 +1,105 @@
+"""The C ABI on the host: libfa.so loads without a GPU, exports every entry point include/fa.h
+declares, and rejects bad arguments before anything reaches the device (no compute calls)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_fa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from exact_attention_fa_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert names == sorted(_lib.SIGNATURES), "binding and header disagree"
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported by libfa.so"
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS.items():
+        assert lib.fa_status_string(code).decode().startswith(name)
+    assert lib.fa_status_string(1234).decode() == "FA_ERR_UNKNOWN"
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null value; never dereferenced on error paths
+
+
+def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Nq=8, Nk=8, d=64, scale=0.125,
+         causal=0):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, None)
+
+
+def test_fwd_validation(lib):
+    assert _fwd(lib, q=None) == 1
+    assert _fwd(lib, lse=None) == 1
+    assert _fwd(lib, B=0) == 2
+    assert _fwd(lib, Nq=0) == 2
+    assert _fwd(lib, Nk=-1) == 2
+    assert _fwd(lib, B=1 << 16, H=1 << 8, Nq=1 << 8) == 2  # B*H*Nq reaches 2^31
+    assert _fwd(lib, d=96) == 3
+    assert _fwd(lib, d=256) == 3
+    assert _fwd(lib, scale=0.0) == 7
+    assert _fwd(lib, scale=float("nan")) == 7
+    assert _fwd(lib, scale=float("inf")) == 7
+    assert _fwd(lib, scale=-1.0) == 7
+    assert _fwd(lib, Nq=9, Nk=8, causal=1) == 5
+    assert _fwd(lib, q=FAKE + 8) == 4
+    assert _fwd(lib, o=FAKE + 2) == 4
+
+
+def test_bwd_validation(lib):
+    ws = lib.fa_bwd_workspace_bytes(2, 3, 100, 50, 64)
+    assert ws >= 2 * 3 * 100 * 4 and ws % 16 == 0
+    assert lib.fa_bwd_workspace_bytes(0, 3, 100, 50, 64) == 0
+
+    def call(ws_ptr=FAKE, ws_bytes=ws, d=64, causal=0, Nq=100, Nk=50, dq=FAKE):
+        return lib.fa_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, ws_ptr, ws_bytes,
+                          2, 3, Nq, Nk, d, 0.125, causal, None)
+    assert call(dq=None) == 1
+    assert call(d=80) == 3
+    assert call(causal=1) == 5
+    assert call(ws_ptr=None) == 6
+    assert call(ws_bytes=ws - 16) == 6
+    assert call(ws_ptr=FAKE + 4) == 4
+    assert call(dq=FAKE + 2) == 4
+
+
+def test_decode_validation(lib):
+    c = lib.fa_decode_num_splits(8, 32, 65536, 128)
+    assert 1 <= c <= 1024
+    assert lib.fa_decode_num_splits(1, 1, 10, 64) >= 1
+    ws = lib.fa_decode_workspace_bytes(8, 32, 65536, 128, 0)
+    assert ws == lib.fa_decode_workspace_bytes(8, 32, 65536, 128, c)
+    assert ws >= 8 * 32 * c * (128 + 1) * 4
+    assert lib.fa_decode_workspace_bytes(8, 32, 65536, 96, 0) == 0
+
+    def call(Nq=1, splits=0, ws_bytes=ws, d=128, Nk=65536):
+        return lib.fa_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, 8, 32, Nq, Nk, d,
+                             0.08, 0, splits, None)
+    assert call(Nq=2) == 8
+    assert call(splits=-1) == 8
+    assert call(splits=1025) == 8
+    assert call(splits=11, Nk=10) == 8
+    assert call(ws_bytes=ws - 1) == 6
+    assert call(d=32) == 3
