@@ -39,30 +39,6 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
   return s;
 }
 
-template <int ctrl>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl,
-                                                               0xF, 0xF, true));
-}
-
-// Sum over the G consecutive lanes that share one key row (G = 16 or 8); every lane of the
-// group receives the total.
-template <int G>
-__device__ __forceinline__ float group_sum(float x) {
-  if constexpr (G == 16) {
-    x += dpp<0x128>(x);  // row_ror:8
-    x += dpp<0x124>(x);  // row_ror:4
-    x += dpp<0x122>(x);  // row_ror:2
-    x += dpp<0x121>(x);  // row_ror:1
-  } else {
-    static_assert(G == 8, "group of 8 or 16 lanes");
-    x += dpp<0x141>(x);  // row_half_mirror: lane i of 8 gets lane 7 - i
-    x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-    x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-  }
-  return x;
-}
-
 template <int D>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,

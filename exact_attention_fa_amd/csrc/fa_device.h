@@ -78,4 +78,80 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ---- DPP reductions within rows of 16 lanes ---------------------------------------------------
+template <int ctrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl,
+                                                               0xF, 0xF, true));
+}
+
+// Sum over the G consecutive lanes that share one key row (G = 16 or 8); every lane of the
+// group receives the total.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (G == 16) {
+    x += dpp<0x128>(x);  // row_ror:8
+    x += dpp<0x124>(x);  // row_ror:4
+    x += dpp<0x122>(x);  // row_ror:2
+    x += dpp<0x121>(x);  // row_ror:1
+  } else {
+    static_assert(G == 8, "group of 8 or 16 lanes");
+    x += dpp<0x141>(x);  // row_half_mirror: lane i of 8 gets lane 7 - i
+    x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  }
+  return x;
+}
+
+// ---- MFMA row order for the score tiles ------------------------------------------------------
+// In a 32 x 32 score tile computed as D = A B with A holding 32 sequence rows, MFMA row m is given
+// the sequence row key_of_row(m) = 16 (j >> 1) + 8 h + 4 (j & 1) + i (m = 8 j + 4 h + i). Result
+// register r of a lane in half-wave h then holds sequence row key_of_reg(r, h) =
+// 16 (r >> 3) + 8 h + (r & 7), so registers 8t..8t+7 cover 8 consecutive rows of the 16-row step t
+// and feed a following MFMA that contracts over those rows without any data movement.
+__device__ __forceinline__ int key_of_row(int m) {
+  const int j = m >> 3, h = (m >> 2) & 1, i = m & 3;
+  return 16 * (j >> 1) + 8 * h + 4 * (j & 1) + i;
+}
+__device__ __forceinline__ int key_of_reg(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
+
+// ---- row-major [rows][D] bf16 tiles in LDS ---------------------------------------------------
+// Each row is D/8 chunks of 16 bytes; the chunk index is XOR-swizzled with bits of the row so
+// that 16-byte reads of one chunk from 16 different rows, and the 8-byte transposing reads of a
+// 4-row x 16-column block, spread over distinct banks.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  constexpr int NCH = D / 8;
+  const int swz = (((row & 3) << 1) | ((row >> 2) & 1) | (row & 8)) & (NCH - 1);
+  return row * (D * 2) + ((((col >> 3) ^ swz)) << 4) + ((col & 7) << 1);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// MFMA A-operand fragment of the transpose of a row-major LDS tile T (row-major [rows][D]):
+// lane (l32 = lane % 32, h = lane / 32) receives T[r0 + 8 h + e][c0 + l32] for e = 0..7, i.e. the
+// 32 x 16 block (columns c0.., rows r0..r0+15) transposed, as two ds_read_b64_tr_b16. Within each
+// group of 16 lanes that instruction hands output lane i, element e, the element (i & 3) of the
+// 4-element piece loaded by input lane 4 e + (i >> 2); so input lane j loads row r0 + 8 h + (j >> 2)
+// (plus 4 for the second half), columns c0 + 16 (group & 1) + 4 (j & 3) .. + 3.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_read_transposed(const unsigned char* tile, int r0, int c0,
+                                                      int lane) {
+  const int j = lane & 15, grp = lane >> 4;
+  const int row = r0 + 8 * (grp >> 1) + (j >> 2);
+  const int col = c0 + 16 * (grp & 1) + 4 * (j & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(tile + tile_off<D>(row, col)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(tile + tile_off<D>(row + 4, col)));
+  u32x4 u;
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  u[0] = a[0];
+  u[1] = a[1];
+  u[2] = b[0];
+  u[3] = b[1];
+  return as_bf16x8(u);
+}
+
 }  // namespace fa

@@ -33,15 +33,6 @@ namespace {
 
 constexpr int kBC = 64;  // keys per tile
 
-// Key (within a 32-key block) assigned to MFMA row m of S^T = K Q^T.
-__device__ __forceinline__ int key_of_row(int m) {
-  const int j = m >> 3, h = (m >> 2) & 1, i = m & 3;
-  return 16 * (j >> 1) + 8 * h + 4 * (j & 1) + i;
-}
-
-// Key (within a 32-key block) held in result register r by a lane in half h.
-__device__ __forceinline__ int key_of_reg(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
-
 // Byte offset of the 16-byte chunk `c` (keys 8c..8c+7) of transposed-V row `d` in LDS.
 // Rows are kBC * 2 = 128 bytes; the chunk index is XOR-swizzled with the row so that both the
 // MFMA operand reads (16 consecutive rows, one chunk) and the transposing writes are free of
