@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Throughput of the exact-attention hot path on one MI355X.
+
+One step = one pass over every kernel of the path on synthetic bf16 inputs already in HBM:
+  * causal forward + backward at B=2, H=16, N=8192, d=128 (fa_fwd, then the backward's three
+    phases: D preprocess, dK/dV, dQ), and
+  * one split-KV decode step at B=8, H=32, KV length 65536, d=128 (fa_decode).
+`value` is the attention TFLOP/s of the causal forward + backward (algorithmic FLOPs:
+4 B H N^2 d, halved for the causal mask, times 3.5 for forward plus 2.5x backward), from the HIP
+events around those kernels; `ms_per_step` is the wall time of the whole step including the decode.
+The decode is reported in GB/s of K and V read. Every kernel's own rate and roofline fraction is
+listed, and `roofline` repeats the entry of the kernel that takes the most time.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from exact_attention_fa_amd import inputs, metrics  # noqa: E402
+
+FB = dict(B=2, H=16, N=8192, d=128, causal=True, seed=3)         # forward + backward workload
+DEC = dict(B=8, H=32, Nk=65536, d=128, seed=5)                  # decode workload
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(heads: int) -> dict:
+    """The fp64 oracle (as it stands) on `heads` heads of the forward + backward workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # threadpoolctl missing: report the visible cores
+        threads = os.cpu_count() or 1
+    N, d = FB["N"], FB["d"]
+    scale = 1.0 / math.sqrt(d)
+    f = inputs.bf16_to_f64
+    t = 0.0
+    for h in range(heads):
+        q = f(inputs.slice_bf16(FB["seed"], "q", 0, h, N, d))
+        k = f(inputs.slice_bf16(FB["seed"], "k", 0, h, N, d))
+        v = f(inputs.slice_bf16(FB["seed"], "v", 0, h, N, d))
+        do = f(inputs.slice_bf16(FB["seed"], "do", 0, h, N, d))
+        t0 = time.perf_counter()
+        oracle.forward_head(q, k, v, scale, True)
+        oracle.backward_head(q, k, v, do, scale, True)
+        t += time.perf_counter() - t0
+    flops = (metrics.attention_flops(1, heads, N, N, d, causal=True)
+             + metrics.attention_flops(1, heads, N, N, d, causal=True, backward=True))
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, forward + backward of {heads} head(s) (b=0) of the "
+                      f"causal B2 H16 N8192 d128 workload, {t:.1f} s; the oracle computes the full "
+                      f"unmasked score matrix, the rate uses the same causal-halved formula"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-heads", type=int, default=16,
+                    help="heads of the oracle CPU baseline sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        return 2
+
+    import torch
+    from exact_attention_fa_amd import _lib as fa
+    fa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(u16):
+        import numpy as np
+        return torch.from_numpy(u16.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    B, H, N, d, causal = FB["B"], FB["H"], FB["N"], FB["d"], FB["causal"]
+    q, k, v = (to_dev(x) for x in inputs.qkv_bf16(FB["seed"], B, H, N, N, d))
+    do = to_dev(inputs.tensor_bf16(FB["seed"], "do", B, H, N, d))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, N, d), dtype=torch.uint8, device=dev)
+    log("forward/backward inputs resident")
+
+    DB, DH, DN, Dd = DEC["B"], DEC["H"], DEC["Nk"], DEC["d"]
+    dq1 = to_dev(inputs.tensor_bf16(DEC["seed"], "q", DB, DH, 1, Dd))
+    dkc = to_dev(inputs.tensor_bf16(DEC["seed"], "k", DB, DH, DN, Dd))
+    dvc = to_dev(inputs.tensor_bf16(DEC["seed"], "v", DB, DH, DN, Dd))
+    dout_o = torch.empty_like(dq1)
+    dout_l = torch.empty((DB, DH, 1), dtype=torch.float32, device=dev)
+    splits = fa.decode_num_splits(DB, DH, DN, Dd)
+    dws = torch.empty(fa.decode_workspace_bytes(DB, DH, DN, Dd, splits), dtype=torch.uint8,
+                      device=dev)
+    log(f"decode inputs resident (splits {splits})")
+
+    names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "decode"]
+
+    def step(ev):
+        ev[0].record()
+        fa.fwd(q, k, v, causal=causal, out=(o, lse))
+        ev[1].record()
+        fa.bwd_phase("preprocess", q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal)
+        ev[2].record()
+        fa.bwd_phase("dkdv", q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal)
+        ev[3].record()
+        fa.bwd_phase("dq", q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal)
+        ev[4].record()
+        fa.decode(dq1, dkc, dvc, num_splits=splits, workspace=dws, out=(dout_o, dout_l))
+        ev[5].record()
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]  # noqa: E731
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    events = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for ev in events:
+        step(ev)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / max(args.steps, 1)
+    ms = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / len(events)
+          for i, n in enumerate(names)}
+    log("timed steps done: " + ", ".join(f"{n} {ms[n]:.3f} ms" for n in names))
+
+    peak_tf, peak_bw = metrics.MI355X_BF16_DENSE_TFLOPS, metrics.MI355X_HBM_GBPS
+    f_fwd = metrics.attention_flops(B, H, N, N, d, causal=causal)
+    f_bwd = metrics.attention_flops(B, H, N, N, d, causal=causal, backward=True)
+    gemm = f_fwd / 2  # one N x N x d product, causal-halved
+    pre_bytes = 2 * B * H * N * d * 2 + B * H * N * 4
+    dec_bytes = metrics.decode_bytes(DB, DH, DN, Dd)
+
+    def mfma_entry(flops, t_ms, note):
+        a = flops / (t_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": a, "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": a / peak_tf, "traffic": None, "ms": t_ms, "work": note}
+
+    def hbm_entry(nbytes, t_ms, note):
+        a = nbytes / (t_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": a, "peak": peak_bw, "unit": "GB/s",
+                "frac": a / peak_bw, "traffic": None, "ms": t_ms, "work": note}
+
+    kernels = {
+        "fwd": mfma_entry(f_fwd, ms["fwd"], "4 B H N^2 d / 2 (QK^T and PV, causal)"),
+        "bwd_dkdv": mfma_entry(4 * gemm, ms["bwd_dkdv"], "4 products (S, dP, dV, dK), causal"),
+        "bwd_dq": mfma_entry(1 * gemm, ms["bwd_dq"],
+                             "1 algorithmic product (dQ); it also re-runs S and dP"),
+        "bwd_preprocess": hbm_entry(pre_bytes, ms["bwd_preprocess"], "read O and dO, write D"),
+        "decode": hbm_entry(dec_bytes, ms["decode"],
+                            "K and V read once + q, o, lse (split + combine kernels)"),
+    }
+    kernels["bwd_dq"]["executed_tflops"] = 3 * gemm / (ms["bwd_dq"] * 1e-3) / 1e12
+    dominant = max(kernels, key=lambda n: kernels[n]["ms"])
+    roof = dict(kernels[dominant])
+    roof["kernel"] = dominant
+
+    fb_ms = ms["fwd"] + ms["bwd_preprocess"] + ms["bwd_dkdv"] + ms["bwd_dq"]
+    value = (f_fwd + f_bwd) / (fb_ms * 1e-3) / 1e12
+    out = {
+        "metric": "attention TFLOP/s (causal fwd+bwd, bf16) + decode HBM GB/s",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1) rounded to bf16)",
+        "config": {"workload": "causal attention forward+backward B=2 H=16 N=8192 d=128, plus one "
+                               "split-KV decode step B=8 H=32 KV=65536 d=128",
+                   "global_batch": B, "seq_len": N, "heads": H, "head_dim": d,
+                   "parallelism": "single-gpu"},
+        "fwd_tflops": kernels["fwd"]["achieved"],
+        "fwd_frac_peak": kernels["fwd"]["frac"],
+        "bwd_tflops": f_bwd / ((ms["bwd_preprocess"] + ms["bwd_dkdv"] + ms["bwd_dq"]) * 1e-3) / 1e12,
+        "decode_gbps": kernels["decode"]["achieved"],
+        "decode_frac_peak": kernels["decode"]["frac"],
+        "decode_splits": splits,
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if args.cpu_heads > 0:
+        log(f"oracle CPU baseline on {args.cpu_heads} head(s) ...")
+        out["cpu_baseline"] = cpu_baseline(args.cpu_heads)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

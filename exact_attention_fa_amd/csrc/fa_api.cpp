@@ -66,22 +66,65 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d) {
   return round_up16((size_t)B * H * N_q * sizeof(float));
 }
 
-fa_status fa_bwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
-                 const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
-                 void* workspace, size_t workspace_bytes, int B, int H, int N_q, int N_k, int d,
-                 float scale, int causal, hipStream_t stream) {
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+namespace {
+
+// Shared validation of fa_bwd and its phases; `need` says which pointers the phase uses
+// (bit 0: o, 1: q/k/v/lse, 2: dk/dv, 3: dq; dout and the workspace are always used).
+fa_status bwd_checked(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                      const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk,
+                      fa_bf16* dv, void* workspace, size_t workspace_bytes, int B, int H,
+                      int N_q, int N_k, int d, float scale, int causal, hipStream_t stream,
+                      unsigned need, unsigned phases) {
+  const bool use_o = need & 1u, use_qkv = need & 2u, use_kv_out = need & 4u, use_q_out = need & 8u;
+  if (!dout || (use_o && !o) || (use_qkv && (!q || !k || !v || !lse)) ||
+      (use_kv_out && (!dk || !dv)) || (use_q_out && !dq))
+    return FA_ERR_NULL;
   fa_status s = check_common(B, H, N_q, N_k, d, scale, causal);
   if (s != FA_OK) return s;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+  if (!aligned16(dout) || (use_o && !aligned16(o)) ||
+      (use_qkv && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse))) ||
+      (use_kv_out && (!aligned16(dk) || !aligned16(dv))) || (use_q_out && !aligned16(dq)))
     return FA_ERR_ALIGN;
   if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, N_q, N_k, d))
     return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
   fa::BwdArgs a{bf(q), bf(k), bf(v), bf(o), lse, bf(dout), bf(dq), bf(dk), bf(dv),
                 static_cast<float*>(workspace), B, H, N_q, N_k, d, scale, causal != 0, stream};
-  return from_hip(fa::launch_bwd(a));
+  return from_hip(fa::launch_bwd(a, phases));
+}
+
+}  // namespace
+
+fa_status fa_bwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                 const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+                 void* workspace, size_t workspace_bytes, int B, int H, int N_q, int N_k, int d,
+                 float scale, int causal, hipStream_t stream) {
+  return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N_q,
+                     N_k, d, scale, causal, stream, 15u, 7u);
+}
+
+fa_status fa_bwd_preprocess(const fa_bf16* o, const fa_bf16* dout, void* workspace,
+                            size_t workspace_bytes, int B, int H, int N_q, int N_k, int d,
+                            hipStream_t stream) {
+  // scale and causal play no part in D; pass valid values to the shared checks
+  return bwd_checked(nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr, nullptr,
+                     workspace, workspace_bytes, B, H, N_q, N_k, d, 1.f, 0, stream, 1u, 1u);
+}
+
+fa_status fa_bwd_dkdv(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const float* lse,
+                      const fa_bf16* dout, fa_bf16* dk, fa_bf16* dv, void* workspace,
+                      size_t workspace_bytes, int B, int H, int N_q, int N_k, int d, float scale,
+                      int causal, hipStream_t stream) {
+  return bwd_checked(q, k, v, nullptr, lse, dout, nullptr, dk, dv, workspace, workspace_bytes, B,
+                     H, N_q, N_k, d, scale, causal, stream, 6u, 2u);
+}
+
+fa_status fa_bwd_dq(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const float* lse,
+                    const fa_bf16* dout, fa_bf16* dq, void* workspace, size_t workspace_bytes,
+                    int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                    hipStream_t stream) {
+  return bwd_checked(q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, workspace,
+                     workspace_bytes, B, H, N_q, N_k, d, scale, causal, stream, 10u, 4u);
 }
 
 int fa_decode_num_splits(int B, int H, int N_k, int d) {

@@ -402,11 +402,11 @@ __global__ __launch_bounds__(kNT) void bwd_dq_kernel(
 
 // ---------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-hipError_t launch(const BwdArgs& a) {
+hipError_t launch(const BwdArgs& a, unsigned phases) {
   const int BH = a.B * a.H;
   const float c = a.scale * kLog2e;
   const int rows = BH * a.Nq;
-  {
+  if (phases & 1u) {
     constexpr int RPB = 256 / (D / 8);
     int grid = (rows + RPB * 4 - 1) / (RPB * 4);
     hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3(grid), dim3(256), 0, a.stream, a.o, a.dout,
@@ -414,7 +414,7 @@ hipError_t launch(const BwdArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (phases & 2u) {
     const long long grid = (long long)BH * ((a.Nk + kBKV - 1) / kBKV);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kNT), 0, a.stream,
@@ -423,20 +423,22 @@ hipError_t launch(const BwdArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (phases & 4u) {
     const long long grid = (long long)BH * ((a.Nq + kBR - 1) / kBR);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kNT), 0, a.stream,
                        a.q, a.k, a.v, a.dout, a.lse, a.delta, a.dq, BH, a.Nq, a.Nk, c, a.scale);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch<128, true>(a) : launch<128, false>(a);
-  return a.causal ? launch<64, true>(a) : launch<64, false>(a);
+hipError_t launch_bwd(const BwdArgs& a, unsigned phases) {
+  if (a.d == 128) return a.causal ? launch<128, true>(a, phases) : launch<128, false>(a, phases);
+  return a.causal ? launch<64, true>(a, phases) : launch<64, false>(a, phases);
 }
 
 }  // namespace fa

@@ -49,7 +49,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
-hipError_t launch_bwd(const BwdArgs& a);
+// Backward phases; `phase_mask` bit 0 = D preprocess, bit 1 = dK/dV, bit 2 = dQ.
+hipError_t launch_bwd(const BwdArgs& a, unsigned phase_mask = 7u);
 hipError_t launch_decode(const DecodeArgs& a);
 
 // Split count used by the decode when the caller passes 0.
