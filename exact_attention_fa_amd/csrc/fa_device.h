@@ -48,6 +48,19 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
   return as_bf16x8(u);
 }
 
+// acc + the sum of the eight bf16 values of v (exact products with 1 in v_dot2_f32_bf16).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const u32x4 u = as_u32x4(v);
+  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t uw = u[w];  // copy first: bit_cast of an indexed vector element miscompiles
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, uw), one, acc, false);
+  }
+  return acc;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

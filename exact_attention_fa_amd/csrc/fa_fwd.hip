@@ -32,6 +32,7 @@ namespace fa {
 namespace {
 
 constexpr int kBC = 64;  // keys per tile
+constexpr float kRescaleSlack = 8.f;  // log2 units
 
 // Byte offset of the 16-byte chunk `c` (keys 8c..8c+7) of transposed-V row `d` in LDS.
 // Rows are kBC * 2 = 128 bytes; the chunk index is XOR-swizzled with the row so that both the
@@ -62,8 +63,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const bf16* __restrict__ Q
   constexpr int BR = NW * 32;         // query rows per workgroup
   constexpr int DCH = D / 8;          // 16-byte chunks per row
   constexpr int KCH = kBC * DCH / NT; // K chunks per thread
-  constexpr int VIT = (kBC / 2) * DCH / NT;  // V (key pair, chunk) items per thread
-  static_assert(KCH >= 1 && VIT >= 1, "tile too small for the workgroup");
+  constexpr int VTOT = (kBC / 2) * DCH;       // V (key pair, chunk) items per tile
+  constexpr int VIT = (VTOT + NT - 1) / NT;   // per thread (the last pass may be partial)
+  static_assert(KCH >= 1 && KCH * NT == kBC * DCH, "K tile must split evenly over the threads");
   using SM = FwdSmem<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SM::kBytes];
 
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const bf16* __restrict__ Q
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f, lq_run = 0.f;  // lq: sum of the bf16-rounded P
 
   // ---- global -> register staging of one K/V tile
   u32x4 kreg[KCH], vreg[VIT][2];
@@ -133,6 +135,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const bf16* __restrict__ Q
 #pragma unroll
     for (int i = 0; i < VIT; ++i) {
       const int it = tid + i * NT;
+      if (VTOT % NT != 0 && it >= VTOT) break;
       const int dc = (it & 3) + 4 * ((it >> 6) % (DCH / 4));
       const int kp = ((it >> 2) & 15) + 16 * ((it >> 6) / (DCH / 4));
       const int key = kb0 + 2 * kp;
@@ -155,6 +158,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const bf16* __restrict__ Q
 #pragma unroll
     for (int i = 0; i < VIT; ++i) {
       const int it = tid + i * NT;
+      if (VTOT % NT != 0 && it >= VTOT) break;
       const int dc = (it & 3) + 4 * ((it >> 6) % (DCH / 4));
       const int kp = ((it >> 2) & 15) + 16 * ((it >> 6) / (DCH / 4));
       const u32x4 a = vreg[i][0], b = vreg[i][1];
@@ -213,32 +217,46 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const bf16* __restrict__ Q
     }
 
     // ---- online softmax (base 2, scale folded into c = scale * log2 e)
+    // The running maximum is only moved when some row of the wave would exceed it by more than
+    // kRescaleSlack (in log2 units); otherwise the stale maximum is kept. Softmax is invariant
+    // to the reference value, so the result is the same up to rounding: probabilities are then
+    // bounded by 2^kRescaleSlack instead of 1, far inside fp32 and bf16 range, and the rescale
+    // of the accumulator (D/2 multiplies per lane) is skipped on most tiles.
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < kBC / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = halves_max(mx);
-    const float m_new = fmaxf(m_run, mx * c);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
-    m_run = m_new;
+    mx = halves_max(mx) * c;
+    if (__any(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2_fast(m_run - m_new);  // m_new is finite: key 0 of tile 0 is visible
+      m_run = m_new;
+      l_run *= alpha;
+      lq_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float m_use = m_run;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < kBC / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(__builtin_fmaf(s[kb][r], c, -m_use));
-        s[kb][r] = p;
-        psum += p;
+        s[kb][r] = exp2_fast(__builtin_fmaf(s[kb][r], c, -m_use));
+        psum += s[kb][r];
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    l_run += psum;
 
+    // P goes to the second product in bf16. The normaliser of O is the row sum of those same
+    // bf16 values (one v_dot2_f32_bf16 against (1, 1) per pair), so O is an exact convex
+    // combination of V rows under the rounded weights: its error becomes
+    // sum_j w_j e_j (v_j - O) instead of sum_j w_j e_j v_j, much smaller when a few keys dominate
+    // a row. The log-sum-exp keeps the fp32 sum.
     bf16x8 pf[kBC / 16];
+    float qsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < kBC / 32; ++kb)
 #pragma unroll
@@ -246,7 +264,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const bf16* __restrict__ Q
         const int r0 = 8 * tt;
         pf[kb * 2 + tt] = pack_bf16x8(s[kb][r0], s[kb][r0 + 1], s[kb][r0 + 2], s[kb][r0 + 3],
                                       s[kb][r0 + 4], s[kb][r0 + 5], s[kb][r0 + 6], s[kb][r0 + 7]);
+        qsum = sum_bf16x8(pf[kb * 2 + tt], qsum);
       }
+    lq_run += qsum;
 
     // ---- O^T += V^T P^T
 #pragma unroll
@@ -262,8 +282,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const bf16* __restrict__ Q
 
   // ---- epilogue: O = acc / l, L = ln 2 * (m + log2 l)
   const float l_tot = halves_sum(l_run);
+  const float lq_tot = halves_sum(lq_run);
   if (qi < Nq) {
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / lq_tot;
     bf16* orow = O + ((size_t)bh * Nq + qi) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -293,8 +314,8 @@ hipError_t launch(const FwdArgs& a) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch<128, 4, true>(a) : launch<128, 4, false>(a);
-  return a.causal ? launch<64, 4, true>(a) : launch<64, 4, false>(a);
+  if (a.d == 128) return a.causal ? launch<128, 8, true>(a) : launch<128, 8, false>(a);
+  return a.causal ? launch<64, 8, true>(a) : launch<64, 8, false>(a);
 }
 
 }  // namespace fa
