@@ -31,6 +31,9 @@ def compile_flags() -> list[str]:
         "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
         # packed fp32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # no NaN ever flows through the kernels (inputs are finite and -inf - -inf is avoided),
+        # so fmaxf needs no NaN canonicalisation and maps to v_max3_f32
+        "-fno-honor-nans",
         "-Wall", "-Wno-unused-result",
     ]
 

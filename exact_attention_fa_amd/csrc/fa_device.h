@@ -142,12 +142,30 @@ __device__ __forceinline__ int tile_off(int row, int col) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// MFMA A-operand fragment of the transpose of a row-major LDS tile T (row-major [rows][D]):
-// lane (l32 = lane % 32, h = lane / 32) receives T[r0 + 8 h + e][c0 + l32] for e = 0..7, i.e. the
-// 32 x 16 block (columns c0.., rows r0..r0+15) transposed, as two ds_read_b64_tr_b16. Within each
-// group of 16 lanes that instruction hands output lane i, element e, the element (i & 3) of the
-// 4-element piece loaded by input lane 4 e + (i >> 2); so input lane j loads row r0 + 8 h + (j >> 2)
-// (plus 4 for the second half), columns c0 + 16 (group & 1) + 4 (j & 3) .. + 3.
+__device__ __forceinline__ bf16x8 concat_s16x4(s16x4 lo, s16x4 hi) {
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  u32x4 u;
+  u[0] = a[0];
+  u[1] = a[1];
+  u[2] = b[0];
+  u[3] = b[1];
+  return as_bf16x8(u);
+}
+
+// Two ds_read_b64_tr_b16 at p and p + second: within each group of 16 lanes the instruction
+// hands output lane i, element e, the element (i & 3) of the 4-element piece that input lane
+// 4 e + (i >> 2) addressed; the two reads give elements 0..3 and 4..7 of an MFMA operand.
+__device__ __forceinline__ bf16x8 lds_read_tr_pair(const unsigned char* p, int second) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + second));
+  return concat_s16x4(lo, hi);
+}
+
+// MFMA A-operand fragment of the transpose of a row-major LDS tile T ([rows][D], tile_off
+// layout): lane (l32 = lane % 32, h = lane / 32) receives T[r0 + 8 h + e][c0 + l32] for e = 0..7,
+// i.e. the 32 x 16 block (columns c0.., rows r0..r0+15) transposed. Input lane j of each group of
+// 16 loads row r0 + 8 h + (j >> 2) (plus 4 for the second half), columns
+// c0 + 16 (group & 1) + 4 (j & 3) .. + 3.
 template <int D>
 __device__ __forceinline__ bf16x8 lds_read_transposed(const unsigned char* tile, int r0, int c0,
                                                       int lane) {
@@ -158,13 +176,26 @@ __device__ __forceinline__ bf16x8 lds_read_transposed(const unsigned char* tile,
       (lds_s16x4*)(tile + tile_off<D>(row, col)));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_s16x4*)(tile + tile_off<D>(row + 4, col)));
-  u32x4 u;
-  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
-  u[0] = a[0];
-  u[1] = a[1];
-  u[2] = b[0];
-  u[3] = b[1];
-  return as_bf16x8(u);
+  return concat_s16x4(lo, hi);
 }
+
+// ---- HBM/L2 -> LDS copies without register staging ------------------------------------------
+#if defined(__HIP_DEVICE_COMPILE__)
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes return zero.
+// Word 3 is the gfx9-family raw-buffer configuration (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// buffer_load_dwordx4 ... lds: lane l of the wave writes its 16 bytes (from voffset) to
+// dst + 16 l. dst must be the same for the whole wave.
+__device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* dst,
+                                              int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voffset, 0, 0, 0);
+}
+#endif
+// Wait until this thread's outstanding vector-memory operations (including the LDS copies
+// above) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace fa

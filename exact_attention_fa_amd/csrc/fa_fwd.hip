@@ -15,62 +15,60 @@
 //     (grid) dimension, and inside a workgroup each wave owns 32 query rows while all waves
 //     share the K/V tiles in LDS.
 //
-// CDNA4 mapping. The products are computed transposed, S^T = K Q^T and O^T = V^T P^T, on
-// v_mfma_f32_32x32x16_bf16, so that one lane owns one query: the row maximum is an in-lane max
-// plus one exchange with the other half-wave, the row sum needs no exchange until the end, and
-// the rescale of the accumulator by alpha is in-lane. The keys of each 32-key block are given
-// to the MFMA rows in an order (key_of_row) that leaves every lane's eight probabilities of a
-// 16-key step in consecutive registers, so they feed the second product directly as its B
-// operand. V is stored transposed in LDS (row = head dimension, keys along the row, 16-byte
-// chunks XOR-swizzled against bank conflicts); K is stored row-major with one 16-byte pad per
-// row. K/V tiles are double-buffered in LDS and the next tile's global loads are issued before
-// the current tile's math.
+// CDNA4 mapping.
+//   * The products are computed transposed, S^T = K Q^T and O^T = V^T P^T, on
+//     v_mfma_f32_32x32x16_bf16, so that one lane owns one query: the row maximum is an in-lane
+//     max plus one v_permlane32_swap, the row sum needs no exchange until the end, and the rescale
+//     of the accumulator is in-lane. The keys of each 32-key block are given to the MFMA rows in
+//     an order (key_of_row) that leaves every lane's eight probabilities of a 16-key step in
+//     consecutive registers, so they feed the second product directly as its B operand.
+//   * K and V tiles (64 keys) are copied HBM/L2 -> LDS by buffer_load_dwordx4 ... lds, with no
+//     register staging; rows past N_k read as zero through the buffer range check. Tiles are
+//     padded (K rows by 16 bytes, V rows by 32 bytes at d = 128) so that the 16-byte K reads of
+//     the first product and the ds_read_b64_tr_b16 reads that assemble V^T for the second product
+//     are free of bank conflicts. K is copied two tiles ahead and V one tile ahead.
+//   * Software pipeline: the QK^T product of tile t+1 is issued while the softmax of tile t runs,
+//     so the matrix cores and the vector ALUs overlap inside a wave; two waves share each SIMD.
+//   * The running maximum only moves when some row of the wave would exceed it by more than
+//     kRescaleSlack (log2 units), so the accumulator rescale is skipped on most tiles. Softmax is
+//     invariant to the reference value; probabilities are then bounded by 2^kRescaleSlack.
+//   * O is normalised by the sum of the same bf16 probabilities that feed the PV product, so it is
+//     an exact convex combination of V rows under the rounded weights; the log-sum-exp keeps the
+//     fp32 sum.
 #include "fa_device.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
-constexpr int kBC = 64;  // keys per tile
+constexpr int kBC = 64;               // keys per tile
 constexpr float kRescaleSlack = 8.f;  // log2 units
 
-// Byte offset of the 16-byte chunk `c` (keys 8c..8c+7) of transposed-V row `d` in LDS.
-// Rows are kBC * 2 = 128 bytes; the chunk index is XOR-swizzled with the row so that both the
-// MFMA operand reads (16 consecutive rows, one chunk) and the transposing writes are free of
-// bank conflicts.
-__device__ __forceinline__ int vt_offset(int d, int c) {
-  const int swz = ((d >> 1) & 7) ^ (((d >> 4) & 1) << 1);
-  return d * (kBC * 2) + 16 * (c ^ swz);
-}
-
 template <int D>
-struct FwdSmem {
-  static constexpr int kStride = D + 8;                 // K row stride in bf16 (16-byte pad)
-  static constexpr int kKBytes = kBC * kStride * 2;     // one K tile
-  static constexpr int kVBytes = D * kBC * 2;           // one transposed V tile
-  static constexpr int kBufBytes = kKBytes + kVBytes;
-  static constexpr int kBytes = 2 * kBufBytes;          // double buffered
+struct FwdLds {
+  static constexpr int KST = 2 * D + 16;                        // K row stride (bytes)
+  static constexpr int VST = 2 * D + (D == 128 ? 32 : 16);      // V row stride (bytes)
+  static constexpr int KCPR = KST / 16, VCPR = VST / 16;        // 16-byte chunks per row
+  static constexpr int KT = kBC * KST, VT = kBC * VST;          // tile bytes
+  static constexpr int KI = kBC * KCPR / 64, VI = kBC * VCPR / 64;  // wave-wide copies per tile
+  static constexpr int kBytes = 2 * KT + 2 * VT;
+  static_assert(KI * 64 == kBC * KCPR && VI * 64 == kBC * VCPR, "tiles are whole wave copies");
 };
 
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(const bf16* __restrict__ Q,
-                                                      const bf16* __restrict__ K,
-                                                      const bf16* __restrict__ V,
-                                                      bf16* __restrict__ O,
-                                                      float* __restrict__ LSE, int BH, int Nq,
-                                                      int Nk, float c) {
-  constexpr int NT = NW * 64;         // threads
-  constexpr int BR = NW * 32;         // query rows per workgroup
-  constexpr int DCH = D / 8;          // 16-byte chunks per row
-  constexpr int KCH = kBC * DCH / NT; // K chunks per thread
-  constexpr int VTOT = (kBC / 2) * DCH;       // V (key pair, chunk) items per tile
-  constexpr int VIT = (VTOT + NT - 1) / NT;   // per thread (the last pass may be partial)
-  static_assert(KCH >= 1 && KCH * NT == kBC * DCH, "K tile must split evenly over the threads");
-  using SM = FwdSmem<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SM::kBytes];
+__global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64) void fwd_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int Nq, int Nk, float c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using L = FwdLds<D>;
+  constexpr int BR = NW * 32;  // query rows per workgroup
+  constexpr int KIW = (L::KI + NW - 1) / NW, VIW = (L::VI + NW - 1) / NW;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::kBytes];
+  unsigned char* kbuf = smem;
+  unsigned char* vbuf = smem + 2 * L::KT;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
   // ---- workgroup -> (b*h, query tile): longest causal tiles first; with BH a multiple of 8,
@@ -90,147 +88,122 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const bf16* __restrict__ Q
   const int qt = CAUSAL ? nqt - 1 - rank : rank;
   const int q0 = qt * BR;
   const int qw = q0 + wave * 32;  // first query row of this wave
+  const int qi = qw + l32;        // this lane's query row
   const int shift = Nk - Nq;      // causal: key j visible to query i iff j <= i + shift
 
   const bf16* Qh = Q + (size_t)bh * Nq * D;
   const bf16* Kh = K + (size_t)bh * Nk * D;
   const bf16* Vh = V + (size_t)bh * Nk * D;
 
-  // ---- key range of the workgroup
   int kend = Nk;
-  if (CAUSAL) kend = min(Nk, min(q0 + BR, Nq) - 1 + shift + 1);
+  if (CAUSAL) kend = min(Nk, min(q0 + BR, Nq) + shift);
   const int ntiles = (kend + kBC - 1) / kBC;
+  // last tile any row of this wave can see
+  const int horizon = CAUSAL ? min(qw + 31, Nq - 1) + shift : Nk - 1;
+  const int last_tile = min(ntiles - 1, horizon / kBC);
 
-  // ---- Q fragments (B operand of S^T = K Q^T): query qw + l32, dims 16 ks + 8 hi + 0..7
-  bf16x8 qf[D / 16];
-  {
-    const int qi = qw + l32;
+  // ---- LDS fill: copy p of a tile (wave-wide, 64 consecutive 16-byte chunks) lands at chunk
+  // positions p*64 .. p*64+63 of the padded tile; pad positions re-read chunk 0 of their row.
+  int koff[KIW], voff[VIW];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (qi < Nq) x = ld16(Qh + (size_t)qi * D + ks * 16 + hi * 8);
-      qf[ks] = as_bf16x8(x);
-    }
+  for (int i = 0; i < KIW; ++i) {
+    const int p = (wave + i * NW) * 64 + lane, row = p / L::KCPR, ch = p % L::KCPR;
+    koff[i] = row * D * 2 + (ch < D / 8 ? ch : 0) * 16;
   }
+#pragma unroll
+  for (int i = 0; i < VIW; ++i) {
+    const int p = (wave + i * NW) * 64 + lane, row = p / L::VCPR, ch = p % L::VCPR;
+    voff[i] = row * D * 2 + (ch < D / 8 ? ch : 0) * 16;
+  }
+  auto tile_rsrc = [&](const bf16* base, int t) {
+    const int rows = max(0, Nk - t * kBC);  // reads at or past N_k return zero
+    return make_rsrc(base + (size_t)t * kBC * D, rows * D * 2);
+  };
+  auto copy_k = [&](int t) {
+    const auto r = tile_rsrc(Kh, t);
+    unsigned char* dst = kbuf + (t & 1) * L::KT;
+#pragma unroll
+    for (int i = 0; i < KIW; ++i)
+      if (wave + i * NW < L::KI) buffer_to_lds(r, dst + (wave + i * NW) * 1024, koff[i]);
+  };
+  auto copy_v = [&](int t) {
+    const auto r = tile_rsrc(Vh, t);
+    unsigned char* dst = vbuf + (t & 1) * L::VT;
+#pragma unroll
+    for (int i = 0; i < VIW; ++i)
+      if (wave + i * NW < L::VI) buffer_to_lds(r, dst + (wave + i * NW) * 1024, voff[i]);
+  };
 
+  // ---- Q fragments (B operand of S^T = K Q^T): query qi, dims 16 ks + 8 hi + 0..7
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (qi < Nq) x = ld16(Qh + (size_t)qi * D + ks * 16 + hi * 8);
+    qf[ks] = as_bf16x8(x);
+  }
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = kNegInf, l_run = 0.f, lq_run = 0.f;  // lq: sum of the bf16-rounded P
+  // m in log2 units of the scaled scores; l: fp32 row sum; lq: sum of the bf16-rounded P
+  float m_run = kNegInf, l_run = 0.f, lq_run = 0.f;
 
-  // ---- global -> register staging of one K/V tile
-  u32x4 kreg[KCH], vreg[VIT][2];
-  auto load_tile = [&](int t) {
-    const int kb0 = t * kBC;
+  // A operand of S^T: K row key_of_row(l32) (and +32), dims 16 ks + 8 hi
+  const int kr0 = key_of_row(l32) * L::KST + hi * 16;
+  // A operand of O^T (V^T rows = dims) via ds_read_b64_tr_b16: within each group of 16 lanes,
+  // input lane j reads row 8 h + (j >> 2), columns 16 (group & 1) + 4 (j & 3) of the 16 x 32
+  // block; the instruction hands output lane i element e of input lane 4 e + (i >> 2).
+  const int vj = lane & 15, vg = lane >> 4;
+  const int vr0 = (8 * (vg >> 1) + (vj >> 2)) * L::VST + (16 * (vg & 1) + 4 * (vj & 3)) * 2;
+
+  auto qk = [&](f32x16& s0, f32x16& s1, const unsigned char* kt) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int it = tid + i * NT;
-      const int key = kb0 + it / DCH, dc = it % DCH;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < Nk) x = ld16(Kh + (size_t)key * D + dc * 8);
-      kreg[i] = x;
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = 0.f;
+      s1[r] = 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int it = tid + i * NT;
-      if (VTOT % NT != 0 && it >= VTOT) break;
-      const int dc = (it & 3) + 4 * ((it >> 6) % (DCH / 4));
-      const int kp = ((it >> 2) & 15) + 16 * ((it >> 6) / (DCH / 4));
-      const int key = kb0 + 2 * kp;
-      u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
-      if (key < Nk) x0 = ld16(Vh + (size_t)key * D + dc * 8);
-      if (key + 1 < Nk) x1 = ld16(Vh + (size_t)(key + 1) * D + dc * 8);
-      vreg[i][0] = x0;
-      vreg[i][1] = x1;
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 a0 = as_bf16x8(ld16(kt + kr0 + ks * 32));
+      const bf16x8 a1 = as_bf16x8(ld16(kt + kr0 + 32 * L::KST + ks * 32));
+      s0 = mfma32(a0, qf[ks], s0);
+      s1 = mfma32(a1, qf[ks], s1);
     }
   };
-  auto store_tile = [&](int buf) {
-    unsigned char* kbuf = smem + buf * SM::kBufBytes;
-    unsigned char* vbuf = kbuf + SM::kKBytes;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int it = tid + i * NT;
-      const int key = it / DCH, dc = it % DCH;
-      st16(kbuf + (key * SM::kStride + dc * 8) * 2, kreg[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int it = tid + i * NT;
-      if (VTOT % NT != 0 && it >= VTOT) break;
-      const int dc = (it & 3) + 4 * ((it >> 6) % (DCH / 4));
-      const int kp = ((it >> 2) & 15) + 16 * ((it >> 6) / (DCH / 4));
-      const u32x4 a = vreg[i][0], b = vreg[i][1];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // dims 8 dc + 2w (low halves) and 8 dc + 2w + 1 (high halves) of keys 2kp, 2kp + 1
-        const uint32_t lo = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);
-        const uint32_t hw = __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);
-        const int d0 = dc * 8 + 2 * w;
-        *reinterpret_cast<uint32_t*>(vbuf + vt_offset(d0, kp >> 2) + 4 * (kp & 3)) = lo;
-        *reinterpret_cast<uint32_t*>(vbuf + vt_offset(d0 + 1, kp >> 2) + 4 * (kp & 3)) = hw;
-      }
-    }
+  auto vt_frag = [&](const unsigned char* vt, int st, int db) {
+    const unsigned char* p = vt + vr0 + st * 16 * L::VST + db * 64;
+    return lds_read_tr_pair(p, 4 * L::VST);
   };
 
-  // horizon of this wave: last key any of its rows can see
-  const int wave_last_q = min(qw + 31, Nq - 1);
-  const int wave_horizon = CAUSAL ? wave_last_q + shift : Nk - 1;
-  const int qi = qw + l32;
-
-  if (ntiles > 0) load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    store_tile(buf);
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
-
+  // One pipeline step: mask, softmax and PV of tile t (scores in sc0/sc1), and the QK^T of
+  // tile t+1 into sn0/sn1, issued between them so that it overlaps the softmax.
+  auto step = [&](f32x16& sc0, f32x16& sc1, f32x16& sn0, f32x16& sn1, int t) {
+    wait_vmem();      // this thread's copies of K[t+1] and V[t] have landed
+    __syncthreads();  // ... everyone's have, and everyone is done with K[t], V[t-1]
+    if (t + 2 < ntiles) copy_k(t + 2);
+    if (t + 1 < ntiles) copy_v(t + 1);
+    if (t > last_tile) return;  // every row of this wave is masked from here on
     const int kbase = t * kBC;
-    if (kbase > wave_horizon) continue;  // every row of this wave is masked for this tile
-    const unsigned char* kbuf = smem + buf * SM::kBufBytes;
-    const unsigned char* vbuf = kbuf + SM::kKBytes;
-
-    // ---- S^T = K Q^T for the 64 keys of the tile (two 32-key blocks)
-    f32x16 s[kBC / 32];
-#pragma unroll
-    for (int kb = 0; kb < kBC / 32; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int krow = kb * 32 + key_of_row(l32);
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = as_bf16x8(ld16(kbuf + (krow * SM::kStride + ks * 16 + hi * 8) * 2));
-        s[kb] = mfma32(a, qf[ks], s[kb]);
-      }
-    }
-
-    // ---- mask the ragged end of the keys and the causal diagonal
     const bool need_mask = (kbase + kBC > Nk) || (CAUSAL && kbase + kBC - 1 > qw + shift);
     if (need_mask) {
       const int lim = CAUSAL ? min(Nk - 1, qi + shift) : Nk - 1;
 #pragma unroll
-      for (int kb = 0; kb < kBC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kbase + kb * 32 + key_of_reg(r, hi) > lim) s[kb][r] = kNegInf;
+      for (int r = 0; r < 16; ++r) {
+        if (kbase + key_of_reg(r, hi) > lim) sc0[r] = kNegInf;
+        if (kbase + 32 + key_of_reg(r, hi) > lim) sc1[r] = kNegInf;
+      }
     }
-
-    // ---- online softmax (base 2, scale folded into c = scale * log2 e)
-    // The running maximum is only moved when some row of the wave would exceed it by more than
-    // kRescaleSlack (in log2 units); otherwise the stale maximum is kept. Softmax is invariant
-    // to the reference value, so the result is the same up to rounding: probabilities are then
-    // bounded by 2^kRescaleSlack instead of 1, far inside fp32 and bf16 range, and the rescale
-    // of the accumulator (D/2 multiplies per lane) is skipped on most tiles.
-    float mx = kNegInf;
+    float mq[4];
 #pragma unroll
-    for (int kb = 0; kb < kBC / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = halves_max(mx) * c;
+    for (int j = 0; j < 4; ++j)
+      mq[j] = fmaxf(fmaxf(fmaxf(sc0[4 * j], sc0[4 * j + 1]), fmaxf(sc0[4 * j + 2], sc0[4 * j + 3])),
+                    fmaxf(fmaxf(sc1[4 * j], sc1[4 * j + 1]), fmaxf(sc1[4 * j + 2], sc1[4 * j + 3])));
+    const float mx = halves_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]))) * c;
     if (__any(mx > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2_fast(m_run - m_new);  // m_new is finite: key 0 of tile 0 is visible
+      const float m_new = fmaxf(m_run, mx);  // finite: key 0 of tile 0 is visible to every row
+      const float alpha = exp2_fast(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
       lq_run *= alpha;
@@ -239,48 +212,46 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const bf16* __restrict__ Q
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
-    const float m_use = m_run;
-    float psum = 0.f;
+    // Issued unconditionally so that it shares a basic block with the softmax below; past the
+    // last tile it reads stale (in-bounds) LDS and its result is never used.
+    qk(sn0, sn1, kbuf + ((t + 1) & 1) * L::KT);
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < kBC / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[kb][r] = exp2_fast(__builtin_fmaf(s[kb][r], c, -m_use));
-        psum += s[kb][r];
-      }
-    l_run += psum;
-
-    // P goes to the second product in bf16. The normaliser of O is the row sum of those same
-    // bf16 values (one v_dot2_f32_bf16 against (1, 1) per pair), so O is an exact convex
-    // combination of V rows under the rounded weights: its error becomes
-    // sum_j w_j e_j (v_j - O) instead of sum_j w_j e_j v_j, much smaller when a few keys dominate
-    // a row. The log-sum-exp keeps the fp32 sum.
-    bf16x8 pf[kBC / 16];
-    float qsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < kBC / 32; ++kb)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int r0 = 8 * tt;
-        pf[kb * 2 + tt] = pack_bf16x8(s[kb][r0], s[kb][r0 + 1], s[kb][r0 + 2], s[kb][r0 + 3],
-                                      s[kb][r0 + 4], s[kb][r0 + 5], s[kb][r0 + 6], s[kb][r0 + 7]);
-        qsum = sum_bf16x8(pf[kb * 2 + tt], qsum);
-      }
-    lq_run += qsum;
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int d = db * 32 + l32;
-#pragma unroll
-      for (int st = 0; st < kBC / 16; ++st) {
-        const bf16x8 a = as_bf16x8(ld16(vbuf + vt_offset(d, 2 * st + hi)));
-        oacc[db] = mfma32(a, pf[st], oacc[db]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      sc0[r] = exp2_fast(__builtin_fmaf(sc0[r], c, -m_run));
+      sc1[r] = exp2_fast(__builtin_fmaf(sc1[r], c, -m_run));
+      ps[r & 3] += sc0[r] + sc1[r];
     }
-  }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    bf16x8 pf[4];
+    pf[0] = pack_bf16x8(sc0[0], sc0[1], sc0[2], sc0[3], sc0[4], sc0[5], sc0[6], sc0[7]);
+    pf[1] = pack_bf16x8(sc0[8], sc0[9], sc0[10], sc0[11], sc0[12], sc0[13], sc0[14], sc0[15]);
+    pf[2] = pack_bf16x8(sc1[0], sc1[1], sc1[2], sc1[3], sc1[4], sc1[5], sc1[6], sc1[7]);
+    pf[3] = pack_bf16x8(sc1[8], sc1[9], sc1[10], sc1[11], sc1[12], sc1[13], sc1[14], sc1[15]);
+    lq_run += (sum_bf16x8(pf[0], 0.f) + sum_bf16x8(pf[1], 0.f)) +
+              (sum_bf16x8(pf[2], 0.f) + sum_bf16x8(pf[3], 0.f));
+    const unsigned char* vt = vbuf + (t & 1) * L::VT;
+#pragma unroll
+    for (int st = 0; st < kBC / 16; ++st)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32(vt_frag(vt, st, db), pf[st], oacc[db]);
+  };
 
-  // ---- epilogue: O = acc / l, L = ln 2 * (m + log2 l)
+  f32x16 sa0, sa1, sb0, sb1;
+  copy_k(0);
+  copy_v(0);
+  if (ntiles > 1) copy_k(1);
+  wait_vmem();
+  __syncthreads();
+  qk(sa0, sa1, kbuf);
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(sa0, sa1, sb0, sb1, t);
+    step(sb0, sb1, sa0, sa1, t + 1);
+  }
+  if (t < ntiles) step(sa0, sa1, sb0, sb1, t);
+
+  // ---- epilogue: O = acc / lq, L = ln 2 * (m + log2 l)
   const float l_tot = halves_sum(l_run);
   const float lq_tot = halves_sum(lq_run);
   if (qi < Nq) {
@@ -297,6 +268,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const bf16* __restrict__ Q
       }
     if (hi == 0) LSE[(size_t)bh * Nq + qi] = (m_run + log2_fast(l_tot)) * kLn2;
   }
+#endif
 }
 
 template <int D, int NW, bool CAUSAL>
