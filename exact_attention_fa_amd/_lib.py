@@ -24,9 +24,9 @@ SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _P]),
-    "fa_bwd_preprocess": (_I, [_P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
-    "fa_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _P]),
-    "fa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_preprocess": (_I, [_P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _P]),
+    "fa_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_num_splits": (_I, [_I, _I, _I, _I]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
@@ -138,20 +138,27 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
 def bwd_phase(phase: str, q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool = False,
               scale: float | None = None) -> None:
     """Run one backward phase ("preprocess", "dkdv" or "dq") into preallocated outputs."""
+    import torch
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
+    for t, n, shp in ((q, "q", (B, H, Nq, d)), (k, "k", (B, H, Nk, d)), (v, "v", (B, H, Nk, d)),
+                      (o, "o", (B, H, Nq, d)), (dout, "dout", (B, H, Nq, d)),
+                      (dq, "dq", (B, H, Nq, d)), (dk, "dk", (B, H, Nk, d)),
+                      (dv, "dv", (B, H, Nk, d))):
+        _need(t, n, shp, torch.bfloat16)
+    _need(lse, "lse", (B, H, Nq), torch.float32)
     lib = load()
     ws, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     sc, ca, st = _scale(scale, d), int(bool(causal)), _stream(q)
     if phase == "preprocess":
-        r = lib.fa_bwd_preprocess(o.data_ptr(), dout.data_ptr(), ws, wsb, B, H, Nq, Nk, d, st)
+        r = lib.fa_bwd_preprocess(o.data_ptr(), lse.data_ptr(), dout.data_ptr(), ws, wsb, B, H,
+                                  Nq, Nk, d, st)
     elif phase == "dkdv":
-        r = lib.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
-                            dout.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws, wsb, B, H, Nq, Nk,
-                            d, sc, ca, st)
+        r = lib.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                            dk.data_ptr(), dv.data_ptr(), ws, wsb, B, H, Nq, Nk, d, sc, ca, st)
     elif phase == "dq":
-        r = lib.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
-                          dout.data_ptr(), dq.data_ptr(), ws, wsb, B, H, Nq, Nk, d, sc, ca, st)
+        r = lib.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                          dq.data_ptr(), ws, wsb, B, H, Nq, Nk, d, sc, ca, st)
     else:
         raise ValueError(phase)
     _check("fa_bwd_" + phase, r)

@@ -63,26 +63,27 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d) {
   (void)N_k;
   (void)d;
   if (B < 1 || H < 1 || N_q < 1) return 0;
-  return round_up16((size_t)B * H * N_q * sizeof(float));
+  // D then L2 = LSE log2(e), each [B, H, N_q] fp32 padded to 16 bytes
+  return 2 * round_up16((size_t)B * H * N_q * sizeof(float));
 }
 
 namespace {
 
 // Shared validation of fa_bwd and its phases; `need` says which pointers the phase uses
-// (bit 0: o, 1: q/k/v/lse, 2: dk/dv, 3: dq; dout and the workspace are always used).
+// (bit 0: o and lse, 1: q/k/v, 2: dk/dv, 3: dq; dout and the workspace are always used).
 fa_status bwd_checked(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
                       const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk,
                       fa_bf16* dv, void* workspace, size_t workspace_bytes, int B, int H,
                       int N_q, int N_k, int d, float scale, int causal, hipStream_t stream,
                       unsigned need, unsigned phases) {
   const bool use_o = need & 1u, use_qkv = need & 2u, use_kv_out = need & 4u, use_q_out = need & 8u;
-  if (!dout || (use_o && !o) || (use_qkv && (!q || !k || !v || !lse)) ||
+  if (!dout || (use_o && (!o || !lse)) || (use_qkv && (!q || !k || !v)) ||
       (use_kv_out && (!dk || !dv)) || (use_q_out && !dq))
     return FA_ERR_NULL;
   fa_status s = check_common(B, H, N_q, N_k, d, scale, causal);
   if (s != FA_OK) return s;
-  if (!aligned16(dout) || (use_o && !aligned16(o)) ||
-      (use_qkv && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse))) ||
+  if (!aligned16(dout) || (use_o && (!aligned16(o) || !aligned16(lse))) ||
+      (use_qkv && (!aligned16(q) || !aligned16(k) || !aligned16(v))) ||
       (use_kv_out && (!aligned16(dk) || !aligned16(dv))) || (use_q_out && !aligned16(dq)))
     return FA_ERR_ALIGN;
   if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, N_q, N_k, d))
@@ -103,27 +104,26 @@ fa_status fa_bwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_
                      N_k, d, scale, causal, stream, 15u, 7u);
 }
 
-fa_status fa_bwd_preprocess(const fa_bf16* o, const fa_bf16* dout, void* workspace,
-                            size_t workspace_bytes, int B, int H, int N_q, int N_k, int d,
-                            hipStream_t stream) {
+fa_status fa_bwd_preprocess(const fa_bf16* o, const float* lse, const fa_bf16* dout,
+                            void* workspace, size_t workspace_bytes, int B, int H, int N_q,
+                            int N_k, int d, hipStream_t stream) {
   // scale and causal play no part in D; pass valid values to the shared checks
-  return bwd_checked(nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr, nullptr,
+  return bwd_checked(nullptr, nullptr, nullptr, o, lse, dout, nullptr, nullptr, nullptr,
                      workspace, workspace_bytes, B, H, N_q, N_k, d, 1.f, 0, stream, 1u, 1u);
 }
 
-fa_status fa_bwd_dkdv(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const float* lse,
+fa_status fa_bwd_dkdv(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v,
                       const fa_bf16* dout, fa_bf16* dk, fa_bf16* dv, void* workspace,
                       size_t workspace_bytes, int B, int H, int N_q, int N_k, int d, float scale,
                       int causal, hipStream_t stream) {
-  return bwd_checked(q, k, v, nullptr, lse, dout, nullptr, dk, dv, workspace, workspace_bytes, B,
-                     H, N_q, N_k, d, scale, causal, stream, 6u, 2u);
+  return bwd_checked(q, k, v, nullptr, nullptr, dout, nullptr, dk, dv, workspace,
+                     workspace_bytes, B, H, N_q, N_k, d, scale, causal, stream, 6u, 2u);
 }
 
-fa_status fa_bwd_dq(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const float* lse,
-                    const fa_bf16* dout, fa_bf16* dq, void* workspace, size_t workspace_bytes,
-                    int B, int H, int N_q, int N_k, int d, float scale, int causal,
-                    hipStream_t stream) {
-  return bwd_checked(q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, workspace,
+fa_status fa_bwd_dq(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* dout,
+                    fa_bf16* dq, void* workspace, size_t workspace_bytes, int B, int H, int N_q,
+                    int N_k, int d, float scale, int causal, hipStream_t stream) {
+  return bwd_checked(q, k, v, nullptr, nullptr, dout, dq, nullptr, nullptr, workspace,
                      workspace_bytes, B, H, N_q, N_k, d, scale, causal, stream, 10u, 4u);
 }
 

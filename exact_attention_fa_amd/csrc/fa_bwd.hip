@@ -7,10 +7,11 @@
 // dS = P * (dP - D) with dP = dO V^T. Then dV = P^T dO, dK = scale dS^T Q, dQ = scale dS K.
 //
 // Three kernels on one stream:
-//   1. bwd_delta:  D_i = sum_k dO_ik O_ik (HBM-bound, one pass over O and dO);
+//   1. bwd_delta:  D_i = sum_k dO_ik O_ik, and L2_i = L_i log2(e) (the log-sum-exp in the base-2
+//                  units the exponentials use); one pass over O and dO, HBM-bound;
 //   2. bwd_dkdv:   one workgroup per (b, h, 128-key tile); each wave keeps 32 keys' K and V
 //                  fragments and fp32 dK, dV accumulators in registers and streams the query
-//                  tiles (Q, dO, L, D) through LDS;
+//                  tiles (Q, dO, L2, D) through LDS;
 //   3. bwd_dq:     one workgroup per (b, h, 128-query tile); each wave keeps 32 queries' Q and dO
 //                  fragments and an fp32 dQ accumulator in registers and streams K/V tiles.
 // Splitting dQ into its own pass recomputes S and dP a second time (7 products where a fused
@@ -20,73 +21,68 @@
 // is S = Q K^T (lane = key, registers = queries) so that P and dS are directly the B operands of
 // dV^T = dO^T P and dK^T = Q^T dS, whose A operands (the transposes of the dO and Q tiles) come
 // from ds_read_b64_tr_b16. The dQ kernel mirrors the forward: S^T = K Q^T (lane = query), and
-// dQ^T = K^T dS^T takes K^T the same way. LDS tiles are row-major with XOR-swizzled 16-byte
-// chunks and double-buffered; the next tile's global loads are issued before the current math.
+// dQ^T = K^T dS^T takes K^T the same way. Tiles are copied HBM/L2 -> LDS by
+// buffer_load_dwordx4 ... lds (rows past the end read as zero) into padded rows whose stride makes
+// both the 16-byte row reads and the 4-row transposing reads free of bank conflicts, so every LDS
+// address is a per-lane base plus a compile-time offset. Tiles are double-buffered, one ahead.
 #include "fa_device.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
-constexpr int kNW = 4;     // waves per workgroup
+constexpr int kNW = 4;  // waves per workgroup
 constexpr int kNT = kNW * 64;
 
-// ---------------------------------------------------------------------------------------------
-// 1. D = rowsum(dO * O)
+// Row stride (bytes) of a [rows][D] bf16 tile read both by 16-byte row reads from 16 rows and by
+// 4-row x 32-byte transposing reads: the stride in 4-byte words is 4 mod 8 (16 row reads hit 16
+// distinct 16-byte bank groups) and 4 consecutive rows start in disjoint 32-byte windows.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__ O,
-                                                        const bf16* __restrict__ dO,
-                                                        float* __restrict__ delta, int rows) {
-  constexpr int G = D / 8;           // lanes per row
-  constexpr int RPB = 256 / G;       // rows per block pass
-  const int g = threadIdx.x / G, gl = threadIdx.x % G;
-  for (int row = blockIdx.x * RPB + g; row < rows; row += gridDim.x * RPB) {
-    const u32x4 a = ld16_nt(O + (size_t)row * D + gl * 8);
-    const u32x4 b = ld16_nt(dO + (size_t)row * D + gl * 8);
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t aw = a[w], bw = b[w];
-      s = __builtin_fmaf(bf16_lo(aw), bf16_lo(bw), s);
-      s = __builtin_fmaf(bf16_hi(aw), bf16_hi(bw), s);
-    }
-    s = group_sum<G>(s);
-    if (gl == 0) delta[row] = s;
-  }
-}
+constexpr int dual_stride() { return D == 128 ? 2 * D + 48 : 2 * D + 16; }
+// Row stride for tiles read only by 16-byte row reads.
+template <int D>
+constexpr int row_stride() { return 2 * D + 16; }
 
-// ---------------------------------------------------------------------------------------------
-// Global -> register -> LDS staging of a [ROWS][D] row-major bf16 tile (rows past `nrows` zero).
-template <int D, int ROWS>
-struct TileStage {
-  static constexpr int kChunks = ROWS * D / 8 / kNT;
-  static_assert(kChunks >= 1, "tile smaller than the workgroup");
-  u32x4 r[kChunks];
-  __device__ __forceinline__ void load(const bf16* src, int row0, int nrows, int tid) {
+// Wave-wide copies that fill a [64][D] bf16 tile with row stride ST: copy p covers 16-byte chunk
+// positions 64 p .. 64 p + 63; pad positions re-read chunk 0 of their row.
+template <int D, int ST>
+struct PaddedTile {
+  static constexpr int kCpr = ST / 16;          // chunks per row including pad
+  static constexpr int kCopies = 64 * kCpr / 64;
+  static constexpr int kPerWave = (kCopies + kNW - 1) / kNW;
+  static constexpr int kBytes = 64 * ST;
+  int off[kPerWave];
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int it = tid + i * kNT;
-      const int row = it / (D / 8), ch = it % (D / 8);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row0 + row < nrows) x = ld16(src + (size_t)(row0 + row) * D + ch * 8);
-      r[i] = x;
+    for (int i = 0; i < kPerWave; ++i) {
+      const int p = (wave + i * kNW) * 64 + lane, row = p / kCpr, ch = p % kCpr;
+      off[i] = row * D * 2 + (ch < D / 8 ? ch : 0) * 16;
     }
   }
-  __device__ __forceinline__ void store(unsigned char* dst, int tid) const {
+  // rows [row0, row0 + 64) of a [nrows][D] tensor starting at base
+  __device__ __forceinline__ void copy(const bf16* base, int row0, int nrows, unsigned char* dst,
+                                      int wave) const {
+    const auto r = make_rsrc(base + (size_t)row0 * D, max(0, nrows - row0) * D * 2);
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int it = tid + i * kNT;
-      const int row = it / (D / 8), ch = it % (D / 8);
-      st16(dst + tile_off<D>(row, ch * 8), r[i]);
-    }
+    for (int i = 0; i < kPerWave; ++i)
+      if (wave + i * kNW < kCopies) buffer_to_lds(r, dst + (wave + i * kNW) * 1024, off[i]);
   }
 };
 
-// Store an fp32 accumulator tile held as D^T (lane = sequence row `row`, registers = dims
-// 32 db + 8 j + 4 h + i) to a bf16 [.][D] tensor, multiplied by `mul`.
+// 64 floats (rows [row0, row0 + 64) of a [nrows] fp32 vector) -> LDS by the 16 first lanes.
+__device__ __forceinline__ void copy_row_vec(const float* base, int row0, int nrows,
+                                             unsigned char* dst, int lane) {
+  if (lane < 16) {
+    const auto r = make_rsrc(base + row0, max(0, nrows - row0) * 4);
+    buffer_to_lds(r, dst, lane * 16);
+  }
+}
+
+// Store an fp32 accumulator tile held as X^T (lane = sequence row, registers = dims
+// 32 db + 8 j + 4 h + i) to one bf16 row of a [.][D] tensor, multiplied by `mul`.
 template <int D>
-__device__ __forceinline__ void store_rows(bf16* dst_row, const f32x16 (&acc)[D / 32], float mul,
-                                           int hi) {
+__device__ __forceinline__ void store_row(bf16* dst_row, const f32x16 (&acc)[D / 32], float mul,
+                                          int hi) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -109,40 +105,81 @@ __device__ __forceinline__ void xcd_map(int bid, int BH, int& bh, int& rank) {
   }
 }
 
+// Per-lane base offset of the ds_read_b64_tr_b16 pair that assembles a transposed 16-row x
+// 32-column block of a tile with row stride ST: within each group of 16 lanes, input lane j reads
+// row 8 h + (j >> 2), columns 16 (group & 1) + 4 (j & 3).
+template <int ST>
+__device__ __forceinline__ int tr_base(int lane) {
+  const int j = lane & 15, grp = lane >> 4;
+  return (8 * (grp >> 1) + (j >> 2)) * ST + (16 * (grp & 1) + 4 * (j & 3)) * 2;
+}
+
+// ---------------------------------------------------------------------------------------------
+// 1. D = rowsum(dO * O) and L2 = L log2(e)
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__ O,
+                                                        const bf16* __restrict__ dO,
+                                                        const float* __restrict__ LSE,
+                                                        float* __restrict__ delta,
+                                                        float* __restrict__ lse2, int rows) {
+  constexpr int G = D / 8;      // lanes per row
+  constexpr int RPB = 256 / G;  // rows per block pass
+  const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  for (int row = blockIdx.x * RPB + g; row < rows; row += gridDim.x * RPB) {
+    const u32x4 a = ld16_nt(O + (size_t)row * D + gl * 8);
+    const u32x4 b = ld16_nt(dO + (size_t)row * D + gl * 8);
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t aw = a[w], bw = b[w];
+      s = __builtin_fmaf(bf16_lo(aw), bf16_lo(bw), s);
+      s = __builtin_fmaf(bf16_hi(aw), bf16_hi(bw), s);
+    }
+    s = group_sum<G>(s);
+    if (gl == 0) {
+      delta[row] = s;
+      lse2[row] = LSE[row] * kLog2e;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // 2. dK, dV
 constexpr int kBKV = 128;  // keys per workgroup (32 per wave)
 constexpr int kBQ = 64;    // queries per streamed tile
 
 template <int D>
-struct DkdvSmem {
-  static constexpr int kTile = kBQ * D * 2;
-  static constexpr int kQ = 0, kDO = kTile, kL = 2 * kTile, kDl = 2 * kTile + kBQ * 4;
-  static constexpr int kBuf = 2 * kTile + 2 * kBQ * 4;
+struct DkdvLds {
+  static constexpr int ST = dual_stride<D>();
+  using Tile = PaddedTile<D, ST>;
+  static constexpr int kQ = 0, kDO = Tile::kBytes, kL = 2 * Tile::kBytes, kDl = kL + kBQ * 4;
+  static constexpr int kBuf = kDl + kBQ * 4;
   static constexpr int kBytes = 2 * kBuf;
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kNT) void bwd_dkdv_kernel(
+__global__ __attribute__((amdgpu_waves_per_eu(1, 1))) __launch_bounds__(kNT) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
+    const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
     bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int Nq, int Nk, float c, float scale) {
-  using SM = DkdvSmem<D>;
+#if defined(__HIP_DEVICE_COMPILE__)
+  using SM = DkdvLds<D>;
+  constexpr int ST = SM::ST;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SM::kBytes];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
   int bh, rank;
   xcd_map(blockIdx.x, BH, bh, rank);
-  const int kt = rank;  // causal: low key tiles see the most queries and are launched first
-  const int k0 = kt * kBKV;
+  const int k0 = rank * kBKV;  // causal: low key tiles see the most queries and go first
   const int kw = k0 + wave * 32;
   const int key = kw + l32;
-  const int shift = Nk - Nq;
+  const int shift = Nk - Nq;  // causal: key j visible to query i iff j <= i + shift
 
   const bf16* Qh = Q + (size_t)bh * Nq * D;
   const bf16* dOh = dO + (size_t)bh * Nq * D;
-  const float* Lh = LSE + (size_t)bh * Nq;
+  const float* Lh = L2 + (size_t)bh * Nq;
   const float* Dh = Dl + (size_t)bh * Nq;
 
   // resident B operands: K^T and V^T columns (lane = key, 8 dims per k-step)
@@ -167,44 +204,34 @@ __global__ __launch_bounds__(kNT) void bwd_dkdv_kernel(
     }
 
   // query tiles that can see any key of this workgroup
-  int qbeg = 0;
-  if (CAUSAL) qbeg = max(0, k0 - shift);
-  const int t0 = qbeg / kBQ;
+  const int t0 = CAUSAL ? max(0, k0 - shift) / kBQ : 0;
   const int t1 = (Nq + kBQ - 1) / kBQ;
 
-  TileStage<D, kBQ> sq, sdo;
-  float lreg = 0.f, dreg = 0.f;
-  auto load = [&](int t) {
+  typename SM::Tile tile;
+  tile.init(wave, lane);
+  auto copy = [&](int t) {
+    unsigned char* b = smem + ((t - t0) & 1) * SM::kBuf;
     const int q0 = t * kBQ;
-    sq.load(Qh, q0, Nq, tid);
-    sdo.load(dOh, q0, Nq, tid);
-    if (tid < kBQ) {
-      const int q = q0 + tid;
-      // rows past N_q get L = +inf, so their probabilities are exactly zero
-      lreg = q < Nq ? Lh[q] * kLog2e : __builtin_huge_valf();
-      dreg = q < Nq ? Dh[q] : 0.f;
-    }
+    tile.copy(Qh, q0, Nq, b + SM::kQ, wave);
+    tile.copy(dOh, q0, Nq, b + SM::kDO, wave);
+    if (wave == 0) copy_row_vec(Lh, q0, Nq, b + SM::kL, lane);
+    if (wave == 1) copy_row_vec(Dh, q0, Nq, b + SM::kDl, lane);
   };
-  auto store = [&](int buf) {
-    unsigned char* b = smem + buf * SM::kBuf;
-    sq.store(b + SM::kQ, tid);
-    sdo.store(b + SM::kDO, tid);
-    if (tid < kBQ) {
-      reinterpret_cast<float*>(b + SM::kL)[tid] = lreg;
-      reinterpret_cast<float*>(b + SM::kDl)[tid] = dreg;
-    }
-  };
+  // rows past N_q read as zero: their Q and dO rows are zero and L2 = D = 0, so P = 1, dP = 0
+  // and dS = 0: they add nothing to dK or dV.
 
-  if (t0 < t1) load(t0);
+  const int qrow = key_of_row(l32) * ST + hi * 16;  // A operand of S and dP: row reads
+  const int trb = tr_base<ST>(lane);                 // A operand of dV^T and dK^T: transposed
+
+  if (t0 < t1) copy(t0);
   for (int t = t0; t < t1; ++t) {
-    const int buf = (t - t0) & 1;
-    store(buf);
+    wait_vmem();
     __syncthreads();
-    if (t + 1 < t1) load(t + 1);
+    if (t + 1 < t1) copy(t + 1);
     const int q0 = t * kBQ;
     // every query of the tile is before this wave's first visible position: nothing to do
     if (CAUSAL && min(q0 + kBQ, Nq) - 1 + shift < kw) continue;
-    const unsigned char* b = smem + buf * SM::kBuf;
+    const unsigned char* b = smem + ((t - t0) & 1) * SM::kBuf;
     const float* ls = reinterpret_cast<const float*>(b + SM::kL);
     const float* dls = reinterpret_cast<const float*>(b + SM::kDl);
     const bool need_mask = CAUSAL && (q0 + shift < kw + 31);
@@ -216,19 +243,14 @@ __global__ __launch_bounds__(kNT) void bwd_dkdv_kernel(
         s[r] = 0.f;
         dp[r] = 0.f;
       }
-      const int qrow = qb * 32 + key_of_row(l32);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = as_bf16x8(ld16(b + SM::kQ + tile_off<D>(qrow, ks * 16 + hi * 8)));
-        s = mfma32(a, kf[ks], s);
+        const int off = qrow + qb * 32 * ST + ks * 32;
+        s = mfma32(as_bf16x8(ld16(b + SM::kQ + off)), kf[ks], s);
+        dp = mfma32(as_bf16x8(ld16(b + SM::kDO + off)), vf[ks], dp);
       }
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = as_bf16x8(ld16(b + SM::kDO + tile_off<D>(qrow, ks * 16 + hi * 8)));
-        dp = mfma32(a, vf[ks], dp);
-      }
-      // P = exp2(c S - L log2 e), dS = P (dP - D); queries of register r: qb*32 + key_of_reg(r, hi)
-      float p[16], ds[16];
+      // queries of register r: qb*32 + key_of_reg(r, hi) = qb*32 + 16 (r >> 3) + 8 hi + (r & 7)
+      bf16x8 pf[2], dsf[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int qi0 = qb * 32 + 16 * half + 8 * hi;
@@ -236,42 +258,35 @@ __global__ __launch_bounds__(kNT) void bwd_dkdv_kernel(
         const f32x4 lb = *reinterpret_cast<const f32x4*>(ls + qi0 + 4);
         const f32x4 da = *reinterpret_cast<const f32x4*>(dls + qi0);
         const f32x4 db4 = *reinterpret_cast<const f32x4*>(dls + qi0 + 4);
+        float p[8], ds[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * half + e;
-          const float lv = e < 4 ? la[e] : lb[e - 4];
-          const float dv4 = e < 4 ? da[e] : db4[e - 4];
-          float pv = exp2_fast(__builtin_fmaf(s[r], c, -lv));
+          float pv = exp2_fast(__builtin_fmaf(s[r], c, -(e < 4 ? la[e] : lb[e - 4])));
           if (need_mask && key > q0 + qi0 + e + shift) pv = 0.f;
-          p[r] = pv;
-          ds[r] = pv * (dp[r] - dv4);
+          p[e] = pv;
+          ds[e] = pv * (dp[r] - (e < 4 ? da[e] : db4[e - 4]));
         }
-      }
-      bf16x8 pf[2], dsf[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        pf[st] = pack_bf16x8(p[8 * st], p[8 * st + 1], p[8 * st + 2], p[8 * st + 3], p[8 * st + 4],
-                             p[8 * st + 5], p[8 * st + 6], p[8 * st + 7]);
-        dsf[st] = pack_bf16x8(ds[8 * st], ds[8 * st + 1], ds[8 * st + 2], ds[8 * st + 3],
-                              ds[8 * st + 4], ds[8 * st + 5], ds[8 * st + 6], ds[8 * st + 7]);
+        pf[half] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+        dsf[half] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
       }
       // dV^T += dO^T P and dK^T += Q^T dS (A operands: transposed 32-dim x 16-query blocks)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const bf16x8 ao = lds_read_transposed<D>(b + SM::kDO, qb * 32 + 16 * st, db * 32, lane);
-          dv[db] = mfma32(ao, pf[st], dv[db]);
-          const bf16x8 aq = lds_read_transposed<D>(b + SM::kQ, qb * 32 + 16 * st, db * 32, lane);
-          dk[db] = mfma32(aq, dsf[st], dk[db]);
+        for (int db = 0; db < D / 32; ++db) {
+          const int off = trb + (qb * 32 + 16 * st) * ST + db * 64;
+          dv[db] = mfma32(lds_read_tr_pair(b + SM::kDO + off, 4 * ST), pf[st], dv[db]);
+          dk[db] = mfma32(lds_read_tr_pair(b + SM::kQ + off, 4 * ST), dsf[st], dk[db]);
         }
     }
   }
 
   if (key < Nk) {
-    store_rows<D>(dK + ((size_t)bh * Nk + key) * D, dk, scale, hi);
-    store_rows<D>(dV + ((size_t)bh * Nk + key) * D, dv, 1.f, hi);
+    store_row<D>(dK + ((size_t)bh * Nk + key) * D, dk, scale, hi);
+    store_row<D>(dV + ((size_t)bh * Nk + key) * D, dv, 1.f, hi);
   }
+#endif
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -280,21 +295,25 @@ constexpr int kBR = 128;  // queries per workgroup (32 per wave)
 constexpr int kBC = 64;   // keys per streamed tile
 
 template <int D>
-struct DqSmem {
-  static constexpr int kTile = kBC * D * 2;
-  static constexpr int kK = 0, kV = kTile;
-  static constexpr int kBuf = 2 * kTile;
+struct DqLds {
+  static constexpr int KST = dual_stride<D>(), VST = row_stride<D>();
+  using KTile = PaddedTile<D, KST>;
+  using VTile = PaddedTile<D, VST>;
+  static constexpr int kK = 0, kV = KTile::kBytes;
+  static constexpr int kBuf = KTile::kBytes + VTile::kBytes;
   static constexpr int kBytes = 2 * kBuf;
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kNT) void bwd_dq_kernel(
+__global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
+    const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
     bf16* __restrict__ dQ, int BH, int Nq, int Nk, float c, float scale) {
-  using SM = DqSmem<D>;
+#if defined(__HIP_DEVICE_COMPILE__)
+  using SM = DqLds<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SM::kBytes];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
   int bh, rank;
@@ -321,7 +340,7 @@ __global__ __launch_bounds__(kNT) void bwd_dq_kernel(
     qf[ks] = as_bf16x8(a);
     dof[ks] = as_bf16x8(b);
   }
-  const float lq = qi < Nq ? LSE[(size_t)bh * Nq + qi] * kLog2e : 0.f;
+  const float lq = qi < Nq ? L2[(size_t)bh * Nq + qi] : 0.f;
   const float dq_d = qi < Nq ? Dl[(size_t)bh * Nq + qi] : 0.f;
 
   f32x16 acc[D / 32];
@@ -331,55 +350,59 @@ __global__ __launch_bounds__(kNT) void bwd_dq_kernel(
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
   int kend = Nk;
-  if (CAUSAL) kend = min(Nk, min(q0 + kBR, Nq) - 1 + shift + 1);
+  if (CAUSAL) kend = min(Nk, min(q0 + kBR, Nq) + shift);
   const int ntiles = (kend + kBC - 1) / kBC;
-  const int wave_horizon = CAUSAL ? min(qw + 31, Nq - 1) + shift : Nk - 1;
+  const int horizon = CAUSAL ? min(qw + 31, Nq - 1) + shift : Nk - 1;
 
-  TileStage<D, kBC> sk, sv;
-  if (ntiles > 0) {
-    sk.load(Kh, 0, Nk, tid);
-    sv.load(Vh, 0, Nk, tid);
-  }
+  typename SM::KTile ktile;
+  typename SM::VTile vtile;
+  ktile.init(wave, lane);
+  vtile.init(wave, lane);
+  auto copy = [&](int t) {
+    unsigned char* b = smem + (t & 1) * SM::kBuf;
+    ktile.copy(Kh, t * kBC, Nk, b + SM::kK, wave);
+    vtile.copy(Vh, t * kBC, Nk, b + SM::kV, wave);
+  };
+  const int krow = key_of_row(l32);
+  const int kro = krow * SM::KST + hi * 16, vro = krow * SM::VST + hi * 16;
+  const int trb = tr_base<SM::KST>(lane);
+
+  if (ntiles > 0) copy(0);
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    unsigned char* b = smem + buf * SM::kBuf;
-    sk.store(b + SM::kK, tid);
-    sv.store(b + SM::kV, tid);
+    wait_vmem();
     __syncthreads();
-    if (t + 1 < ntiles) {
-      sk.load(Kh, (t + 1) * kBC, Nk, tid);
-      sv.load(Vh, (t + 1) * kBC, Nk, tid);
-    }
+    if (t + 1 < ntiles) copy(t + 1);
     const int kbase = t * kBC;
-    if (kbase > wave_horizon) continue;
+    if (kbase > horizon) continue;
+    const unsigned char* b = smem + (t & 1) * SM::kBuf;
     const bool need_mask = (kbase + kBC > Nk) || (CAUSAL && kbase + kBC - 1 > qw + shift);
     const int lim = CAUSAL ? min(Nk - 1, qi + shift) : Nk - 1;
-    bf16x8 dsf[kBC / 16];
+    f32x16 s[2], dp[2];
 #pragma unroll
-    for (int kb = 0; kb < kBC / 32; ++kb) {
-      f32x16 s, dp;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
-      const int krow = kb * 32 + key_of_row(l32);
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = as_bf16x8(ld16(b + SM::kK + tile_off<D>(krow, ks * 16 + hi * 8)));
-        s = mfma32(a, qf[ks], s);
+        s[kb][r] = 0.f;
+        dp[kb][r] = 0.f;
       }
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = as_bf16x8(ld16(b + SM::kV + tile_off<D>(krow, ks * 16 + hi * 8)));
-        dp = mfma32(a, dof[ks], dp);
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = mfma32(as_bf16x8(ld16(b + SM::kK + kro + kb * 32 * SM::KST + ks * 32)), qf[ks],
+                       s[kb]);
+        dp[kb] = mfma32(as_bf16x8(ld16(b + SM::kV + vro + kb * 32 * SM::VST + ks * 32)),
+                        dof[ks], dp[kb]);
       }
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = exp2_fast(__builtin_fmaf(s[r], c, -lq));
+        float pv = exp2_fast(__builtin_fmaf(s[kb][r], c, -lq));
         if (need_mask && kbase + kb * 32 + key_of_reg(r, hi) > lim) pv = 0.f;
-        ds[r] = pv * (dp[r] - dq_d);
+        ds[r] = pv * (dp[kb][r] - dq_d);
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
@@ -389,15 +412,16 @@ __global__ __launch_bounds__(kNT) void bwd_dq_kernel(
     }
     // dQ^T += K^T dS^T
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int st = 0; st < kBC / 16; ++st)
 #pragma unroll
-      for (int st = 0; st < kBC / 16; ++st) {
-        const bf16x8 a = lds_read_transposed<D>(b + SM::kK, 16 * st, db * 32, lane);
-        acc[db] = mfma32(a, dsf[st], acc[db]);
+      for (int db = 0; db < D / 32; ++db) {
+        const int off = trb + 16 * st * SM::KST + db * 64;
+        acc[db] = mfma32(lds_read_tr_pair(b + SM::kK + off, 4 * SM::KST), dsf[st], acc[db]);
       }
   }
 
-  if (qi < Nq) store_rows<D>(dQ + ((size_t)bh * Nq + qi) * D, acc, scale, hi);
+  if (qi < Nq) store_row<D>(dQ + ((size_t)bh * Nq + qi) * D, acc, scale, hi);
+#endif
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -406,11 +430,12 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
   const int BH = a.B * a.H;
   const float c = a.scale * kLog2e;
   const int rows = BH * a.Nq;
+  float* lse2 = a.delta + bwd_lse2_offset(a.B, a.H, a.Nq);
   if (phases & 1u) {
     constexpr int RPB = 256 / (D / 8);
-    int grid = (rows + RPB * 4 - 1) / (RPB * 4);
+    const int grid = (rows + RPB * 4 - 1) / (RPB * 4);
     hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3(grid), dim3(256), 0, a.stream, a.o, a.dout,
-                       a.delta, rows);
+                       a.lse, a.delta, lse2, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -418,7 +443,7 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
     const long long grid = (long long)BH * ((a.Nk + kBKV - 1) / kBKV);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kNT), 0, a.stream,
-                       a.q, a.k, a.v, a.dout, a.lse, a.delta, a.dk, a.dv, BH, a.Nq, a.Nk, c,
+                       a.q, a.k, a.v, a.dout, lse2, a.delta, a.dk, a.dv, BH, a.Nq, a.Nk, c,
                        a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -427,7 +452,7 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
     const long long grid = (long long)BH * ((a.Nq + kBR - 1) / kBR);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kNT), 0, a.stream,
-                       a.q, a.k, a.v, a.dout, a.lse, a.delta, a.dq, BH, a.Nq, a.Nk, c, a.scale);
+                       a.q, a.k, a.v, a.dout, lse2, a.delta, a.dq, BH, a.Nq, a.Nk, c, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -435,6 +460,11 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
 }
 
 }  // namespace
+
+size_t bwd_lse2_offset(int B, int H, int Nq) {
+  // D first, then L2, each padded to a multiple of 16 bytes (counted in floats)
+  return (((size_t)B * H * Nq + 3) / 4) * 4;
+}
 
 hipError_t launch_bwd(const BwdArgs& a, unsigned phases) {
   if (a.d == 128) return a.causal ? launch<128, true>(a, phases) : launch<128, false>(a, phases);

@@ -180,20 +180,30 @@ __device__ __forceinline__ bf16x8 lds_read_transposed(const unsigned char* tile,
 }
 
 // ---- HBM/L2 -> LDS copies without register staging ------------------------------------------
-#if defined(__HIP_DEVICE_COMPILE__)
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes return zero.
 // Word 3 is the gfx9-family raw-buffer configuration (32-bit data format, no swizzle).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+#else
+  (void)base;
+  (void)bytes;
+  __builtin_unreachable();  // device code: never executed by the host pass
+#endif
 }
 // buffer_load_dwordx4 ... lds: lane l of the wave writes its 16 bytes (from voffset) to
 // dst + 16 l. dst must be the same for the whole wave.
 __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* dst,
                                               int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
                                            voffset, 0, 0, 0);
-}
+#else
+  (void)r;
+  (void)dst;
+  (void)voffset;
 #endif
+}
 // Wait until this thread's outstanding vector-memory operations (including the LDS copies
 // above) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

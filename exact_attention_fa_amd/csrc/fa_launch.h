@@ -28,7 +28,7 @@ struct BwdArgs {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  float* delta;  // workspace: D = rowsum(dO * O), [B, H, Nq]
+  float* delta;  // workspace: D = rowsum(dO * O) [B, H, Nq], then L2 = LSE log2(e) [B, H, Nq]
   int B, H, Nq, Nk, d;
   float scale;
   bool causal;
@@ -49,6 +49,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
+// Offset (in floats) of L2 after D in the backward workspace.
+size_t bwd_lse2_offset(int B, int H, int Nq);
 // Backward phases; `phase_mask` bit 0 = D preprocess, bit 1 = dK/dV, bit 2 = dQ.
 hipError_t launch_bwd(const BwdArgs& a, unsigned phase_mask = 7u);
 hipError_t launch_decode(const DecodeArgs& a);

@@ -72,7 +72,8 @@ fa_status fa_fwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* 
                  int B, int H, int N_q, int N_k, int d, float scale, int causal,
                  hipStream_t stream);
 
-/* Bytes of device workspace fa_bwd needs (the fp32 row vector D = rowsum(dO * O)). */
+/* Bytes of device workspace fa_bwd needs: two fp32 row vectors [B, H, N_q], D = rowsum(dO * O)
+ * and the log-sum-exp in base-2 units, each padded to 16 bytes. */
 size_t fa_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d);
 
 /*
@@ -94,27 +95,23 @@ fa_status fa_bwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_
 
 /*
  * The three phases fa_bwd runs, exposed so that a caller can schedule or time them separately.
- * Same arguments, layouts, workspace and validation as fa_bwd; they must run in this order on
- * one stream (each reads what the previous one wrote into the workspace):
- *   fa_bwd_preprocess: D = rowsum(dO * O) into the workspace ("Geri Yayılım": D is taken from
- *                      the forward output);
- *   fa_bwd_dkdv:       dK and dV (reads D from the workspace);
- *   fa_bwd_dq:         dQ (reads D from the workspace).
- * Pointers a phase does not use may be NULL: preprocess uses o, dout and the workspace; dkdv
- * uses q, k, v, lse, dout, the workspace, dk and dv; dq uses q, k, v, lse, dout, the workspace
- * and dq.
+ * Same layouts, workspace and validation as fa_bwd; they must run in this order on one stream,
+ * since the later two read what the first writes into the workspace:
+ *   fa_bwd_preprocess: D = rowsum(dO * O) ("Geri Yayılım": D is taken from the forward output)
+ *                      and L2 = lse * log2(e) into the workspace; uses o, lse, dout;
+ *   fa_bwd_dkdv:       dK and dV; uses q, k, v, dout and the workspace;
+ *   fa_bwd_dq:         dQ; uses q, k, v, dout and the workspace.
  */
-fa_status fa_bwd_preprocess(const fa_bf16* o, const fa_bf16* dout, void* workspace,
-                            size_t workspace_bytes, int B, int H, int N_q, int N_k, int d,
-                            hipStream_t stream);
-fa_status fa_bwd_dkdv(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const float* lse,
+fa_status fa_bwd_preprocess(const fa_bf16* o, const float* lse, const fa_bf16* dout,
+                            void* workspace, size_t workspace_bytes, int B, int H, int N_q,
+                            int N_k, int d, hipStream_t stream);
+fa_status fa_bwd_dkdv(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v,
                       const fa_bf16* dout, fa_bf16* dk, fa_bf16* dv, void* workspace,
                       size_t workspace_bytes, int B, int H, int N_q, int N_k, int d, float scale,
                       int causal, hipStream_t stream);
-fa_status fa_bwd_dq(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const float* lse,
-                    const fa_bf16* dout, fa_bf16* dq, void* workspace, size_t workspace_bytes,
-                    int B, int H, int N_q, int N_k, int d, float scale, int causal,
-                    hipStream_t stream);
+fa_status fa_bwd_dq(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* dout,
+                    fa_bf16* dq, void* workspace, size_t workspace_bytes, int B, int H, int N_q,
+                    int N_k, int d, float scale, int causal, hipStream_t stream);
 
 /* The split count fa_decode uses when called with num_splits = 0. */
 int fa_decode_num_splits(int B, int H, int N_k, int d);

@@ -87,16 +87,18 @@ def test_bwd_validation(lib):
 
 def test_bwd_phase_validation(lib):
     ws = lib.fa_bwd_workspace_bytes(1, 2, 64, 64, 128)
-    assert lib.fa_bwd_preprocess(None, FAKE, FAKE, ws, 1, 2, 64, 64, 128, None) == 1
-    assert lib.fa_bwd_preprocess(FAKE, FAKE, FAKE, ws - 16, 1, 2, 64, 64, 128, None) == 6
-    assert lib.fa_bwd_preprocess(FAKE, FAKE, FAKE, ws, 1, 2, 64, 64, 48, None) == 3
-    assert lib.fa_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws, 1, 2, 64, 64, 128,
+    assert ws == 2 * 2 * 64 * 4
+    assert lib.fa_bwd_preprocess(None, FAKE, FAKE, FAKE, ws, 1, 2, 64, 64, 128, None) == 1
+    assert lib.fa_bwd_preprocess(FAKE, None, FAKE, FAKE, ws, 1, 2, 64, 64, 128, None) == 1
+    assert lib.fa_bwd_preprocess(FAKE, FAKE, FAKE, FAKE, ws - 16, 1, 2, 64, 64, 128, None) == 6
+    assert lib.fa_bwd_preprocess(FAKE, FAKE, FAKE, FAKE, ws, 1, 2, 64, 64, 48, None) == 3
+    assert lib.fa_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws, 1, 2, 64, 64, 128,
                            0.1, 0, None) == 1
-    assert lib.fa_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 1, 2, 65, 64, 128,
+    assert lib.fa_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 1, 2, 65, 64, 128,
                            0.1, 1, None) == 5
-    assert lib.fa_bwd_dq(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, 1, 2, 64, 64, 128, 0.1, 0,
+    assert lib.fa_bwd_dq(FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, 1, 2, 64, 64, 128, 0.1, 0,
                          None) == 1
-    assert lib.fa_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, ws, 1, 2, 64, 64, 128, 0.1,
+    assert lib.fa_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, ws, 1, 2, 64, 64, 128, 0.1,
                          0, None) == 4
 
 
