@@ -34,6 +34,9 @@ def compile_flags() -> list[str]:
         # no NaN ever flows through the kernels (inputs are finite and -inf - -inf is avoided),
         # so fmaxf needs no NaN canonicalisation and maps to v_max3_f32
         "-fno-honor-nans",
+        # MFMA results in VGPRs: the score tiles feed vector ALU work directly, and keeping the
+        # accumulators out of AGPRs avoids register-class copies in the backward kernels
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wall", "-Wno-unused-result",
     ]
 

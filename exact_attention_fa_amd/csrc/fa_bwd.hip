@@ -237,6 +237,9 @@ __global__ __attribute__((amdgpu_waves_per_eu(1, 1))) __launch_bounds__(kNT) voi
     const bool need_mask = CAUSAL && (q0 + shift < kw + 31);
 #pragma unroll
     for (int qb = 0; qb < kBQ / 32; ++qb) {
+      // keep the two 32-query blocks apart: overlapping them would double the live scores and
+      // push the register allocator into copying through AGPRs
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
