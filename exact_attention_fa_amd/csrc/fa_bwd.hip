@@ -158,7 +158,7 @@ struct DkdvLds {
 };
 
 template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_waves_per_eu(1, 1))) __launch_bounds__(kNT) void bwd_dkdv_kernel(
+__global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
     bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int Nq, int Nk, float c, float scale) {
