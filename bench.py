@@ -187,7 +187,7 @@ def main() -> int:
     f_fwd = metrics.attention_flops(B, H, N, N, d, causal=causal)
     f_bwd = metrics.attention_flops(B, H, N, N, d, causal=causal, backward=True)
     gemm = f_fwd / 2  # one N x N x d product, causal-halved
-    pre_bytes = 2 * B * H * N * d * 2 + B * H * N * 4
+    pre_bytes = 2 * B * H * N * d * 2 + B * H * N * 12  # O, dO, LSE read; D, LSE*log2(e) written
     dec_bytes = metrics.decode_bytes(DB, DH, DN, Dd)
 
     def mfma_entry(flops, t_ms, note):
@@ -205,7 +205,7 @@ def main() -> int:
         "bwd_dkdv": mfma_entry(4 * gemm, ms["bwd_dkdv"], "4 products (S, dP, dV, dK), causal"),
         "bwd_dq": mfma_entry(1 * gemm, ms["bwd_dq"],
                              "1 algorithmic product (dQ); it also re-runs S and dP"),
-        "bwd_preprocess": hbm_entry(pre_bytes, ms["bwd_preprocess"], "read O and dO, write D"),
+        "bwd_preprocess": hbm_entry(pre_bytes, ms["bwd_preprocess"], "read O, dO and LSE, write D and LSE*log2(e)"),
         "decode": hbm_entry(dec_bytes, ms["decode"],
                             "K and V read once + q, o, lse (split + combine kernels)"),
     }
