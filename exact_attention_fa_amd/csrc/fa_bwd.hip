@@ -28,6 +28,8 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -152,9 +154,9 @@ template <int D>
 struct DkdvLds {
   static constexpr int ST = dual_stride<D>();
   using Tile = PaddedTile<D, ST>;
+  // one buffer: Q tile, dO tile, L2 and D of its 64 rows
   static constexpr int kQ = 0, kDO = Tile::kBytes, kL = 2 * Tile::kBytes, kDl = kL + kBQ * 4;
   static constexpr int kBuf = kDl + kBQ * 4;
-  static constexpr int kBytes = 2 * kBuf;
 };
 
 template <int D, bool CAUSAL>
@@ -165,7 +167,10 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 #if defined(__HIP_DEVICE_COMPILE__)
   using SM = DkdvLds<D>;
   constexpr int ST = SM::ST;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SM::kBytes];
+  // one array per buffer, so that the LDS copies into one buffer provably do not alias the reads
+  // of the other and need no wait before those reads
+  __shared__ __attribute__((aligned(16))) unsigned char buf0[SM::kBuf];
+  __shared__ __attribute__((aligned(16))) unsigned char buf1[SM::kBuf];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -203,14 +208,16 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
       dv[db][r] = 0.f;
     }
 
-  // query tiles that can see any key of this workgroup
+  // query tiles that can see any key of this workgroup; the first ones (causal) cross the
+  // diagonal of some wave and are masked, from tm on every query sees every key of the workgroup
   const int t0 = CAUSAL ? max(0, k0 - shift) / kBQ : 0;
   const int t1 = (Nq + kBQ - 1) / kBQ;
+  int tm = t0;
+  if (CAUSAL) tm = min(t1, max(t0, (k0 + kBKV - 1 - shift + kBQ - 1) / kBQ));
 
   typename SM::Tile tile;
   tile.init(wave, lane);
-  auto copy = [&](int t) {
-    unsigned char* b = smem + ((t - t0) & 1) * SM::kBuf;
+  auto copy = [&](int t, unsigned char* b) {
     const int q0 = t * kBQ;
     tile.copy(Qh, q0, Nq, b + SM::kQ, wave);
     tile.copy(dOh, q0, Nq, b + SM::kDO, wave);
@@ -223,18 +230,22 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   const int qrow = key_of_row(l32) * ST + hi * 16;  // A operand of S and dP: row reads
   const int trb = tr_base<ST>(lane);                 // A operand of dV^T and dK^T: transposed
 
-  if (t0 < t1) copy(t0);
-  for (int t = t0; t < t1; ++t) {
-    wait_vmem();
-    __syncthreads();
-    if (t + 1 < t1) copy(t + 1);
-    const int q0 = t * kBQ;
-    // every query of the tile is before this wave's first visible position: nothing to do
-    if (CAUSAL && min(q0 + kBQ, Nq) - 1 + shift < kw) continue;
-    const unsigned char* b = smem + ((t - t0) & 1) * SM::kBuf;
+  // One query tile t from buffer P; the copies of tile t+1 go to the other buffer. MASKED: tiles
+  // that cross the causal diagonal of some wave (a wave whose keys all lie past the tile skips it).
+  auto step = [&](auto PAR, auto MASKED, int t) {
+    constexpr int P = decltype(PAR)::value;
+    constexpr bool MK = decltype(MASKED)::value;
+    const unsigned char* b = P ? buf1 : buf0;
+    const unsigned char* qt = b + SM::kQ;
+    const unsigned char* ot = b + SM::kDO;
     const float* ls = reinterpret_cast<const float*>(b + SM::kL);
     const float* dls = reinterpret_cast<const float*>(b + SM::kDl);
-    const bool need_mask = CAUSAL && (q0 + shift < kw + 31);
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < t1) copy(t + 1, P ? buf0 : buf1);
+    const int q0 = t * kBQ;
+    // every query of the tile is before this wave's first visible position: nothing to do
+    if (MK && min(q0 + kBQ, Nq) - 1 + shift < kw) return;
 #pragma unroll
     for (int qb = 0; qb < kBQ / 32; ++qb) {
       // keep the two 32-query blocks apart: overlapping them would double the live scores and
@@ -249,10 +260,15 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const int off = qrow + qb * 32 * ST + ks * 32;
-        s = mfma32(as_bf16x8(ld16(b + SM::kQ + off)), kf[ks], s);
-        dp = mfma32(as_bf16x8(ld16(b + SM::kDO + off)), vf[ks], dp);
+        s = mfma32(as_bf16x8(ld16(qt + off)), kf[ks], s);
+        dp = mfma32(as_bf16x8(ld16(ot + off)), vf[ks], dp);
       }
       // queries of register r: qb*32 + key_of_reg(r, hi) = qb*32 + 16 (r >> 3) + 8 hi + (r & 7)
+      if (MK) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key > q0 + qb * 32 + key_of_reg(r, hi) + shift) s[r] = kNegInf;
+      }
       bf16x8 pf[2], dsf[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -265,8 +281,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * half + e;
-          float pv = exp2_fast(__builtin_fmaf(s[r], c, -(e < 4 ? la[e] : lb[e - 4])));
-          if (need_mask && key > q0 + qi0 + e + shift) pv = 0.f;
+          const float pv = exp2_fast(__builtin_fmaf(s[r], c, -(e < 4 ? la[e] : lb[e - 4])));
           p[e] = pv;
           ds[e] = pv * (dp[r] - (e < 4 ? da[e] : db4[e - 4]));
         }
@@ -279,11 +294,33 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           const int off = trb + (qb * 32 + 16 * st) * ST + db * 64;
-          dv[db] = mfma32(lds_read_tr_pair(b + SM::kDO + off, 4 * ST), pf[st], dv[db]);
-          dk[db] = mfma32(lds_read_tr_pair(b + SM::kQ + off, 4 * ST), dsf[st], dk[db]);
+          dv[db] = mfma32(lds_read_tr_pair(ot + off, 4 * ST), pf[st], dv[db]);
+          dk[db] = mfma32(lds_read_tr_pair(qt + off, 4 * ST), dsf[st], dk[db]);
         }
     }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using BT = std::integral_constant<bool, true>;
+  using BF = std::integral_constant<bool, false>;
+
+  if (t0 < t1) copy(t0, buf0);
+  // buffer of tile t: (t - t0) & 1
+  int t = t0;
+  for (; t + 1 < tm; t += 2) {
+    step(I0(), BT(), t);
+    step(I1(), BT(), t + 1);
   }
+  if (t < tm) {
+    step(I0(), BT(), t);
+    ++t;
+    if (t < t1) step(I1(), BF(), t++);
+  }
+  for (; t + 1 < t1; t += 2) {
+    step(I0(), BF(), t);
+    step(I1(), BF(), t + 1);
+  }
+  if (t < t1) step(I0(), BF(), t);
 
   if (key < Nk) {
     store_row<D>(dK + ((size_t)bh * Nk + key) * D, dk, scale, hi);
@@ -302,9 +339,6 @@ struct DqLds {
   static constexpr int KST = dual_stride<D>(), VST = row_stride<D>();
   using KTile = PaddedTile<D, KST>;
   using VTile = PaddedTile<D, VST>;
-  static constexpr int kK = 0, kV = KTile::kBytes;
-  static constexpr int kBuf = KTile::kBytes + VTile::kBytes;
-  static constexpr int kBytes = 2 * kBuf;
 };
 
 template <int D, bool CAUSAL>
@@ -314,7 +348,12 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
     bf16* __restrict__ dQ, int BH, int Nq, int Nk, float c, float scale) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using SM = DqLds<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SM::kBytes];
+  // one array per buffer: the LDS copies into one buffer then provably do not alias the reads of
+  // the other, so no wait for the copies in flight is needed before those reads
+  __shared__ __attribute__((aligned(16))) unsigned char kb0[SM::KTile::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char kb1[SM::KTile::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char vb0[SM::VTile::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char vb1[SM::VTile::kBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -356,30 +395,37 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   if (CAUSAL) kend = min(Nk, min(q0 + kBR, Nq) + shift);
   const int ntiles = (kend + kBC - 1) / kBC;
   const int horizon = CAUSAL ? min(qw + 31, Nq - 1) + shift : Nk - 1;
+  // leading tiles that need no mask for any row of the workgroup: below N_k, and (causal) every
+  // key at or before the first row's diagonal
+  int nfull = Nk / kBC;
+  if (CAUSAL) nfull = min(nfull, max(0, q0 + shift + 1) / kBC);
+  nfull = min(nfull, ntiles);
 
   typename SM::KTile ktile;
   typename SM::VTile vtile;
   ktile.init(wave, lane);
   vtile.init(wave, lane);
-  auto copy = [&](int t) {
-    unsigned char* b = smem + (t & 1) * SM::kBuf;
-    ktile.copy(Kh, t * kBC, Nk, b + SM::kK, wave);
-    vtile.copy(Vh, t * kBC, Nk, b + SM::kV, wave);
-  };
   const int krow = key_of_row(l32);
   const int kro = krow * SM::KST + hi * 16, vro = krow * SM::VST + hi * 16;
   const int trb = tr_base<SM::KST>(lane);
+  const int lim = CAUSAL ? min(Nk - 1, qi + shift) : Nk - 1;
 
-  if (ntiles > 0) copy(0);
-  for (int t = 0; t < ntiles; ++t) {
+  // One key tile t from buffer P (K tile kt, V tile vt); the copies of tile t+1 go to the other
+  // buffer. MASKED: tiles on the causal diagonal or past N_k; waves whose rows see no key of the
+  // tile skip it.
+  auto step = [&](auto PAR, auto MASKED, int t) {
+    constexpr int P = decltype(PAR)::value;
+    constexpr bool MK = decltype(MASKED)::value;
+    const unsigned char* kt = P ? kb1 : kb0;
+    const unsigned char* vt = P ? vb1 : vb0;
     wait_vmem();
     __syncthreads();
-    if (t + 1 < ntiles) copy(t + 1);
+    if (t + 1 < ntiles) {
+      ktile.copy(Kh, (t + 1) * kBC, Nk, P ? kb0 : kb1, wave);
+      vtile.copy(Vh, (t + 1) * kBC, Nk, P ? vb0 : vb1, wave);
+    }
     const int kbase = t * kBC;
-    if (kbase > horizon) continue;
-    const unsigned char* b = smem + (t & 1) * SM::kBuf;
-    const bool need_mask = (kbase + kBC > Nk) || (CAUSAL && kbase + kBC - 1 > qw + shift);
-    const int lim = CAUSAL ? min(Nk - 1, qi + shift) : Nk - 1;
+    if (MK && kbase > horizon) return;
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -392,19 +438,23 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
     for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = mfma32(as_bf16x8(ld16(b + SM::kK + kro + kb * 32 * SM::KST + ks * 32)), qf[ks],
-                       s[kb]);
-        dp[kb] = mfma32(as_bf16x8(ld16(b + SM::kV + vro + kb * 32 * SM::VST + ks * 32)),
-                        dof[ks], dp[kb]);
+        s[kb] = mfma32(as_bf16x8(ld16(kt + kro + kb * 32 * SM::KST + ks * 32)), qf[ks], s[kb]);
+        dp[kb] = mfma32(as_bf16x8(ld16(vt + vro + kb * 32 * SM::VST + ks * 32)), dof[ks], dp[kb]);
       }
+    if (MK) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kbase + kb * 32 + key_of_reg(r, hi) > lim) s[kb][r] = kNegInf;
+    }
     bf16x8 dsf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = exp2_fast(__builtin_fmaf(s[kb][r], c, -lq));
-        if (need_mask && kbase + kb * 32 + key_of_reg(r, hi) > lim) pv = 0.f;
+        const float pv = exp2_fast(__builtin_fmaf(s[kb][r], c, -lq));
         ds[r] = pv * (dp[kb][r] - dq_d);
       }
 #pragma unroll
@@ -419,9 +469,33 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int off = trb + 16 * st * SM::KST + db * 64;
-        acc[db] = mfma32(lds_read_tr_pair(b + SM::kK + off, 4 * SM::KST), dsf[st], acc[db]);
+        acc[db] = mfma32(lds_read_tr_pair(kt + off, 4 * SM::KST), dsf[st], acc[db]);
       }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using BT = std::integral_constant<bool, true>;
+  using BF = std::integral_constant<bool, false>;
+
+  if (ntiles > 0) {
+    ktile.copy(Kh, 0, Nk, kb0, wave);
+    vtile.copy(Vh, 0, Nk, vb0, wave);
   }
+  int t = 0;
+  for (; t + 1 < nfull; t += 2) {
+    step(I0(), BF(), t);
+    step(I1(), BF(), t + 1);
+  }
+  if (t < nfull) {
+    step(I0(), BF(), t);
+    ++t;
+    if (t < ntiles) step(I1(), BT(), t++);
+  }
+  for (; t + 1 < ntiles; t += 2) {
+    step(I0(), BT(), t);
+    step(I1(), BT(), t + 1);
+  }
+  if (t < ntiles) step(I0(), BT(), t);
 
   if (qi < Nq) store_row<D>(dQ + ((size_t)bh * Nq + qi) * D, acc, scale, hi);
 #endif
