@@ -38,6 +38,8 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -51,7 +53,6 @@ struct FwdLds {
   static constexpr int KCPR = KST / 16, VCPR = VST / 16;        // 16-byte chunks per row
   static constexpr int KT = kBC * KST, VT = kBC * VST;          // tile bytes
   static constexpr int KI = kBC * KCPR / 64, VI = kBC * VCPR / 64;  // wave-wide copies per tile
-  static constexpr int kBytes = 2 * KT + 2 * VT;
   static_assert(KI * 64 == kBC * KCPR && VI * 64 == kBC * VCPR, "tiles are whole wave copies");
 };
 
@@ -63,9 +64,12 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
   using L = FwdLds<D>;
   constexpr int BR = NW * 32;  // query rows per workgroup
   constexpr int KIW = (L::KI + NW - 1) / NW, VIW = (L::VI + NW - 1) / NW;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[L::kBytes];
-  unsigned char* kbuf = smem;
-  unsigned char* vbuf = smem + 2 * L::KT;
+  // one array per buffer: the LDS copies into one buffer then provably do not alias the reads of
+  // the other, so the reads wait for nothing but their own data
+  __shared__ __attribute__((aligned(16))) unsigned char kb0[L::KT];
+  __shared__ __attribute__((aligned(16))) unsigned char kb1[L::KT];
+  __shared__ __attribute__((aligned(16))) unsigned char vb0[L::VT];
+  __shared__ __attribute__((aligned(16))) unsigned char vb1[L::VT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -119,16 +123,14 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     const int rows = max(0, Nk - t * kBC);  // reads at or past N_k return zero
     return make_rsrc(base + (size_t)t * kBC * D, rows * D * 2);
   };
-  auto copy_k = [&](int t) {
+  auto copy_k = [&](int t, unsigned char* dst) {
     const auto r = tile_rsrc(Kh, t);
-    unsigned char* dst = kbuf + (t & 1) * L::KT;
 #pragma unroll
     for (int i = 0; i < KIW; ++i)
       if (wave + i * NW < L::KI) buffer_to_lds(r, dst + (wave + i * NW) * 1024, koff[i]);
   };
-  auto copy_v = [&](int t) {
+  auto copy_v = [&](int t, unsigned char* dst) {
     const auto r = tile_rsrc(Vh, t);
-    unsigned char* dst = vbuf + (t & 1) * L::VT;
 #pragma unroll
     for (int i = 0; i < VIW; ++i)
       if (wave + i * NW < L::VI) buffer_to_lds(r, dst + (wave + i * NW) * 1024, voff[i]);
@@ -179,11 +181,13 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
 
   // One pipeline step: mask, softmax and PV of tile t (scores in sc0/sc1), and the QK^T of
   // tile t+1 into sn0/sn1, issued between them so that it overlaps the softmax.
-  auto step = [&](f32x16& sc0, f32x16& sc1, f32x16& sn0, f32x16& sn1, int t) {
+  // Tile t uses buffer t & 1 == P for V[t] and K[t+2], the other buffer for K[t+1] and V[t+1].
+  auto step = [&](auto PAR, f32x16& sc0, f32x16& sc1, f32x16& sn0, f32x16& sn1, int t) {
+    constexpr int P = decltype(PAR)::value;
     wait_vmem();      // this thread's copies of K[t+1] and V[t] have landed
     __syncthreads();  // ... everyone's have, and everyone is done with K[t], V[t-1]
-    if (t + 2 < ntiles) copy_k(t + 2);
-    if (t + 1 < ntiles) copy_v(t + 1);
+    if (t + 2 < ntiles) copy_k(t + 2, P ? kb1 : kb0);
+    if (t + 1 < ntiles) copy_v(t + 1, P ? vb0 : vb1);
     if (t > last_tile) return;  // every row of this wave is masked from here on
     const int kbase = t * kBC;
     const bool need_mask = (kbase + kBC > Nk) || (CAUSAL && kbase + kBC - 1 > qw + shift);
@@ -195,12 +199,14 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
         if (kbase + 32 + key_of_reg(r, hi) > lim) sc1[r] = kNegInf;
       }
     }
-    float mq[4];
+    // row maximum: two independent v_max3 chains over the 32 scores of the lane
+    float ma = fmaxf(fmaxf(sc0[0], sc0[1]), sc0[2]), mb = fmaxf(fmaxf(sc1[0], sc1[1]), sc1[2]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      mq[j] = fmaxf(fmaxf(fmaxf(sc0[4 * j], sc0[4 * j + 1]), fmaxf(sc0[4 * j + 2], sc0[4 * j + 3])),
-                    fmaxf(fmaxf(sc1[4 * j], sc1[4 * j + 1]), fmaxf(sc1[4 * j + 2], sc1[4 * j + 3])));
-    const float mx = halves_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]))) * c;
+    for (int r = 3; r < 15; r += 2) {
+      ma = fmaxf(fmaxf(ma, sc0[r]), sc0[r + 1]);
+      mb = fmaxf(fmaxf(mb, sc1[r]), sc1[r + 1]);
+    }
+    const float mx = halves_max(fmaxf(fmaxf(ma, sc0[15]), fmaxf(mb, sc1[15]))) * c;
     if (__any(mx > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mx);  // finite: key 0 of tile 0 is visible to every row
       const float alpha = exp2_fast(m_run - m_new);
@@ -214,23 +220,25 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     }
     // Issued unconditionally so that it shares a basic block with the softmax below; past the
     // last tile it reads stale (in-bounds) LDS and its result is never used.
-    qk(sn0, sn1, kbuf + ((t + 1) & 1) * L::KT);
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    qk(sn0, sn1, P ? kb0 : kb1);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       sc0[r] = exp2_fast(__builtin_fmaf(sc0[r], c, -m_run));
       sc1[r] = exp2_fast(__builtin_fmaf(sc1[r], c, -m_run));
-      ps[r & 3] += sc0[r] + sc1[r];
     }
+    float ps[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ps[j] = sc0[j] + sc1[j];
+#pragma unroll
+    for (int r = 4; r < 16; ++r) ps[r & 3] += sc0[r] + sc1[r];
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     bf16x8 pf[4];
     pf[0] = pack_bf16x8(sc0[0], sc0[1], sc0[2], sc0[3], sc0[4], sc0[5], sc0[6], sc0[7]);
     pf[1] = pack_bf16x8(sc0[8], sc0[9], sc0[10], sc0[11], sc0[12], sc0[13], sc0[14], sc0[15]);
     pf[2] = pack_bf16x8(sc1[0], sc1[1], sc1[2], sc1[3], sc1[4], sc1[5], sc1[6], sc1[7]);
     pf[3] = pack_bf16x8(sc1[8], sc1[9], sc1[10], sc1[11], sc1[12], sc1[13], sc1[14], sc1[15]);
-    lq_run += (sum_bf16x8(pf[0], 0.f) + sum_bf16x8(pf[1], 0.f)) +
-              (sum_bf16x8(pf[2], 0.f) + sum_bf16x8(pf[3], 0.f));
-    const unsigned char* vt = vbuf + (t & 1) * L::VT;
+    lq_run = sum_bf16x8(pf[3], sum_bf16x8(pf[2], sum_bf16x8(pf[1], sum_bf16x8(pf[0], lq_run))));
+    const unsigned char* vt = P ? vb1 : vb0;
 #pragma unroll
     for (int st = 0; st < kBC / 16; ++st)
 #pragma unroll
@@ -238,18 +246,20 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
   };
 
   f32x16 sa0, sa1, sb0, sb1;
-  copy_k(0);
-  copy_v(0);
-  if (ntiles > 1) copy_k(1);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  copy_k(0, kb0);
+  copy_v(0, vb0);
+  if (ntiles > 1) copy_k(1, kb1);
   wait_vmem();
   __syncthreads();
-  qk(sa0, sa1, kbuf);
+  qk(sa0, sa1, kb0);
   int t = 0;
   for (; t + 1 < ntiles; t += 2) {
-    step(sa0, sa1, sb0, sb1, t);
-    step(sb0, sb1, sa0, sa1, t + 1);
+    step(I0(), sa0, sa1, sb0, sb1, t);
+    step(I1(), sb0, sb1, sa0, sa1, t + 1);
   }
-  if (t < ntiles) step(sa0, sa1, sb0, sb1, t);
+  if (t < ntiles) step(I0(), sa0, sa1, sb0, sb1, t);
 
   // ---- epilogue: O = acc / lq, L = ln 2 * (m + log2 l)
   const float l_tot = halves_sum(l_run);
