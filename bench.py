@@ -29,6 +29,8 @@ from exact_attention_fa_amd import inputs, metrics  # noqa: E402
 
 FB = dict(B=2, H=16, N=8192, d=128, causal=True, seed=3)         # forward + backward workload
 DEC = dict(B=8, H=32, Nk=65536, d=128, seed=5)                  # decode workload
+PAGED = dict(H_kv=8, block_size=16, seed=9)  # paged GQA decode: the decode workload's first 8
+                                             # K/V heads as a shuffled block cache, 4 q heads each
 
 
 def log(msg: str) -> None:
@@ -244,6 +246,50 @@ def main() -> int:
         "kernels": kernels,
         "roofline": roof,
     }
+    # ---- paged KV cache with grouped query heads (timed on its own, outside the step)
+    Hkv, bs = PAGED["H_kv"], PAGED["block_size"]
+    mb = DN // bs
+    nblk = DB * mb
+    blocks = (dkc[:, :Hkv].reshape(DB, Hkv, mb, bs, Dd).permute(0, 2, 1, 3, 4)
+              .reshape(nblk, Hkv, bs, Dd))
+    vblocks = (dvc[:, :Hkv].reshape(DB, Hkv, mb, bs, Dd).permute(0, 2, 1, 3, 4)
+               .reshape(nblk, Hkv, bs, Dd))
+    gen = torch.Generator(device="cpu").manual_seed(PAGED["seed"])
+    perm = torch.randperm(nblk, generator=gen).to(dev)
+    kcache = torch.empty_like(blocks)
+    vcache = torch.empty_like(vblocks)
+    kcache[perm] = blocks
+    vcache[perm] = vblocks
+    del blocks, vblocks
+    table = perm.to(torch.int32).reshape(DB, mb).contiguous()
+    lens = torch.full((DB,), DN, dtype=torch.int32, device=dev)
+    qp = dq1.reshape(DB, DH, Dd)
+    po, pl = torch.empty_like(qp), torch.empty((DB, DH), dtype=torch.float32, device=dev)
+    psplits = fa.decode_paged_num_splits(DB, DH, Hkv, mb, bs, Dd)
+    pws = torch.empty(fa.decode_paged_workspace_bytes(DB, DH, Hkv, mb, bs, Dd, psplits),
+                      dtype=torch.uint8, device=dev)
+    run_p = lambda: fa.decode_paged(qp, kcache, vcache, table, lens, num_splits=psplits,  # noqa: E731
+                                    workspace=pws, out=(po, pl))
+    for _ in range(max(args.warmup, 3)):
+        run_p()
+    torch.cuda.synchronize()
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a_, b_ in pev:
+        a_.record()
+        run_p()
+        b_.record()
+    torch.cuda.synchronize()
+    p_ms = sum(a_.elapsed_time(b_) for a_, b_ in pev) / len(pev)
+    p_bytes = 2 * DB * Hkv * DN * Dd * 2 + DB * DH * Dd * 2 * 2 + DB * DH * 4 + DB * mb * 4
+    log(f"paged GQA decode {p_ms:.3f} ms")
+    kernels["decode_paged_gqa"] = hbm_entry(
+        p_bytes, p_ms, f"paged K/V cache (B{DB}, {Hkv} K/V heads, {DN} positions, block {bs}) "
+                       f"read once for {DH} query heads; q, o, lse, block table; timed apart "
+                       f"from the step")
+    kernels["decode_paged_gqa"]["splits"] = psplits
+    del kcache, vcache
+
     if args.cpu_heads > 0:
         log(f"oracle CPU baseline on {args.cpu_heads} head(s) ...")
         out["cpu_baseline"] = cpu_baseline(args.cpu_heads)

@@ -30,6 +30,10 @@ SIGNATURES = {
     "fa_decode_num_splits": (_I, [_I, _I, _I, _I]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_decode_paged_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
+    "fa_decode_paged_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
+    "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _I, _F,
+                             _I, _P]),
 }
 
 _lib = None
@@ -192,4 +196,50 @@ def decode(q, k, v, scale: float | None = None, num_splits: int = 0, workspace=N
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           B, H, Nq, Nk, d, _scale(scale, d), 0, int(num_splits), _stream(q))
     _check("fa_decode", st)
+    return o, lse
+
+
+def decode_paged_num_splits(B: int, H: int, H_kv: int, max_blocks: int, block_size: int,
+                            d: int) -> int:
+    return int(load().fa_decode_paged_num_splits(B, H, H_kv, max_blocks, block_size, d))
+
+
+def decode_paged_workspace_bytes(B: int, H: int, H_kv: int, max_blocks: int, block_size: int,
+                                 d: int, num_splits: int = 0) -> int:
+    return int(load().fa_decode_paged_workspace_bytes(B, H, H_kv, max_blocks, block_size, d,
+                                                      num_splits))
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale: float | None = None,
+                 num_splits: int = 0, workspace=None, out=None):
+    """One decode step over a paged KV cache with grouped query heads.
+
+    q [B,H,d] bf16; k_cache/v_cache [num_blocks,H_kv,block_size,d] bf16; block_table
+    [B,max_blocks] int32; seq_lens [B] int32 -> (o [B,H,d] bf16, lse [B,H] fp32)."""
+    import torch
+    B, H, d = q.shape
+    num_blocks, H_kv, block_size = k_cache.shape[:3]
+    max_blocks = block_table.shape[1]
+    _need(q, "q", (B, H, d), torch.bfloat16)
+    _need(k_cache, "k_cache", (num_blocks, H_kv, block_size, d), torch.bfloat16)
+    _need(v_cache, "v_cache", (num_blocks, H_kv, block_size, d), torch.bfloat16)
+    _need(block_table, "block_table", (B, max_blocks), torch.int32)
+    _need(seq_lens, "seq_lens", (B,), torch.int32)
+    nbytes = decode_paged_workspace_bytes(B, H, H_kv, max_blocks, block_size, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _need(o, "o", (B, H, d), torch.bfloat16)
+        _need(lse, "lse", (B, H), torch.float32)
+    st = load().fa_decode_paged(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                block_table.data_ptr(), seq_lens.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), B, H, H_kv, d,
+                                block_size, num_blocks, max_blocks, _scale(scale, d),
+                                int(num_splits), _stream(q))
+    _check("fa_decode_paged", st)
     return o, lse

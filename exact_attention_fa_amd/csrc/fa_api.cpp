@@ -162,4 +162,66 @@ fa_status fa_decode(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf1
   return from_hip(fa::launch_decode(a));
 }
 
+int fa_decode_paged_num_splits(int B, int H, int H_kv, int max_blocks_per_seq, int block_size,
+                               int d) {
+  if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || max_blocks_per_seq < 1 || block_size < 1)
+    return 1;
+  const long long max_len = (long long)max_blocks_per_seq * block_size;
+  if (max_len >= (1LL << 31)) return 1;
+  return fa::decode_paged_auto_splits(B, H, H_kv, (int)max_len, d);
+}
+
+size_t fa_decode_paged_workspace_bytes(int B, int H, int H_kv, int max_blocks_per_seq,
+                                       int block_size, int d, int num_splits) {
+  if (B < 1 || H < 1 || H_kv < 1 || max_blocks_per_seq < 1 || block_size < 1 ||
+      (d != 64 && d != 128) || num_splits < 0)
+    return 0;
+  const int c = num_splits == 0
+                    ? fa_decode_paged_num_splits(B, H, H_kv, max_blocks_per_seq, block_size, d)
+                    : num_splits;
+  const size_t rows = (size_t)B * H * c;
+  return round_up16(rows * d * sizeof(float)) + round_up16(rows * sizeof(float));
+}
+
+fa_status fa_decode_paged(const fa_bf16* q, const fa_bf16* k_cache, const fa_bf16* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, fa_bf16* o,
+                          float* lse, void* workspace, size_t workspace_bytes, int B, int H,
+                          int H_kv, int d, int block_size, int num_blocks, int max_blocks_per_seq,
+                          float scale, int num_splits, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || H_kv < 1 || num_blocks < 1 || max_blocks_per_seq < 1 || block_size < 1)
+    return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (H % H_kv != 0) return FA_ERR_ARG;
+  if (block_size > 4096 || (block_size & (block_size - 1)) != 0) return FA_ERR_ARG;
+  const long long max_len = (long long)max_blocks_per_seq * block_size;
+  if (max_len >= (1LL << 31) || (long long)B * max_blocks_per_seq >= (1LL << 31) ||
+      (long long)B * H >= (1LL << 31))
+    return FA_ERR_SHAPE;
+  // the cache holds num_blocks * H_kv * block_size rows of d elements
+  if ((long long)num_blocks * H_kv * block_size >= (1LL << 40)) return FA_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > 1024 || num_splits > max_len) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return FA_ERR_ALIGN;
+  const int c = num_splits == 0
+                    ? fa_decode_paged_num_splits(B, H, H_kv, max_blocks_per_seq, block_size, d)
+                    : num_splits;
+  if (!workspace || workspace_bytes < fa_decode_paged_workspace_bytes(
+                                          B, H, H_kv, max_blocks_per_seq, block_size, d, c))
+    return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  const size_t rows = (size_t)B * H * c;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             round_up16(rows * d * sizeof(float)));
+  fa::DecodePagedArgs a{bf(q), bf(k_cache), bf(v_cache), block_table, seq_lens, bf(o), lse,
+                        part_o, part_lse, B, H, H_kv, d, block_size, num_blocks,
+                        max_blocks_per_seq, c, scale, stream};
+  return from_hip(fa::launch_decode_paged(a));
+}
+
 }  // extern "C"

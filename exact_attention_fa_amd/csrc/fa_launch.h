@@ -48,14 +48,34 @@ struct DecodeArgs {
   hipStream_t stream;
 };
 
+struct DecodePagedArgs {
+  const __bf16* q;        // [B, H, d]
+  const __bf16* k_cache;  // [num_blocks, H_kv, block_size, d]
+  const __bf16* v_cache;
+  const int* block_table;  // [B, max_blocks]
+  const int* seq_lens;     // [B]
+  __bf16* o;               // [B, H, d]
+  float* lse;              // [B, H]
+  float* part_o;           // workspace: [B, H, splits, d]
+  float* part_lse;         // workspace: [B, H, splits]
+  int B, H, Hkv, d, block_size, num_blocks, max_blocks, splits;
+  float scale;
+  hipStream_t stream;
+};
+
 hipError_t launch_fwd(const FwdArgs& a);
 // Offset (in floats) of L2 after D in the backward workspace.
 size_t bwd_lse2_offset(int B, int H, int Nq);
 // Backward phases; `phase_mask` bit 0 = D preprocess, bit 1 = dK/dV, bit 2 = dQ.
 hipError_t launch_bwd(const BwdArgs& a, unsigned phase_mask = 7u);
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_decode_paged(const DecodePagedArgs& a);
 
 // Split count used by the decode when the caller passes 0.
 int decode_auto_splits(int B, int H, int Nk, int d);
+// Query heads that one paged-decode workgroup serves together (a divisor of H / H_kv, <= 8).
+int decode_paged_heads_per_group(int H, int Hkv);
+// Split count used by the paged decode when the caller passes 0.
+int decode_paged_auto_splits(int B, int H, int Hkv, int max_len, int d);
 
 }  // namespace fa

@@ -75,3 +75,31 @@ def qkv_bf16(seed: int, B: int, H: int, n_q: int, n_k: int, d: int, with_do: boo
     if with_do:
         return q, k, v, tensor_bf16(seed, "do", B, H, n_q, d)
     return q, k, v
+
+
+def paged_kv_bf16(seed: int, B: int, H_kv: int, seq_lens, d: int, block_size: int,
+                  max_blocks: int, spare_blocks: int = 3):
+    """A paged KV cache holding, for sequence b and key/value head h, the rows of
+    slice_bf16(seed, "k"/"v", b, h, seq_lens[b], d), scattered over shuffled physical blocks.
+
+    Returns (k_cache, v_cache [num_blocks, H_kv, block_size, d] uint16, block_table
+    [B, max_blocks] int32, seq_lens [B] int32). num_blocks = B * max_blocks + spare_blocks; the
+    table lists every block of a sequence (also those past its length), drawn without
+    repetition from a seeded permutation; unused rows hold a fixed filler pattern (bf16 1.0).
+    """
+    lens = np.asarray(seq_lens, dtype=np.int32)
+    if np.any(lens > max_blocks * block_size):
+        raise ValueError("a sequence does not fit in max_blocks blocks")
+    num_blocks = B * max_blocks + spare_blocks
+    perm = Generator(PCG64(SeedSequence([seed, 7, B, max_blocks]))).permutation(num_blocks)
+    table = perm[: B * max_blocks].reshape(B, max_blocks).astype(np.int32)
+    kc = np.full((num_blocks, H_kv, block_size, d), 0x3F80, dtype=np.uint16)
+    vc = np.full((num_blocks, H_kv, block_size, d), 0x3F80, dtype=np.uint16)
+    for b in range(B):
+        n = int(lens[b])
+        j = np.arange(n)
+        blocks, rows = table[b][j // block_size], j % block_size
+        for h in range(H_kv):
+            kc[blocks, h, rows] = slice_bf16(seed, "k", b, h, n, d)
+            vc[blocks, h, rows] = slice_bf16(seed, "v", b, h, n, d)
+    return kc, vc, table, lens

@@ -136,6 +136,50 @@ fa_status fa_decode(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf1
                     int B, int H, int N_q, int N_k, int d, float scale, int causal,
                     int num_splits, hipStream_t stream);
 
+/* ---- Decode over a paged KV cache with grouped-query heads -----------------------------------
+ *
+ * Page "Bellek Duvarının Fiziği", section "Duvarın Ötesi: KV Cache, Uzun Bağlam ve Yaklaşık
+ * Attention": at inference the KV cache is the second IO front, attacked by a paged cache
+ * (PagedAttention) and by query heads that share K/V heads (GQA/MQA); section "Decode Aşaması:
+ * Flash-Decoding" pairs Flash-Decoding with the paged cache. The pages name these methods without
+ * defining them; the definitions used here:
+ *   * grouped query heads: H query heads, H_kv key/value heads, H a multiple of H_kv; query head
+ *     h attends with key/value head h / (H / H_kv) (H_kv = H: multi-head, H_kv = 1: multi-query);
+ *   * paged cache: K and V live in fixed-size blocks of block_size positions,
+ *       k_cache, v_cache   [num_blocks, H_kv, block_size, d]   bf16
+ *     and sequence b's position j sits in block block_table[b, j / block_size] at row
+ *     j % block_size;
+ *       block_table        [B, max_blocks_per_seq]  int32, entries in [0, num_blocks)
+ *       seq_lens           [B]                      int32, 1 <= seq_lens[b] <= max_blocks_per_seq * block_size
+ *   * each (b, h) computes O = softmax(scale * q K_b^T) V_b over its seq_lens[b] positions, with
+ *       q, o   [B, H, d] bf16 (one query row per head),   lse [B, H] fp32 (natural log).
+ * Device-side arguments (block table entries, sequence lengths) cannot be validated before the
+ * launch: block ids outside [0, num_blocks) read as zero rows, lengths are clamped to
+ * [0, max_blocks_per_seq * block_size], and a row with no position gets o = 0, lse = -inf.
+ * block_size must be a power of two (1 .. 4096).
+ */
+
+/* The split count fa_decode_paged uses when called with num_splits = 0. */
+int fa_decode_paged_num_splits(int B, int H, int H_kv, int max_blocks_per_seq, int block_size,
+                               int d);
+
+/* Bytes of device workspace fa_decode_paged needs (0 = the automatic split count): per (b, h,
+ * split) one fp32 partial output row of d values and one fp32 log-sum-exp. */
+size_t fa_decode_paged_workspace_bytes(int B, int H, int H_kv, int max_blocks_per_seq,
+                                       int block_size, int d, int num_splits);
+
+/* Split-KV decode over the paged cache. num_splits: 0 = automatic, else 1 .. min(1024,
+ * max_blocks_per_seq * block_size); split c of a sequence covers positions
+ * [c * chunk, (c + 1) * chunk) with chunk = ceil(max_blocks_per_seq * block_size / num_splits).
+ * q, k_cache, v_cache, o and workspace 16-byte aligned; block_table, seq_lens, lse 4-byte aligned.
+ * Errors as for fa_decode; FA_ERR_ARG also for H not a multiple of H_kv, a block_size that is
+ * not a power of two, or a split count out of range. */
+fa_status fa_decode_paged(const fa_bf16* q, const fa_bf16* k_cache, const fa_bf16* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, fa_bf16* o,
+                          float* lse, void* workspace, size_t workspace_bytes, int B, int H,
+                          int H_kv, int d, int block_size, int num_blocks, int max_blocks_per_seq,
+                          float scale, int num_splits, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

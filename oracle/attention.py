@@ -164,3 +164,50 @@ def decode(q, k, v, scale: float):
     if np.shape(q)[2] != 1:
         raise ValueError("decode takes exactly one query row per (b, h)")
     return forward(q, k, v, scale, causal=False)
+
+
+def gather_paged(cache, block_table_row, seq_len: int, kv_head: int) -> np.ndarray:
+    """Positions 0 .. seq_len-1 of one sequence and one key/value head of a paged cache.
+
+    cache [num_blocks, H_kv, block_size, d]; position j of the sequence lives in block
+    block_table_row[j // block_size] at row j % block_size (the paged-cache reading of
+    [MW] "Duvarın Ötesi: KV Cache, Uzun Bağlam ve Yaklaşık Attention", which names PagedAttention
+    without defining it). Returns fp64 [seq_len, d].
+    """
+    cache = np.asarray(cache)
+    bs = cache.shape[2]
+    j = np.arange(seq_len)
+    blocks = np.asarray(block_table_row)[j // bs]
+    return _f64(cache[blocks, kv_head, j % bs])
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale: float):
+    """Decode step over a paged KV cache with grouped query heads.
+
+    [MW] "Duvarın Ötesi: KV Cache, ...": query heads may share key/value heads (GQA/MQA); the
+    reading used here: with H query heads and H_kv key/value heads (H a multiple of H_kv), query
+    head h uses key/value head h // (H // H_kv). Each (b, h) is the decode function of
+    [MW] "Decode Aşaması: Flash-Decoding" (one query row, every position visible) over the
+    sequence's seq_lens[b] positions gathered from the cache. A sequence with no position gives
+    o = 0 and lse = -inf.
+    q [B,H,d]; k_cache/v_cache [num_blocks,H_kv,block_size,d]; block_table [B,max_blocks];
+    seq_lens [B] -> (o [B,H,d], lse [B,H]) fp64.
+    """
+    B, H, d = np.shape(q)
+    H_kv = np.shape(k_cache)[1]
+    if H % H_kv != 0:
+        raise ValueError("the query head count must be a multiple of the key/value head count")
+    group = H // H_kv
+    o = np.zeros((B, H, np.shape(v_cache)[3]), dtype=np.float64)
+    lse = np.full((B, H), -np.inf, dtype=np.float64)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n <= 0:
+            continue
+        for kvh in range(H_kv):
+            kk = gather_paged(k_cache, block_table[b], n, kvh)
+            vv = gather_paged(v_cache, block_table[b], n, kvh)
+            for h in range(kvh * group, (kvh + 1) * group):
+                ob, lb = forward_head(np.asarray(q[b, h])[None, :], kk, vv, scale, causal=False)
+                o[b, h], lse[b, h] = ob[0], lb[0]
+    return o, lse

@@ -247,6 +247,73 @@ def pin_decode_split_combine():
         np.testing.assert_allclose(L, lse[..., 0], rtol=1e-14, atol=1e-14)
 
 
+def _paged_case(rng, B, H, H_kv, d, bs, max_blocks, lens):
+    """Random paged cache with two spare blocks and a shuffled block table."""
+    num_blocks = B * max_blocks + 2
+    kc = rng.standard_normal((num_blocks, H_kv, bs, d))
+    vc = rng.standard_normal((num_blocks, H_kv, bs, d))
+    table = rng.permutation(num_blocks)[: B * max_blocks].reshape(B, max_blocks)
+    q = rng.standard_normal((B, H, d))
+    return q, kc, vc, table, np.asarray(lens)
+
+
+PAGED_CASES = [  # (B, H, H_kv, d, block_size, max_blocks, seq_lens)
+    (2, 4, 2, 4, 2, 3, [5, 1]),
+    (1, 6, 1, 8, 4, 2, [7]),
+    (3, 2, 2, 4, 1, 4, [4, 2, 3]),
+    (2, 4, 4, 4, 4, 2, [8, 6]),
+]
+
+
+def pin_paged_gqa_brute_force():
+    """Paged, grouped-query decode against direct loops over the positions of each sequence:
+    block block_table[b][j // block_size], row j % block_size, and query head h reading key/value
+    head h // (H // H_kv) ([MW] "Duvarın Ötesi: KV Cache, ...", reading of GQA/MQA and the paged
+    cache)."""
+    rng = _rng(11)
+    for B, H, H_kv, d, bs, max_blocks, lens in PAGED_CASES:
+        q, kc, vc, table, sl = _paged_case(rng, B, H, H_kv, d, bs, max_blocks, lens)
+        scale = 0.7
+        o, lse = A.decode_paged(q, kc, vc, table, sl, scale)
+        group = H // H_kv
+        for b in range(B):
+            for h in range(H):
+                kvh = h // group
+                pos = [(int(table[b][j // bs]), j % bs) for j in range(int(sl[b]))]
+                s = [scale * sum(q[b, h, t] * kc[blk, kvh, row, t] for t in range(d))
+                     for blk, row in pos]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                z = sum(w)
+                for t in range(d):
+                    ref = sum(w[i] * vc[blk, kvh, row, t] for i, (blk, row) in enumerate(pos)) / z
+                    assert abs(o[b, h, t] - ref) <= 1e-12 * (1 + abs(ref)), (B, H, H_kv, b, h, t)
+                assert abs(lse[b, h] - (mx + math.log(z))) <= 1e-12 * (1 + abs(lse[b, h]))
+
+
+def pin_paged_invariances():
+    """Moving the blocks to other physical slots (table rewritten to match) changes nothing
+    bitwise; giving every query head its own copy of its key/value head (H_kv = H) changes
+    nothing; a sequence with no position gives o = 0 and lse = -inf."""
+    rng = _rng(12)
+    for B, H, H_kv, d, bs, max_blocks, lens in PAGED_CASES:
+        q, kc, vc, table, sl = _paged_case(rng, B, H, H_kv, d, bs, max_blocks, lens)
+        o, lse = A.decode_paged(q, kc, vc, table, sl, 0.5)
+        perm = rng.permutation(kc.shape[0])       # new slot of each physical block
+        kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+        kc2[perm], vc2[perm] = kc, vc
+        o2, lse2 = A.decode_paged(q, kc2, vc2, perm[table], sl, 0.5)
+        assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+        group = H // H_kv
+        kc3, vc3 = np.repeat(kc, group, axis=1), np.repeat(vc, group, axis=1)
+        o3, lse3 = A.decode_paged(q, kc3, vc3, table, sl, 0.5)
+        assert np.allclose(o, o3, rtol=0, atol=1e-13) and np.allclose(lse, lse3, rtol=0, atol=1e-13)
+    q, kc, vc, table, _ = _paged_case(rng, 2, 2, 1, 4, 2, 2, [3, 1])
+    o, lse = A.decode_paged(q, kc, vc, table, np.array([3, 0]), 1.0)
+    assert np.all(o[1] == 0.0) and np.all(np.isneginf(lse[1])) and np.all(np.isfinite(lse[0]))
+
+
 ALL_PINS = [pin_brute_force_rows, pin_rows_sum_to_one, pin_causal_future_invariance,
             pin_finite_differences, pin_closed_forms, pin_invariances, pin_gradient_sum_rules,
-            pin_torch_sdpa, pin_hand_examples, pin_decode_split_combine]
+            pin_torch_sdpa, pin_hand_examples, pin_decode_split_combine,
+            pin_paged_gqa_brute_force, pin_paged_invariances]

@@ -120,3 +120,39 @@ def test_decode_validation(lib):
     assert call(splits=11, Nk=10) == 8
     assert call(ws_bytes=ws - 1) == 6
     assert call(d=32) == 3
+
+
+def test_decode_paged_validation(lib):
+    # B8 H32 H_kv8, 512 blocks of 16 positions per sequence, d128
+    c = lib.fa_decode_paged_num_splits(8, 32, 8, 512, 16, 128)
+    assert 1 <= c <= 1024
+    assert lib.fa_decode_paged_num_splits(1, 4, 3, 4, 16, 64) == 1  # H not a multiple of H_kv
+    ws = lib.fa_decode_paged_workspace_bytes(8, 32, 8, 512, 16, 128, 0)
+    assert ws == lib.fa_decode_paged_workspace_bytes(8, 32, 8, 512, 16, 128, c)
+    assert ws >= 8 * 32 * c * (128 + 1) * 4 and ws % 16 == 0
+    assert lib.fa_decode_paged_workspace_bytes(8, 32, 8, 512, 16, 96, 0) == 0
+
+    def call(q=FAKE, table=FAKE, lens=FAKE, lse=FAKE, ws_ptr=FAKE, ws_bytes=ws, B=8, H=32,
+             H_kv=8, d=128, bs=16, nblocks=4096, max_blocks=512, scale=0.08, splits=0):
+        return lib.fa_decode_paged(q, FAKE, FAKE, table, lens, FAKE, lse, ws_ptr, ws_bytes, B, H,
+                                   H_kv, d, bs, nblocks, max_blocks, scale, splits, None)
+    assert call(q=None) == 1
+    assert call(table=None) == 1
+    assert call(lens=None) == 1
+    assert call(B=0) == 2
+    assert call(H_kv=0) == 2
+    assert call(nblocks=0) == 2
+    assert call(max_blocks=0) == 2
+    assert call(d=80) == 3
+    assert call(scale=0.0) == 7
+    assert call(H=30) == 8                     # not a multiple of H_kv
+    assert call(bs=24) == 8                    # not a power of two
+    assert call(bs=8192) == 8
+    assert call(splits=1025) == 8
+    assert call(splits=-1) == 8
+    assert call(splits=9, bs=1, max_blocks=8) == 8  # more splits than positions
+    assert call(q=FAKE + 8) == 4
+    assert call(table=FAKE + 2) == 4
+    assert call(lse=FAKE + 1) == 4
+    assert call(ws_ptr=None) == 6
+    assert call(ws_bytes=ws - 16) == 6

@@ -127,7 +127,45 @@ def _bwd_factory(variant):
     return bwd
 
 
+_orig_gather = A.gather_paged
+
+
+def _gather_block_and_row_swapped(cache, block_table_row, seq_len, kv_head):
+    cache = np.asarray(cache)
+    bs = cache.shape[2]
+    j = np.arange(seq_len)
+    blocks = np.asarray(block_table_row)[np.minimum(j % bs, len(block_table_row) - 1)]
+    return np.asarray(cache[blocks, kv_head, np.minimum(j // bs, bs - 1)], dtype=np.float64)
+
+
+def _gather_physical_order(cache, block_table_row, seq_len, kv_head):
+    # ignores the block table: reads blocks 0, 1, 2, ... in physical order
+    cache = np.asarray(cache)
+    bs = cache.shape[2]
+    j = np.arange(seq_len)
+    return np.asarray(cache[j // bs, kv_head, j % bs], dtype=np.float64)
+
+
+def _decode_paged_head_modulo(q, k_cache, v_cache, block_table, seq_lens, scale):
+    # query head h reads key/value head h % H_kv instead of h // (H // H_kv)
+    B, H, d = np.shape(q)
+    H_kv = np.shape(k_cache)[1]
+    o = np.zeros((B, H, d))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        n = int(seq_lens[b])
+        for h in range(H):
+            kk = A.gather_paged(k_cache, block_table[b], n, h % H_kv)
+            vv = A.gather_paged(v_cache, block_table[b], n, h % H_kv)
+            ob, lb = A.forward_head(np.asarray(q[b, h])[None, :], kk, vv, scale, causal=False)
+            o[b, h], lse[b, h] = ob[0], lb[0]
+    return o, lse
+
+
 MUTANTS = {
+    "paged_block_and_row_swapped": ("gather_paged", _gather_block_and_row_swapped),
+    "paged_ignores_block_table": ("gather_paged", _gather_physical_order),
+    "gqa_head_modulo": ("decode_paged", _decode_paged_head_modulo),
     "scores_no_scale": ("scores", _scores_no_scale),
     "scores_transposed": ("scores", _scores_transposed),
     "mask_off_by_one": ("visible", _visible_off_by_one),
