@@ -40,7 +40,8 @@ def log(msg: str) -> None:
 KERNEL_SOURCES = {"fwd": ["fa_fwd.hip", "fa_device.h"], "bwd": ["fa_bwd.hip", "fa_device.h"],
                   "decode": ["fa_decode.hip", "fa_device.h"]}
 KERNEL_FAMILY = {"fwd": "fwd", "bwd_preprocess": "bwd", "bwd_dkdv": "bwd", "bwd_dq": "bwd",
-                 "decode": "decode"}
+                 "decode": "decode", "decode_paged_gqa": "decode"}
+TRAFFIC_KEY = {"decode": "decode_split", "decode_paged_gqa": "decode_paged_split"}
 
 
 def measured_traffic() -> dict:
@@ -54,7 +55,7 @@ def measured_traffic() -> dict:
         rec = json.load(f)["kernels"]
     out = {}
     for name, fam in KERNEL_FAMILY.items():
-        key = "decode_split" if name == "decode" else name
+        key = TRAFFIC_KEY.get(name, name)
         if key not in rec:
             continue
         m = hashlib.sha256()
@@ -63,7 +64,7 @@ def measured_traffic() -> dict:
                 m.update(f.read())
         if m.hexdigest()[:16] == rec[key]["source_hash"]:
             b = rec[key]["bytes_per_launch"]
-            if name == "decode" and "decode_combine" in rec:
+            if name in TRAFFIC_KEY and "decode_combine" in rec:
                 b += rec["decode_combine"]["bytes_per_launch"]
             out[name] = b
     return out
@@ -212,8 +213,10 @@ def main() -> int:
                             "K and V read once + q, o, lse (split + combine kernels)"),
     }
     kernels["bwd_dq"]["executed_tflops"] = 3 * gemm / (ms["bwd_dq"] * 1e-3) / 1e12
-    for name, nbytes in measured_traffic().items():
-        kernels[name]["traffic"] = nbytes
+    traffic = measured_traffic()
+    for name, nbytes in traffic.items():
+        if name in kernels:
+            kernels[name]["traffic"] = nbytes
     dominant = max(kernels, key=lambda n: kernels[n]["ms"])
     roof = dict(kernels[dominant])
     roof["kernel"] = dominant
@@ -288,6 +291,8 @@ def main() -> int:
                        f"read once for {DH} query heads; q, o, lse, block table; timed apart "
                        f"from the step")
     kernels["decode_paged_gqa"]["splits"] = psplits
+    if "decode_paged_gqa" in traffic:
+        kernels["decode_paged_gqa"]["traffic"] = traffic["decode_paged_gqa"]
     del kcache, vcache
 
     if args.cpu_heads > 0:
