@@ -9,7 +9,10 @@ One step = one pass over every kernel of the path on synthetic bf16 inputs alrea
 4 B H N^2 d, halved for the causal mask, times 3.5 for forward plus 2.5x backward), from the HIP
 events around those kernels; `ms_per_step` is the wall time of the whole step including the decode.
 The decode is reported in GB/s of K and V read. Every kernel's own rate and roofline fraction is
-listed, and `roofline` repeats the entry of the kernel that takes the most time.
+listed, and `roofline` repeats the entry of the step's kernel that takes the most time. Two more
+entries are timed apart from the step: the paged-cache decode with grouped query heads, and a
+causal forward + backward over a batch of eight sequences of different lengths (TFLOP/s of the
+valid rows and keys only).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -31,6 +34,8 @@ FB = dict(B=2, H=16, N=8192, d=128, causal=True, seed=3)         # forward + bac
 DEC = dict(B=8, H=32, Nk=65536, d=128, seed=5)                  # decode workload
 PAGED = dict(H_kv=8, block_size=16, seed=9)  # paged GQA decode: the decode workload's first 8
                                              # K/V heads as a shuffled block cache, 4 q heads each
+VARLEN = dict(B=8, H=16, N=8192, d=128, n_min=1024, causal=True, seed=21)  # variable lengths,
+                                             # uniform on [n_min, N], padded to N
 
 
 def log(msg: str) -> None:
@@ -294,6 +299,43 @@ def main() -> int:
     if "decode_paged_gqa" in traffic:
         kernels["decode_paged_gqa"]["traffic"] = traffic["decode_paged_gqa"]
     del kcache, vcache
+
+    # ---- variable-length batch: causal forward + backward (timed on its own, outside the step)
+    VB, VH, VN, Vd = VARLEN["B"], VARLEN["H"], VARLEN["N"], VARLEN["d"]
+    vlens_np = inputs.varlen_lengths(VARLEN["seed"], VB, VARLEN["n_min"], VN)
+    vlens = torch.as_tensor(vlens_np).to(dev)
+    vq, vk, vv, vdo = (to_dev(x) for x in inputs.qkv_bf16(VARLEN["seed"], VB, VH, VN, VN, Vd,
+                                                            with_do=True))
+    vo = torch.empty_like(vq)
+    vlse = torch.empty((VB, VH, VN), dtype=torch.float32, device=dev)
+    vgrads = (torch.empty_like(vq), torch.empty_like(vk), torch.empty_like(vv))
+    vws = torch.empty(fa.bwd_workspace_bytes(VB, VH, VN, VN, Vd), dtype=torch.uint8, device=dev)
+    vc = VARLEN["causal"]
+    run_vf = lambda: fa.fwd_varlen(vq, vk, vv, vlens, vlens, causal=vc, out=(vo, vlse))  # noqa: E731
+    run_vb = lambda: fa.bwd_varlen(vq, vk, vv, vo, vlse, vdo, vlens, vlens, causal=vc,  # noqa: E731
+                                   workspace=vws, out=vgrads)
+    for _ in range(max(args.warmup, 3)):
+        run_vf()
+        run_vb()
+    torch.cuda.synchronize()
+    vev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in vev:
+        e[0].record()
+        run_vf()
+        e[1].record()
+        run_vb()
+        e[2].record()
+    torch.cuda.synchronize()
+    vf_ms = sum(e[0].elapsed_time(e[1]) for e in vev) / len(vev)
+    vb_ms = sum(e[1].elapsed_time(e[2]) for e in vev) / len(vev)
+    vf_flops = sum(metrics.attention_flops(1, VH, int(n), int(n), Vd, causal=vc) for n in vlens_np)
+    log(f"varlen fwd {vf_ms:.3f} ms, bwd {vb_ms:.3f} ms (lengths {vlens_np.tolist()})")
+    vnote = (f"B{VB} H{VH} d{Vd} causal, lengths {vlens_np.tolist()} padded to {VN}: FLOPs of "
+             f"the valid rows and keys only")
+    kernels["fwd_varlen"] = mfma_entry(vf_flops, vf_ms, vnote)
+    kernels["bwd_varlen"] = mfma_entry(2.5 * vf_flops, vb_ms,
+                                       vnote + "; preprocess + dK/dV + dQ, 2.5x the forward")
+    del vq, vk, vv, vdo, vo, vgrads, vws
 
     if args.cpu_heads > 0:
         log(f"oracle CPU baseline on {args.cpu_heads} head(s) ...")

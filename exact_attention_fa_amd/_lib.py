@@ -30,6 +30,8 @@ SIGNATURES = {
     "fa_decode_num_splits": (_I, [_I, _I, _I, _I]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_varlen": (_I, [_P] * 12 + [_Z, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_paged_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "fa_decode_paged_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -243,3 +245,63 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale: float | None
                                 int(num_splits), _stream(q))
     _check("fa_decode_paged", st)
     return o, lse
+
+
+def _lens(t, name: str, B: int) -> None:
+    import torch
+    _need(t, name, (B,), torch.int32)
+
+
+def fwd_varlen(q, k, v, seq_lens_q, seq_lens_k, causal: bool = False,
+               scale: float | None = None, out=None):
+    """Forward over a batch of different-length sequences in the padded [B,H,N,d] layout
+    (seq_lens_q/seq_lens_k: int32 [B] on the GPU) -> (o, lse); padding rows get o = 0,
+    lse = -inf."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _need(q, "q", (B, H, Nq, d), torch.bfloat16)
+    _need(k, "k", (B, H, Nk, d), torch.bfloat16)
+    _need(v, "v", (B, H, Nk, d), torch.bfloat16)
+    _lens(seq_lens_q, "seq_lens_q", B)
+    _lens(seq_lens_k, "seq_lens_k", B)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _need(o, "o", (B, H, Nq, d), torch.bfloat16)
+        _need(lse, "lse", (B, H, Nq), torch.float32)
+    st = load().fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), seq_lens_q.data_ptr(), seq_lens_k.data_ptr(), B, H,
+                              Nq, Nk, d, _scale(scale, d), int(bool(causal)), _stream(q))
+    _check("fa_fwd_varlen", st)
+    return o, lse
+
+
+def bwd_varlen(q, k, v, o, lse, dout, seq_lens_q, seq_lens_k, causal: bool = False,
+               scale: float | None = None, workspace=None, out=None):
+    """Gradients (dq, dk, dv) for fwd_varlen; padding rows and keys get zero gradients."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for t, n, shp in ((q, "q", (B, H, Nq, d)), (k, "k", (B, H, Nk, d)), (v, "v", (B, H, Nk, d)),
+                      (o, "o", (B, H, Nq, d)), (dout, "dout", (B, H, Nq, d))):
+        _need(t, n, shp, torch.bfloat16)
+    _need(lse, "lse", (B, H, Nq), torch.float32)
+    _lens(seq_lens_q, "seq_lens_q", B)
+    _lens(seq_lens_k, "seq_lens_k", B)
+    nbytes = bwd_workspace_bytes(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    st = load().fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), seq_lens_q.data_ptr(), seq_lens_k.data_ptr(),
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              B, H, Nq, Nk, d, _scale(scale, d), int(bool(causal)), _stream(q))
+    _check("fa_bwd_varlen", st)
+    return dq, dk, dv

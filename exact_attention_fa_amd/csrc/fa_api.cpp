@@ -75,12 +75,16 @@ fa_status bwd_checked(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, cons
                       const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk,
                       fa_bf16* dv, void* workspace, size_t workspace_bytes, int B, int H,
                       int N_q, int N_k, int d, float scale, int causal, hipStream_t stream,
-                      unsigned need, unsigned phases) {
+                      unsigned need, unsigned phases, const int32_t* lens_q = nullptr,
+                      const int32_t* lens_k = nullptr) {
+  const bool varlen = lens_q != nullptr;
   const bool use_o = need & 1u, use_qkv = need & 2u, use_kv_out = need & 4u, use_q_out = need & 8u;
   if (!dout || (use_o && (!o || !lse)) || (use_qkv && (!q || !k || !v)) ||
       (use_kv_out && (!dk || !dv)) || (use_q_out && !dq))
     return FA_ERR_NULL;
-  fa_status s = check_common(B, H, N_q, N_k, d, scale, causal);
+  // per-sequence lengths define their own causal alignment; the padded extents need not
+  // satisfy N_q <= N_k
+  fa_status s = check_common(B, H, N_q, N_k, d, scale, varlen ? 0 : causal);
   if (s != FA_OK) return s;
   if (!aligned16(dout) || (use_o && (!aligned16(o) || !aligned16(lse))) ||
       (use_qkv && (!aligned16(q) || !aligned16(k) || !aligned16(v))) ||
@@ -90,7 +94,8 @@ fa_status bwd_checked(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, cons
     return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
   fa::BwdArgs a{bf(q), bf(k), bf(v), bf(o), lse, bf(dout), bf(dq), bf(dk), bf(dv),
-                static_cast<float*>(workspace), B, H, N_q, N_k, d, scale, causal != 0, stream};
+                static_cast<float*>(workspace), B, H, N_q, N_k, d, scale, causal != 0, stream,
+                lens_q, lens_k};
   return from_hip(fa::launch_bwd(a, phases));
 }
 
@@ -222,6 +227,36 @@ fa_status fa_decode_paged(const fa_bf16* q, const fa_bf16* k_cache, const fa_bf1
                         part_o, part_lse, B, H, H_kv, d, block_size, num_blocks,
                         max_blocks_per_seq, c, scale, stream};
   return from_hip(fa::launch_decode_paged(a));
+}
+
+namespace {
+bool lens_ok(const int32_t* p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+}  // namespace
+
+fa_status fa_fwd_varlen(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
+                        float* lse, const int32_t* seq_lens_q, const int32_t* seq_lens_k, int B,
+                        int H, int N_q, int N_k, int d, float scale, int causal,
+                        hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !seq_lens_q || !seq_lens_k) return FA_ERR_NULL;
+  fa_status s = check_common(B, H, N_q, N_k, d, scale, 0);
+  if (s != FA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !lens_ok(seq_lens_q) || !lens_ok(seq_lens_k))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a{bf(q), bf(k), bf(v), bf(o), lse, B, H, N_q, N_k, d, scale, causal != 0, stream,
+                seq_lens_q, seq_lens_k};
+  return from_hip(fa::launch_fwd(a));
+}
+
+fa_status fa_bwd_varlen(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                        const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk,
+                        fa_bf16* dv, const int32_t* seq_lens_q, const int32_t* seq_lens_k,
+                        void* workspace, size_t workspace_bytes, int B, int H, int N_q, int N_k,
+                        int d, float scale, int causal, hipStream_t stream) {
+  if (!seq_lens_q || !seq_lens_k) return FA_ERR_NULL;
+  if (!lens_ok(seq_lens_q) || !lens_ok(seq_lens_k)) return FA_ERR_ALIGN;
+  return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N_q,
+                     N_k, d, scale, causal, stream, 15u, 7u, seq_lens_q, seq_lens_k);
 }
 
 }  // extern "C"

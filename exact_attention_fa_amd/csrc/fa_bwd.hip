@@ -96,6 +96,15 @@ __device__ __forceinline__ void store_row(bf16* dst_row, const f32x16 (&acc)[D /
     }
 }
 
+template <int D>
+__device__ __forceinline__ void store_zero_row(bf16* dst_row, int hi) {
+  const u32x2 z = {0u, 0u};
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(dst_row + db * 32 + 8 * j + 4 * hi) = z;
+}
+
 __device__ __forceinline__ void xcd_map(int bid, int BH, int& bh, int& rank) {
   if ((BH & 7) == 0) {
     const int xcd = bid & 7, local = bid >> 3, per = BH >> 3;
@@ -140,7 +149,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__
     s = group_sum<G>(s);
     if (gl == 0) {
       delta[row] = s;
-      lse2[row] = LSE[row] * kLog2e;
+      // a row that saw no key (LSE = -inf) gets L2 = +inf, so that every probability the
+      // backward rebuilds for it is exp2(S c - inf) = 0
+      const float l = LSE[row];
+      lse2[row] = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
     }
   }
 }
@@ -159,11 +171,14 @@ struct DkdvLds {
   static constexpr int kBuf = kDl + kBQ * 4;
 };
 
-template <int D, bool CAUSAL>
+// VL: per-sequence lengths lens_q[b] <= Nq, lens_k[b] <= Nk inside the padded tensors; the
+// gradients of padding rows are zero.
+template <int D, bool CAUSAL, bool VL>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
-    bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int Nq, int Nk, float c, float scale) {
+    bf16* __restrict__ dK, bf16* __restrict__ dV, const int* __restrict__ lens_q,
+    const int* __restrict__ lens_k, int BH, int H, int Nq, int Nk, float c, float scale) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using SM = DkdvLds<D>;
   constexpr int ST = SM::ST;
@@ -180,7 +195,9 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   const int k0 = rank * kBKV;  // causal: low key tiles see the most queries and go first
   const int kw = k0 + wave * 32;
   const int key = kw + l32;
-  const int shift = Nk - Nq;  // causal: key j visible to query i iff j <= i + shift
+  const int nq = VL ? min(max(lens_q[bh / H], 0), Nq) : Nq;  // valid lengths of this sequence
+  const int nk = VL ? min(max(lens_k[bh / H], 0), Nk) : Nk;
+  const int shift = nk - nq;  // causal: key j visible to query i iff j <= i + shift
 
   const bf16* Qh = Q + (size_t)bh * Nq * D;
   const bf16* dOh = dO + (size_t)bh * Nq * D;
@@ -192,7 +209,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (key < Nk) {
+    if (key < nk) {
       a = ld16(K + ((size_t)bh * Nk + key) * D + ks * 16 + hi * 8);
       b = ld16(V + ((size_t)bh * Nk + key) * D + ks * 16 + hi * 8);
     }
@@ -211,7 +228,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   // query tiles that can see any key of this workgroup; the first ones (causal) cross the
   // diagonal of some wave and are masked, from tm on every query sees every key of the workgroup
   const int t0 = CAUSAL ? max(0, k0 - shift) / kBQ : 0;
-  const int t1 = (Nq + kBQ - 1) / kBQ;
+  const int t1 = (VL && k0 >= nk) ? t0 : (nq + kBQ - 1) / kBQ;  // no valid key: nothing to do
   int tm = t0;
   if (CAUSAL) tm = min(t1, max(t0, (k0 + kBKV - 1 - shift + kBQ - 1) / kBQ));
 
@@ -219,10 +236,10 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   tile.init(wave, lane);
   auto copy = [&](int t, unsigned char* b) {
     const int q0 = t * kBQ;
-    tile.copy(Qh, q0, Nq, b + SM::kQ, wave);
-    tile.copy(dOh, q0, Nq, b + SM::kDO, wave);
-    if (wave == 0) copy_row_vec(Lh, q0, Nq, b + SM::kL, lane);
-    if (wave == 1) copy_row_vec(Dh, q0, Nq, b + SM::kDl, lane);
+    tile.copy(Qh, q0, nq, b + SM::kQ, wave);
+    tile.copy(dOh, q0, nq, b + SM::kDO, wave);
+    if (wave == 0) copy_row_vec(Lh, q0, nq, b + SM::kL, lane);
+    if (wave == 1) copy_row_vec(Dh, q0, nq, b + SM::kDl, lane);
   };
   // rows past N_q read as zero: their Q and dO rows are zero and L2 = D = 0, so P = 1, dP = 0
   // and dS = 0: they add nothing to dK or dV.
@@ -245,7 +262,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
     if (t + 1 < t1) copy(t + 1, P ? buf0 : buf1);
     const int q0 = t * kBQ;
     // every query of the tile is before this wave's first visible position: nothing to do
-    if (MK && min(q0 + kBQ, Nq) - 1 + shift < kw) return;
+    if (MK && min(q0 + kBQ, nq) - 1 + shift < kw) return;
 #pragma unroll
     for (int qb = 0; qb < kBQ / 32; ++qb) {
       // keep the two 32-query blocks apart: overlapping them would double the live scores and
@@ -322,9 +339,12 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   }
   if (t < t1) step(I0(), BF(), t);
 
-  if (key < Nk) {
+  if (key < nk) {
     store_row<D>(dK + ((size_t)bh * Nk + key) * D, dk, scale, hi);
     store_row<D>(dV + ((size_t)bh * Nk + key) * D, dv, 1.f, hi);
+  } else if (VL && key < Nk) {  // padding keys
+    store_zero_row<D>(dK + ((size_t)bh * Nk + key) * D, hi);
+    store_zero_row<D>(dV + ((size_t)bh * Nk + key) * D, hi);
   }
 #endif
 }
@@ -341,11 +361,12 @@ struct DqLds {
   using VTile = PaddedTile<D, VST>;
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VL>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
-    bf16* __restrict__ dQ, int BH, int Nq, int Nk, float c, float scale) {
+    bf16* __restrict__ dQ, const int* __restrict__ lens_q, const int* __restrict__ lens_k,
+    int BH, int H, int Nq, int Nk, float c, float scale) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using SM = DqLds<D>;
   // one array per buffer: the LDS copies into one buffer then provably do not alias the reads of
@@ -365,7 +386,9 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   const int q0 = qt * kBR;
   const int qw = q0 + wave * 32;
   const int qi = qw + l32;
-  const int shift = Nk - Nq;
+  const int nq = VL ? min(max(lens_q[bh / H], 0), Nq) : Nq;  // valid lengths of this sequence
+  const int nk = VL ? min(max(lens_k[bh / H], 0), Nk) : Nk;
+  const int shift = nk - nq;
 
   const bf16* Kh = K + (size_t)bh * Nk * D;
   const bf16* Vh = V + (size_t)bh * Nk * D;
@@ -375,15 +398,15 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (qi < Nq) {
+    if (qi < nq) {
       a = ld16(Q + ((size_t)bh * Nq + qi) * D + ks * 16 + hi * 8);
       b = ld16(dO + ((size_t)bh * Nq + qi) * D + ks * 16 + hi * 8);
     }
     qf[ks] = as_bf16x8(a);
     dof[ks] = as_bf16x8(b);
   }
-  const float lq = qi < Nq ? L2[(size_t)bh * Nq + qi] : 0.f;
-  const float dq_d = qi < Nq ? Dl[(size_t)bh * Nq + qi] : 0.f;
+  const float lq = qi < nq ? L2[(size_t)bh * Nq + qi] : 0.f;
+  const float dq_d = qi < nq ? Dl[(size_t)bh * Nq + qi] : 0.f;
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -391,13 +414,14 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  int kend = Nk;
-  if (CAUSAL) kend = min(Nk, min(q0 + kBR, Nq) + shift);
-  const int ntiles = (kend + kBC - 1) / kBC;
-  const int horizon = CAUSAL ? min(qw + 31, Nq - 1) + shift : Nk - 1;
-  // leading tiles that need no mask for any row of the workgroup: below N_k, and (causal) every
-  // key at or before the first row's diagonal
-  int nfull = Nk / kBC;
+  int kend = nk;
+  if (CAUSAL) kend = min(nk, min(q0 + kBR, nq) + shift);
+  if (VL && q0 >= nq) kend = 0;  // every row of the workgroup is padding
+  const int ntiles = max(0, (kend + kBC - 1) / kBC);
+  const int horizon = CAUSAL ? min(qw + 31, nq - 1) + shift : nk - 1;
+  // leading tiles that need no mask for any row of the workgroup: below the key length, and
+  // (causal) every key at or before the first row's diagonal
+  int nfull = nk / kBC;
   if (CAUSAL) nfull = min(nfull, max(0, q0 + shift + 1) / kBC);
   nfull = min(nfull, ntiles);
 
@@ -408,7 +432,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   const int krow = key_of_row(l32);
   const int kro = krow * SM::KST + hi * 16, vro = krow * SM::VST + hi * 16;
   const int trb = tr_base<SM::KST>(lane);
-  const int lim = CAUSAL ? min(Nk - 1, qi + shift) : Nk - 1;
+  const int lim = CAUSAL ? min(nk - 1, qi + shift) : nk - 1;
 
   // One key tile t from buffer P (K tile kt, V tile vt); the copies of tile t+1 go to the other
   // buffer. MASKED: tiles on the causal diagonal or past N_k; waves whose rows see no key of the
@@ -421,8 +445,8 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
     wait_vmem();
     __syncthreads();
     if (t + 1 < ntiles) {
-      ktile.copy(Kh, (t + 1) * kBC, Nk, P ? kb0 : kb1, wave);
-      vtile.copy(Vh, (t + 1) * kBC, Nk, P ? vb0 : vb1, wave);
+      ktile.copy(Kh, (t + 1) * kBC, nk, P ? kb0 : kb1, wave);
+      vtile.copy(Vh, (t + 1) * kBC, nk, P ? vb0 : vb1, wave);
     }
     const int kbase = t * kBC;
     if (MK && kbase > horizon) return;
@@ -478,8 +502,8 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   using BF = std::integral_constant<bool, false>;
 
   if (ntiles > 0) {
-    ktile.copy(Kh, 0, Nk, kb0, wave);
-    vtile.copy(Vh, 0, Nk, vb0, wave);
+    ktile.copy(Kh, 0, nk, kb0, wave);
+    vtile.copy(Vh, 0, nk, vb0, wave);
   }
   int t = 0;
   for (; t + 1 < nfull; t += 2) {
@@ -497,12 +521,13 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   }
   if (t < ntiles) step(I0(), BT(), t);
 
-  if (qi < Nq) store_row<D>(dQ + ((size_t)bh * Nq + qi) * D, acc, scale, hi);
+  if (qi < nq) store_row<D>(dQ + ((size_t)bh * Nq + qi) * D, acc, scale, hi);
+  else if (VL && qi < Nq) store_zero_row<D>(dQ + ((size_t)bh * Nq + qi) * D, hi);  // padding
 #endif
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VL>
 hipError_t launch(const BwdArgs& a, unsigned phases) {
   const int BH = a.B * a.H;
   const float c = a.scale * kLog2e;
@@ -519,17 +544,18 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
   if (phases & 2u) {
     const long long grid = (long long)BH * ((a.Nk + kBKV - 1) / kBKV);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kNT), 0, a.stream,
-                       a.q, a.k, a.v, a.dout, lse2, a.delta, a.dk, a.dv, BH, a.Nq, a.Nk, c,
-                       a.scale);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL>), dim3((unsigned)grid), dim3(kNT), 0,
+                       a.stream, a.q, a.k, a.v, a.dout, lse2, a.delta, a.dk, a.dv, a.lens_q,
+                       a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (phases & 4u) {
     const long long grid = (long long)BH * ((a.Nq + kBR - 1) / kBR);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kNT), 0, a.stream,
-                       a.q, a.k, a.v, a.dout, lse2, a.delta, a.dq, BH, a.Nq, a.Nk, c, a.scale);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VL>), dim3((unsigned)grid), dim3(kNT), 0,
+                       a.stream, a.q, a.k, a.v, a.dout, lse2, a.delta, a.dq, a.lens_q, a.lens_k,
+                       BH, a.H, a.Nq, a.Nk, c, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -543,9 +569,15 @@ size_t bwd_lse2_offset(int B, int H, int Nq) {
   return (((size_t)B * H * Nq + 3) / 4) * 4;
 }
 
+template <int D, bool VL>
+hipError_t launch_d(const BwdArgs& a, unsigned phases) {
+  return a.causal ? launch<D, true, VL>(a, phases) : launch<D, false, VL>(a, phases);
+}
+
 hipError_t launch_bwd(const BwdArgs& a, unsigned phases) {
-  if (a.d == 128) return a.causal ? launch<128, true>(a, phases) : launch<128, false>(a, phases);
-  return a.causal ? launch<64, true>(a, phases) : launch<64, false>(a, phases);
+  const bool vl = a.lens_q != nullptr;
+  if (a.d == 128) return vl ? launch_d<128, true>(a, phases) : launch_d<128, false>(a, phases);
+  return vl ? launch_d<64, true>(a, phases) : launch_d<64, false>(a, phases);
 }
 
 }  // namespace fa

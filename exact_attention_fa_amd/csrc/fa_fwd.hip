@@ -56,10 +56,14 @@ struct FwdLds {
   static_assert(KI * 64 == kBC * KCPR && VI * 64 == kBC * VCPR, "tiles are whole wave copies");
 };
 
-template <int D, int NW, bool CAUSAL>
+// VL: per-sequence lengths lens_q[b] <= Nq, lens_k[b] <= Nk inside the padded [B, H, N, d]
+// tensors; query rows past a sequence's length, and rows that see no key, get O = 0 and
+// LSE = -inf.
+template <int D, int NW, bool CAUSAL, bool VL>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64) void fwd_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int Nq, int Nk, float c) {
+    bf16* __restrict__ O, float* __restrict__ LSE, const int* __restrict__ lens_q,
+    const int* __restrict__ lens_k, int BH, int H, int Nq, int Nk, float c) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using L = FwdLds<D>;
   constexpr int BR = NW * 32;  // query rows per workgroup
@@ -93,17 +97,21 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
   const int q0 = qt * BR;
   const int qw = q0 + wave * 32;  // first query row of this wave
   const int qi = qw + l32;        // this lane's query row
-  const int shift = Nk - Nq;      // causal: key j visible to query i iff j <= i + shift
+  // valid lengths of this sequence (the whole padded extent without per-sequence lengths)
+  const int nq = VL ? min(max(lens_q[bh / H], 0), Nq) : Nq;
+  const int nk = VL ? min(max(lens_k[bh / H], 0), Nk) : Nk;
+  const int shift = nk - nq;      // causal: key j visible to query i iff j <= i + shift
 
   const bf16* Qh = Q + (size_t)bh * Nq * D;
   const bf16* Kh = K + (size_t)bh * Nk * D;
   const bf16* Vh = V + (size_t)bh * Nk * D;
 
-  int kend = Nk;
-  if (CAUSAL) kend = min(Nk, min(q0 + BR, Nq) + shift);
-  const int ntiles = (kend + kBC - 1) / kBC;
+  int kend = nk;
+  if (CAUSAL) kend = min(nk, min(q0 + BR, nq) + shift);
+  if (VL && q0 >= nq) kend = 0;  // every row of the workgroup is padding
+  const int ntiles = max(0, (kend + kBC - 1) / kBC);
   // last tile any row of this wave can see
-  const int horizon = CAUSAL ? min(qw + 31, Nq - 1) + shift : Nk - 1;
+  const int horizon = CAUSAL ? min(qw + 31, nq - 1) + shift : nk - 1;
   const int last_tile = min(ntiles - 1, horizon / kBC);
 
   // ---- LDS fill: copy p of a tile (wave-wide, 64 consecutive 16-byte chunks) lands at chunk
@@ -120,7 +128,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     voff[i] = row * D * 2 + (ch < D / 8 ? ch : 0) * 16;
   }
   auto tile_rsrc = [&](const bf16* base, int t) {
-    const int rows = max(0, Nk - t * kBC);  // reads at or past N_k return zero
+    const int rows = max(0, nk - t * kBC);  // reads at or past the key length return zero
     return make_rsrc(base + (size_t)t * kBC * D, rows * D * 2);
   };
   auto copy_k = [&](int t, unsigned char* dst) {
@@ -141,7 +149,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (qi < Nq) x = ld16(Qh + (size_t)qi * D + ks * 16 + hi * 8);
+    if (qi < nq) x = ld16(Qh + (size_t)qi * D + ks * 16 + hi * 8);
     qf[ks] = as_bf16x8(x);
   }
   f32x16 oacc[D / 32];
@@ -190,9 +198,9 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     if (t + 1 < ntiles) copy_v(t + 1, P ? vb0 : vb1);
     if (t > last_tile) return;  // every row of this wave is masked from here on
     const int kbase = t * kBC;
-    const bool need_mask = (kbase + kBC > Nk) || (CAUSAL && kbase + kBC - 1 > qw + shift);
+    const bool need_mask = (kbase + kBC > nk) || (CAUSAL && kbase + kBC - 1 > qw + shift);
     if (need_mask) {
-      const int lim = CAUSAL ? min(Nk - 1, qi + shift) : Nk - 1;
+      const int lim = CAUSAL ? min(nk - 1, qi + shift) : nk - 1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         if (kbase + key_of_reg(r, hi) > lim) sc0[r] = kNegInf;
@@ -208,8 +216,11 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     }
     const float mx = halves_max(fmaxf(fmaxf(ma, sc0[15]), fmaxf(mb, sc1[15]))) * c;
     if (__any(mx > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mx);  // finite: key 0 of tile 0 is visible to every row
-      const float alpha = exp2_fast(m_run - m_new);
+      // finite for every row that sees a key: key 0 of tile 0 is visible to all of them
+      const float m_new = fmaxf(m_run, mx);
+      // a row that has seen no key yet has nothing to rescale; with per-sequence lengths it may
+      // still have no key here (m_new = -inf), and exp2(-inf - -inf) would be NaN
+      const float alpha = (VL && m_new == kNegInf) ? 1.f : exp2_fast(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
       lq_run *= alpha;
@@ -221,10 +232,13 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     // Issued unconditionally so that it shares a basic block with the softmax below; past the
     // last tile it reads stale (in-bounds) LDS and its result is never used.
     qk(sn0, sn1, P ? kb0 : kb1);
+    // a row that sees no key at all (possible only with per-sequence lengths) keeps m = -inf;
+    // reference it to 0 so that its probabilities are exp2(-inf) = 0, not NaN
+    const float m_use = (VL && m_run == kNegInf) ? 0.f : m_run;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      sc0[r] = exp2_fast(__builtin_fmaf(sc0[r], c, -m_run));
-      sc1[r] = exp2_fast(__builtin_fmaf(sc1[r], c, -m_run));
+      sc0[r] = exp2_fast(__builtin_fmaf(sc0[r], c, -m_use));
+      sc1[r] = exp2_fast(__builtin_fmaf(sc1[r], c, -m_use));
     }
     float ps[4];
 #pragma unroll
@@ -265,7 +279,8 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
   const float l_tot = halves_sum(l_run);
   const float lq_tot = halves_sum(lq_run);
   if (qi < Nq) {
-    const float inv = 1.f / lq_tot;
+    const bool empty = VL && (qi >= nq || lq_tot == 0.f);  // padding, or a row that sees no key
+    const float inv = empty ? 0.f : 1.f / lq_tot;
     bf16* orow = O + ((size_t)bh * Nq + qi) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -276,28 +291,35 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
         w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * j + 4 * hi) = w;
       }
-    if (hi == 0) LSE[(size_t)bh * Nq + qi] = (m_run + log2_fast(l_tot)) * kLn2;
+    if (hi == 0) LSE[(size_t)bh * Nq + qi] = empty ? kNegInf : (m_run + log2_fast(l_tot)) * kLn2;
   }
 #endif
 }
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, bool CAUSAL, bool VL>
 hipError_t launch(const FwdArgs& a) {
   constexpr int BR = NW * 32;
   const int nqt = (a.Nq + BR - 1) / BR;
   const long long grid = (long long)a.B * a.H * nqt;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float c = a.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_kernel<D, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     a.stream, a.q, a.k, a.v, a.o, a.lse, a.B * a.H, a.Nq, a.Nk, c);
+  hipLaunchKernelGGL((fwd_kernel<D, NW, CAUSAL, VL>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                     a.stream, a.q, a.k, a.v, a.o, a.lse, a.lens_q, a.lens_k, a.B * a.H, a.H,
+                     a.Nq, a.Nk, c);
   return hipGetLastError();
 }
 
 }  // namespace
 
+template <int D, bool VL>
+hipError_t launch_d(const FwdArgs& a) {
+  return a.causal ? launch<D, 8, true, VL>(a) : launch<D, 8, false, VL>(a);
+}
+
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch<128, 8, true>(a) : launch<128, 8, false>(a);
-  return a.causal ? launch<64, 8, true>(a) : launch<64, 8, false>(a);
+  const bool vl = a.lens_q != nullptr;
+  if (a.d == 128) return vl ? launch_d<128, true>(a) : launch_d<128, false>(a);
+  return vl ? launch_d<64, true>(a) : launch_d<64, false>(a);
 }
 
 }  // namespace fa

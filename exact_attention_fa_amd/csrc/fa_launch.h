@@ -16,6 +16,8 @@ struct FwdArgs {
   float scale;
   bool causal;
   hipStream_t stream;
+  const int* lens_q = nullptr;  // per-sequence lengths (both or neither), device int32 [B]
+  const int* lens_k = nullptr;
 };
 
 struct BwdArgs {
@@ -33,6 +35,8 @@ struct BwdArgs {
   float scale;
   bool causal;
   hipStream_t stream;
+  const int* lens_q = nullptr;  // per-sequence lengths (both or neither), device int32 [B]
+  const int* lens_k = nullptr;
 };
 
 struct DecodeArgs {

@@ -103,3 +103,21 @@ def paged_kv_bf16(seed: int, B: int, H_kv: int, seq_lens, d: int, block_size: in
             kc[blocks, h, rows] = slice_bf16(seed, "k", b, h, n, d)
             vc[blocks, h, rows] = slice_bf16(seed, "v", b, h, n, d)
     return kc, vc, table, lens
+
+
+def varlen_lengths(seed: int, B: int, n_min: int, n_max: int) -> np.ndarray:
+    """Per-sequence lengths of a variable-length batch: int32 [B], uniform on [n_min, n_max]."""
+    g = Generator(PCG64(SeedSequence([seed, 11, B, n_min, n_max])))
+    return g.integers(n_min, n_max + 1, size=B).astype(np.int32)
+
+
+BF16_NAN = 0x7FC0
+
+
+def fill_padding(u16: np.ndarray, lens, pattern: int = BF16_NAN) -> np.ndarray:
+    """Copy of a [B, H, n, d] bf16 tensor with rows n >= lens[b] of batch entry b set to a bit
+    pattern (default: a quiet NaN), so that a test can show those rows are never used."""
+    out = np.array(u16, copy=True)
+    for b, n in enumerate(np.asarray(lens)):
+        out[b, :, max(int(n), 0):] = pattern
+    return out

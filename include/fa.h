@@ -113,6 +113,33 @@ fa_status fa_bwd_dq(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const 
                     fa_bf16* dq, void* workspace, size_t workspace_bytes, int B, int H, int N_q,
                     int N_k, int d, float scale, int causal, hipStream_t stream);
 
+/* ---- Variable-length batches ------------------------------------------------------------------
+ *
+ * Batches whose sequences have different lengths, kept in the padded layouts above: sequence b
+ * uses its first seq_lens_q[b] query rows and first seq_lens_k[b] key rows of the [B, H, N_q, d]
+ * and [B, H, N_k, d] tensors (device int32 arrays [B]; values are clamped to [0, N_q] and
+ * [0, N_k]). The pages do not define batching ([MW] "Attention'ın Cebiri" defines one sequence);
+ * each sequence here is that definition on its own lengths, with the causal alignment of the
+ * "Maskeleme ve Dropout" reading applied per sequence: key j visible to query i iff
+ * j <= i + seq_lens_k[b] - seq_lens_q[b]. A query row past its sequence's length, or one that
+ * sees no key (causal with seq_lens_q[b] > seq_lens_k[b]), gets o = 0 and lse = -inf; the
+ * backward gives zero gradients for padding rows and keys and for rows that see no key.
+ * Rows and keys past a sequence's lengths are never read, so the padding may hold any bit
+ * pattern (NaN included). Because the lengths live on the device, causal is accepted for any
+ * N_q, N_k.
+ * seq_lens_q, seq_lens_k: 4-byte aligned; other arguments as for fa_fwd / fa_bwd (the backward
+ * uses the same workspace size, fa_bwd_workspace_bytes).
+ */
+fa_status fa_fwd_varlen(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
+                        float* lse, const int32_t* seq_lens_q, const int32_t* seq_lens_k,
+                        int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                        hipStream_t stream);
+fa_status fa_bwd_varlen(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                        const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk,
+                        fa_bf16* dv, const int32_t* seq_lens_q, const int32_t* seq_lens_k,
+                        void* workspace, size_t workspace_bytes, int B, int H, int N_q, int N_k,
+                        int d, float scale, int causal, hipStream_t stream);
+
 /* The split count fa_decode uses when called with num_splits = 0. */
 int fa_decode_num_splits(int B, int H, int N_k, int d);
 

@@ -29,7 +29,11 @@ Readings where the pages are silent (each also listed in the design notes):
     no row is empty;
   * the stored statistic is the natural-log log-sum-exp of the scaled, masked scores,
     L_i = ln sum_j exp(S_ij);
-  * d_v = d.
+  * d_v = d;
+  * a batch of different-length sequences (padded tensors plus per-sequence lengths) is the
+    single-sequence definition applied to each sequence's own rows and keys, causal alignment
+    per sequence; a row that sees no key (padding, or causal with more queries than keys) has
+    o = 0 and lse = -inf and contributes no gradient.
 
 Every function here is pinned by tests that do not reuse its formulas: brute-force per-row
 softmax in pure Python, rows of P summing to one, bitwise causal invariance to future keys,
@@ -211,3 +215,84 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale: float):
                 ob, lb = forward_head(np.asarray(q[b, h])[None, :], kk, vv, scale, causal=False)
                 o[b, h], lse[b, h] = ob[0], lb[0]
     return o, lse
+
+
+def _clamp_len(x, n: int) -> int:
+    return min(max(int(x), 0), n)
+
+
+def visible_varlen(l_q: int, l_k: int, causal: bool) -> np.ndarray:
+    """Boolean [l_q, l_k] visibility for one sequence of a variable-length batch.
+
+    Same bottom-right causal alignment as `visible`, key j visible to query i iff
+    j <= i + l_k - l_q, but l_q > l_k is allowed: the first l_q - l_k query rows then see no
+    key at all (reading: such a row has no softmax, it gets o = 0 and lse = -inf).
+    """
+    if not causal:
+        return np.ones((l_q, l_k), dtype=bool)
+    i = np.arange(l_q)[:, None]
+    j = np.arange(l_k)[None, :]
+    return j <= i + (l_k - l_q)
+
+
+def _varlen_probs(qs, ks, mask, scale):
+    # scores of the rows that see at least one key, masked entries -inf, then the row softmax
+    s = scale * (qs @ ks.T)
+    s[~mask] = -np.inf
+    return softmax_rows(s)
+
+
+def forward_varlen(q, k, v, seq_lens_q, seq_lens_k, scale: float, causal: bool):
+    """Forward over a batch of sequences of different lengths held in padded tensors.
+
+    q [B,H,N_q,d], k/v [B,H,N_k,d]; sequence b uses its first seq_lens_q[b] query rows and
+    first seq_lens_k[b] key rows (lengths clamped to [0, N]). The pages define attention for one
+    sequence ([MW] "Attention'ın Cebiri"); the reading for a batch is that definition on each
+    sequence's own rows and keys, with the causal mask of [MW] "Maskeleme ve Dropout" aligned
+    per sequence (`visible_varlen`). Padding rows, and rows that see no key, get o = 0 and
+    lse = -inf. Returns (o [B,H,N_q,d_v], lse [B,H,N_q]) fp64.
+    """
+    B, H, n_q, _ = np.shape(q)
+    n_k = np.shape(k)[2]
+    o = np.zeros((B, H, n_q, np.shape(v)[3]), dtype=np.float64)
+    lse = np.full((B, H, n_q), -np.inf, dtype=np.float64)
+    for b in range(B):
+        lq, lk = _clamp_len(seq_lens_q[b], n_q), _clamp_len(seq_lens_k[b], n_k)
+        mask = visible_varlen(lq, lk, causal)
+        live = np.flatnonzero(mask.any(axis=1))
+        if live.size == 0:
+            continue
+        for h in range(H):
+            p, l_ = _varlen_probs(_f64(q[b, h, :lq])[live], _f64(k[b, h, :lk]), mask[live], scale)
+            o[b, h, live] = p @ _f64(v[b, h, :lk])
+            lse[b, h, live] = l_
+    return o, lse
+
+
+def backward_varlen(q, k, v, do, seq_lens_q, seq_lens_k, scale: float, causal: bool):
+    """Gradients of forward_varlen's o with respect to q, k, v (the chain rule of
+    [MW] "Geri Yayılım" on each sequence's live rows and keys). Padding rows and keys, and
+    rows that see no key, have zero gradient: o does not depend on them (the o = 0 of an
+    empty row is a constant). Returns (dq, dk, dv) fp64, shaped like (q, k, v).
+    """
+    B, H, n_q, _ = np.shape(q)
+    n_k = np.shape(k)[2]
+    dq = np.zeros(np.shape(q), dtype=np.float64)
+    dk = np.zeros(np.shape(k), dtype=np.float64)
+    dv = np.zeros(np.shape(v), dtype=np.float64)
+    for b in range(B):
+        lq, lk = _clamp_len(seq_lens_q[b], n_q), _clamp_len(seq_lens_k[b], n_k)
+        mask = visible_varlen(lq, lk, causal)
+        live = np.flatnonzero(mask.any(axis=1))
+        if live.size == 0:
+            continue
+        for h in range(H):
+            qs, ks = _f64(q[b, h, :lq])[live], _f64(k[b, h, :lk])
+            vs, dos = _f64(v[b, h, :lk]), _f64(do[b, h, :lq])[live]
+            p, _ = _varlen_probs(qs, ks, mask[live], scale)
+            dv[b, h, :lk] = p.T @ dos
+            dp = dos @ vs.T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dq[b, h, live] = scale * (ds @ ks)
+            dk[b, h, :lk] = scale * (ds.T @ qs)
+    return dq, dk, dv

@@ -313,7 +313,122 @@ def pin_paged_invariances():
     assert np.all(o[1] == 0.0) and np.all(np.isneginf(lse[1])) and np.all(np.isfinite(lse[0]))
 
 
+VARLEN_CASES = [  # (N_q, N_k, d, seq_lens_q, seq_lens_k)
+    (7, 9, 4, [7, 3, 0, 5, 6], [9, 4, 6, 2, 0]),
+    (6, 5, 8, [6, 2, 1], [5, 5, 1]),
+    (4, 4, 4, [4, 9, -3], [4, 2, 7]),   # lengths beyond N or below 0 are clamped
+]
+
+
+def _varlen_case(rng, B, H, n_q, n_k, d):
+    return (rng.standard_normal((B, H, n_q, d)), rng.standard_normal((B, H, n_k, d)),
+            rng.standard_normal((B, H, n_k, d)), rng.standard_normal((B, H, n_q, d)))
+
+
+def pin_varlen_brute_force():
+    """Each sequence's rows by direct loops over its own keys with math.exp: key j is
+    visible to row i of a sequence with l_q rows and l_k keys iff j < l_k and, if causal,
+    j <= i + l_k - l_q; a row with no visible key, or past l_q, is o = 0, lse = -inf."""
+    rng = _rng(13)
+    for n_q, n_k, d, lq_list, lk_list in VARLEN_CASES:
+        B, H = len(lq_list), 2
+        q, k, v, _ = _varlen_case(rng, B, H, n_q, n_k, d)
+        lens_q, lens_k = np.array(lq_list), np.array(lk_list)
+        for causal in (False, True):
+            o, lse = A.forward_varlen(q, k, v, lens_q, lens_k, 0.45, causal)
+            for b in range(B):
+                lq = min(max(lq_list[b], 0), n_q)
+                lk = min(max(lk_list[b], 0), n_k)
+                for h in range(H):
+                    for i in range(n_q):
+                        keys = [j for j in range(lk)
+                                if i < lq and (not causal or j <= i + lk - lq)]
+                        if not keys:
+                            assert np.all(o[b, h, i] == 0.0) and lse[b, h, i] == -math.inf
+                            continue
+                        s = [0.45 * sum(q[b, h, i, t] * k[b, h, j, t] for t in range(d))
+                             for j in keys]
+                        mx = max(s)
+                        w = [math.exp(x - mx) for x in s]
+                        z = sum(w)
+                        for t in range(d):
+                            ref = sum(w[m] * v[b, h, j, t] for m, j in enumerate(keys)) / z
+                            assert abs(o[b, h, i, t] - ref) <= 1e-12 * (1 + abs(ref)), \
+                                (n_q, n_k, b, h, i, t, causal)
+                        assert abs(lse[b, h, i] - (mx + math.log(z))) <= 1e-12 * (1 + abs(mx))
+
+
+def pin_varlen_padding_and_truncation():
+    """Values in the padding (query rows past l_q, keys past l_k, dO on padding rows) change
+    nothing, bitwise, and padding gradients are exactly zero; a sequence equals the dense
+    oracle on its truncated tensors (for causal l_q > l_k: its last l_k rows equal square
+    causal attention on those rows, its first rows are empty)."""
+    rng = _rng(14)
+    for n_q, n_k, d, lq_list, lk_list in VARLEN_CASES:
+        B, H = len(lq_list), 2
+        q, k, v, do = _varlen_case(rng, B, H, n_q, n_k, d)
+        lens_q, lens_k = np.array(lq_list), np.array(lk_list)
+        for causal in (False, True):
+            o, lse = A.forward_varlen(q, k, v, lens_q, lens_k, 0.7, causal)
+            g = A.backward_varlen(q, k, v, do, lens_q, lens_k, 0.7, causal)
+            q2, k2, v2, do2 = q.copy(), k.copy(), v.copy(), do.copy()
+            for b in range(B):
+                lq = min(max(lq_list[b], 0), n_q)
+                lk = min(max(lk_list[b], 0), n_k)
+                q2[b, :, lq:] = 50.0 * rng.standard_normal(q2[b, :, lq:].shape)
+                do2[b, :, lq:] = rng.standard_normal(do2[b, :, lq:].shape)
+                k2[b, :, lk:] = -50.0 * rng.standard_normal(k2[b, :, lk:].shape)
+                v2[b, :, lk:] = 1e3
+                assert np.all(g[0][b, :, lq:] == 0.0)
+                assert np.all(g[1][b, :, lk:] == 0.0) and np.all(g[2][b, :, lk:] == 0.0)
+                assert np.all(o[b, :, lq:] == 0.0) and np.all(np.isneginf(lse[b, :, lq:]))
+                if lq == 0 or lk == 0:
+                    assert np.all(o[b] == 0.0) and np.all(np.isneginf(lse[b]))
+                    assert all(np.all(x[b] == 0.0) for x in g)
+                    continue
+                r0 = max(0, lq - lk) if causal else 0     # first row that sees a key
+                sq = slice(r0, lq)
+                od, ld = A.forward(q[b:b + 1, :, sq], k[b:b + 1, :, :lk], v[b:b + 1, :, :lk],
+                                   0.7, causal)
+                assert np.allclose(o[b, :, sq], od[0], rtol=0, atol=1e-13)
+                assert np.allclose(lse[b, :, sq], ld[0], rtol=0, atol=1e-13)
+                assert np.all(o[b, :, :r0] == 0.0) and np.all(np.isneginf(lse[b, :, :r0]))
+                gd = A.backward(q[b:b + 1, :, sq], k[b:b + 1, :, :lk], v[b:b + 1, :, :lk],
+                                do[b:b + 1, :, sq], 0.7, causal)
+                assert np.allclose(g[0][b, :, sq], gd[0][0], rtol=0, atol=1e-12)
+                assert np.all(g[0][b, :, :r0] == 0.0)
+                assert np.allclose(g[1][b, :, :lk], gd[1][0], rtol=0, atol=1e-12)
+                assert np.allclose(g[2][b, :, :lk], gd[2][0], rtol=0, atol=1e-12)
+            o2, lse2 = A.forward_varlen(q2, k2, v2, lens_q, lens_k, 0.7, causal)
+            g2 = A.backward_varlen(q2, k2, v2, do2, lens_q, lens_k, 0.7, causal)
+            assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+            assert all(np.array_equal(x, y) for x, y in zip(g, g2))
+
+
+def pin_varlen_finite_differences():
+    """Central differences of sum(o * W) match backward_varlen, padding entries included
+    (there the difference is exactly zero)."""
+    rng = _rng(15)
+    n_q, n_k, d = 5, 4, 3
+    lens_q, lens_k = np.array([5, 3, 2]), np.array([3, 4, 0])
+    q, k, v, w = _varlen_case(rng, 3, 1, n_q, n_k, d)
+    h = 1e-6
+    for causal in (False, True):
+        dq, dk, dv = A.backward_varlen(q, k, v, w, lens_q, lens_k, 0.6, causal)
+        for x, gx in ((q, dq), (k, dk), (v, dv)):
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + h
+                fp = np.sum(A.forward_varlen(q, k, v, lens_q, lens_k, 0.6, causal)[0] * w)
+                x[idx] = old - h
+                fm = np.sum(A.forward_varlen(q, k, v, lens_q, lens_k, 0.6, causal)[0] * w)
+                x[idx] = old
+                fd = (fp - fm) / (2 * h)
+                assert abs(fd - gx[idx]) <= 1e-6 * (1 + abs(fd)), (causal, idx, fd, gx[idx])
+
+
 ALL_PINS = [pin_brute_force_rows, pin_rows_sum_to_one, pin_causal_future_invariance,
             pin_finite_differences, pin_closed_forms, pin_invariances, pin_gradient_sum_rules,
             pin_torch_sdpa, pin_hand_examples, pin_decode_split_combine,
-            pin_paged_gqa_brute_force, pin_paged_invariances]
+            pin_paged_gqa_brute_force, pin_paged_invariances, pin_varlen_brute_force,
+            pin_varlen_padding_and_truncation, pin_varlen_finite_differences]

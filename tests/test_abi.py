@@ -85,6 +85,32 @@ def test_bwd_validation(lib):
     assert call(dq=FAKE + 2) == 4
 
 
+def test_varlen_validation(lib):
+    def fwd(lq=FAKE, lk=FAKE, q=FAKE, d=64, B=2, scale=0.125, causal=1):
+        return lib.fa_fwd_varlen(q, FAKE, FAKE, FAKE, FAKE, lq, lk, B, 3, 9, 8, d, scale,
+                                 causal, None)
+    assert fwd(lq=None) == 1
+    assert fwd(lk=None) == 1
+    assert fwd(q=None) == 1
+    assert fwd(lq=FAKE + 2) == 4
+    assert fwd(lk=FAKE + 1) == 4
+    assert fwd(q=FAKE + 8) == 4
+    assert fwd(d=96) == 3
+    assert fwd(B=0) == 2
+    assert fwd(scale=-1.0) == 7
+    ws = lib.fa_bwd_workspace_bytes(2, 3, 9, 8, 64)
+
+    def bwd(lq=FAKE, lk=FAKE, ws_bytes=ws, dk=FAKE, d=64):
+        return lib.fa_bwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dk, FAKE, lq, lk,
+                                 FAKE, ws_bytes, 2, 3, 9, 8, d, 0.125, 1, None)
+    assert bwd(lq=None) == 1
+    assert bwd(lk=FAKE + 2) == 4
+    assert bwd(dk=None) == 1
+    assert bwd(dk=FAKE + 2) == 4
+    assert bwd(ws_bytes=ws - 16) == 6
+    assert bwd(d=32) == 3
+
+
 def test_bwd_phase_validation(lib):
     ws = lib.fa_bwd_workspace_bytes(1, 2, 64, 64, 128)
     assert ws == 2 * 2 * 64 * 4

@@ -162,10 +162,52 @@ def _decode_paged_head_modulo(q, k_cache, v_cache, block_table, seq_lens, scale)
     return o, lse
 
 
+_orig_fwd_varlen = A.forward_varlen
+_orig_bwd_varlen = A.backward_varlen
+
+
+def _visible_varlen_top_left(l_q, l_k, causal):
+    if not causal:
+        return np.ones((l_q, l_k), dtype=bool)
+    return np.arange(l_k)[None, :] <= np.arange(l_q)[:, None]
+
+
+def _visible_varlen_padded_shift(l_q, l_k, causal):
+    # empty causal rows wrongly see the first key (a clamped shift)
+    m = _orig_visible_varlen(l_q, l_k, causal)
+    if causal and l_k > 0:
+        m[:, 0] = True
+    return m
+
+
+def _fwd_varlen_full_keys(q, k, v, seq_lens_q, seq_lens_k, scale, causal):
+    return _orig_fwd_varlen(q, k, v, seq_lens_q, np.full(len(seq_lens_k), np.shape(k)[2]),
+                            scale, causal)
+
+
+def _bwd_varlen_do_unaligned(q, k, v, do, seq_lens_q, seq_lens_k, scale, causal):
+    # takes dO from the first rows of the sequence instead of the live rows
+    do = np.array(do, dtype=np.float64)
+    for b in range(np.shape(q)[0]):
+        lq = min(max(int(seq_lens_q[b]), 0), np.shape(q)[2])
+        lk = min(max(int(seq_lens_k[b]), 0), np.shape(k)[2])
+        r0 = max(0, lq - lk) if causal else 0
+        if lk > 0 and r0 > 0:
+            do[b, :, r0:lq] = do[b, :, :lq - r0].copy()
+    return _orig_bwd_varlen(q, k, v, do, seq_lens_q, seq_lens_k, scale, causal)
+
+
+_orig_visible_varlen = A.visible_varlen
+
+
 MUTANTS = {
     "paged_block_and_row_swapped": ("gather_paged", _gather_block_and_row_swapped),
     "paged_ignores_block_table": ("gather_paged", _gather_physical_order),
     "gqa_head_modulo": ("decode_paged", _decode_paged_head_modulo),
+    "varlen_mask_top_left": ("visible_varlen", _visible_varlen_top_left),
+    "varlen_empty_rows_see_key0": ("visible_varlen", _visible_varlen_padded_shift),
+    "varlen_ignores_key_lengths": ("forward_varlen", _fwd_varlen_full_keys),
+    "varlen_bwd_do_unaligned": ("backward_varlen", _bwd_varlen_do_unaligned),
     "scores_no_scale": ("scores", _scores_no_scale),
     "scores_transposed": ("scores", _scores_transposed),
     "mask_off_by_one": ("visible", _visible_off_by_one),
