@@ -3,7 +3,9 @@ benchmark's CPU-baseline leg may use it; the product path never does."""
 from .attention import (backward, backward_head, backward_varlen, decode, decode_paged, forward,
                         forward_head, forward_varlen, gather_paged, scores, softmax_rows, visible,
                         visible_varlen)
+from .dropout import backward_dropout, dropout_keep, forward_dropout, keep_threshold, philox
 
 __all__ = ["backward", "backward_head", "backward_varlen", "decode", "decode_paged", "forward",
            "forward_head", "forward_varlen", "gather_paged", "scores", "softmax_rows", "visible",
-           "visible_varlen"]
+           "visible_varlen", "backward_dropout", "dropout_keep", "forward_dropout",
+           "keep_threshold", "philox"]

@@ -16,6 +16,7 @@ import os
 import numpy as np
 
 import oracle.attention as A
+import oracle.dropout as DR
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -427,8 +428,145 @@ def pin_varlen_finite_differences():
                 assert abs(fd - gx[idx]) <= 1e-6 * (1 + abs(fd)), (causal, idx, fd, gx[idx])
 
 
+
+def pin_philox_against_numpy():
+    """The Philox rounds, key schedule and word order, run at W = 64, reproduce numpy's
+    Philox4x64-10 bit generator (an independent library implementation of [PX]); numpy advances
+    its 256-bit counter by one before the first block it returns."""
+    rng = _rng(16)
+    cases = [((0, 0, 0, 0), (0, 0)), ((2**64 - 1, 2**64 - 1, 5, 9), (1, 2**63))]
+    cases += [(tuple(int(x) for x in rng.integers(0, 2**63, 4)),
+               tuple(int(x) for x in rng.integers(0, 2**63, 2))) for _ in range(6)]
+    for ctr, key in cases:
+        bg = np.random.Philox(counter=np.array(ctr, dtype=np.uint64),
+                              key=np.array(key, dtype=np.uint64))
+        want = [int(x) for x in bg.random_raw(4)]
+        total = sum(int(c) << (64 * w) for w, c in enumerate(ctr)) + 1
+        nxt = [(total >> (64 * w)) & (2**64 - 1) for w in range(4)]
+        got = [int(x) for x in DR.philox([nxt], key, word_bits=64)[0]]
+        assert got == want, (ctr, key)
+
+
+def pin_philox_constants():
+    """Weyl increments are floor(2^W (golden ratio - 1)) and floor(2^W (sqrt(3) - 1)), computed
+    here with exact integer square roots; multipliers are odd (invertible mod 2^W)."""
+    for W in (32, 64):
+        golden = (math.isqrt(5 << (2 * W)) - (1 << W)) >> 1
+        root3 = math.isqrt(3 << (2 * W)) - (1 << W)
+        assert DR.PHILOX_W[W] == (golden, root3)
+        assert all(m % 2 == 1 and m < (1 << W) for m in DR.PHILOX_M[W])
+
+
+def pin_dropout_mask_statistics():
+    """Keep rate t/65536 within five binomial standard deviations; masks of different heads,
+    offsets and seeds agree only as often as independent coins would; threshold edge values."""
+    assert DR.keep_threshold(0.0) == 65536 and DR.keep_threshold(0.5) == 32768
+    assert DR.keep_threshold(0.1) == 58982        # floor(0.9 * 65536) = floor(58982.4)
+    assert DR.keep_threshold(1 / 3) == 43690      # floor(43690.67): rounds down, not to nearest
+    n = 512
+    for p in (0.1, 0.5, 0.9):
+        t = DR.keep_threshold(p)
+        k = t / 65536
+        masks = [DR.dropout_keep(seed, off, bh, n, n, p)
+                 for seed, off, bh in ((1, 0, 0), (1, 0, 1), (1, 1, 0), (2**40 + 1, 0, 0))]
+        for m in masks:
+            sd = math.sqrt(k * (1 - k) / m.size)
+            assert abs(m.mean() - k) < 5 * sd, (p, m.mean(), k)
+            # no row or column is systematically biased
+            assert abs(m.mean(axis=1).std() - math.sqrt(k * (1 - k) / n)) < 0.3 * math.sqrt(k * (1 - k) / n)
+        agree = k * k + (1 - k) * (1 - k)
+        for a in range(len(masks)):
+            for b in range(a + 1, len(masks)):
+                frac = np.mean(masks[a] == masks[b])
+                assert abs(frac - agree) < 5 * math.sqrt(agree * (1 - agree) / masks[a].size)
+    assert np.all(DR.dropout_keep(3, 0, 0, 20, 20, 0.0))
+
+
+def pin_dropout_mask_layout():
+    """Element (i, j) is decided by number j mod 8 of the Philox call with counter
+    (j div 8, i, bh, offset), low half first; a prefix of the keys is a prefix of the mask."""
+    seed, off, bh = 0x123456789A, 77, 5
+    m = DR.dropout_keep(seed, off, bh, 9, 21, 0.4)
+    t = DR.keep_threshold(0.4)
+    for i, j in [(0, 0), (0, 1), (3, 7), (8, 8), (5, 13), (2, 20)]:
+        w = DR.philox([[j // 8, i, bh, off]], (seed % 2**32, seed >> 32))[0]
+        u = (int(w[(j % 8) // 2]) >> (16 * (j % 2))) & 0xFFFF
+        assert m[i, j] == (u < t), (i, j)
+    assert np.array_equal(DR.dropout_keep(seed, off, bh, 9, 13, 0.4), m[:, :13])
+
+
+def pin_dropout_brute_force():
+    """Direct loops: o_i = sum_j exp(s_ij - m) z_ij v_j / ((1 - p) sum_j exp(s_ij - m)), the
+    normaliser over every visible key (dropout acts after the softmax), L unchanged."""
+    rng = _rng(17)
+    for n_q, n_k, d, causal in [(5, 5, 4, True), (3, 11, 4, False), (6, 9, 8, True)]:
+        q, k, v = (rng.standard_normal((1, 2, n, d)) for n in (n_q, n_k, n_k))
+        p, seed, off = 0.3, 99, 4
+        o, lse = DR.forward_dropout(q, k, v, 0.5, causal, p, seed, off)
+        o0, lse0 = A.forward(q, k, v, 0.5, causal)
+        assert np.allclose(lse, lse0, rtol=0, atol=1e-14)
+        for h in range(2):
+            z = DR.dropout_keep(seed, off, h, n_q, n_k, p)
+            for i in range(n_q):
+                js = range(i + n_k - n_q + 1) if causal else range(n_k)
+                s = [0.5 * sum(q[0, h, i, t] * k[0, h, j, t] for t in range(d)) for j in js]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                zsum = sum(w)
+                for t in range(d):
+                    ref = sum(w[a] * z[i, j] * v[0, h, j, t] for a, j in enumerate(js)) / zsum / (1 - p)
+                    assert abs(o[0, h, i, t] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def pin_dropout_expectation_and_identities():
+    """Averaged over seeds the dropout output is the plain output (inverted dropout is
+    unbiased); p = 0 is the plain forward and backward; rowsum(P dP) = rowsum(dO O) still holds
+    with the mask (the identity the backward's D = rowsum(dO O) relies on)."""
+    rng = _rng(18)
+    q, k, v, do = (rng.standard_normal((1, 1, 6, 4)) for _ in range(4))
+    o0, _ = A.forward(q, k, v, 0.6, True)
+    n = 1500
+    acc = sum(DR.forward_dropout(q, k, v, 0.6, True, 0.25, s, 0)[0] for s in range(n)) / n
+    # per element: Var(o) <= sum_j P_ij^2 v_j^2 p/(1-p); 6 standard errors
+    P, _ = A.softmax_rows(A.scores(q[0, 0], k[0, 0], 0.6, True))
+    sd = np.sqrt((P ** 2) @ (v[0, 0] ** 2) * 0.25 / 0.75 / n)
+    assert np.all(np.abs(acc[0, 0] - o0[0, 0]) <= 6 * sd + 1e-12)
+    od, _ = DR.forward_dropout(q, k, v, 0.6, True, 0.0, 5, 1)
+    assert np.allclose(od, o0, rtol=0, atol=1e-14)
+    g0 = A.backward(q, k, v, do, 0.6, True)
+    gd = DR.backward_dropout(q, k, v, do, 0.6, True, 0.0, 5, 1)
+    assert all(np.allclose(a, b, rtol=0, atol=1e-13) for a, b in zip(g0, gd))
+    o, _ = DR.forward_dropout(q, k, v, 0.6, True, 0.4, 8, 2)
+    z = DR.dropout_keep(8, 2, 0, 6, 6, 0.4) / 0.6
+    dP = (do[0, 0] @ v[0, 0].T) * z
+    assert np.allclose(np.sum(P * dP, axis=1), np.sum(do[0, 0] * o[0, 0], axis=1), atol=1e-13)
+
+
+def pin_dropout_finite_differences():
+    """Central differences of sum(O * W) with the mask fixed match backward_dropout."""
+    rng = _rng(19)
+    q, k, v, w = (rng.standard_normal((1, 2, n, 3)) for n in (4, 5, 5, 4))
+    h = 1e-6
+    for causal in (False, True):
+        args = (0.7, causal, 0.35, 1234, 3)
+        dq, dk, dv = DR.backward_dropout(q, k, v, w, *args)
+        for x, gx in ((q, dq), (k, dk), (v, dv)):
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + h
+                fp = np.sum(DR.forward_dropout(q, k, v, *args)[0] * w)
+                x[idx] = old - h
+                fm = np.sum(DR.forward_dropout(q, k, v, *args)[0] * w)
+                x[idx] = old
+                fd = (fp - fm) / (2 * h)
+                assert abs(fd - gx[idx]) <= 1e-6 * (1 + abs(fd)), (causal, idx, fd, gx[idx])
+
+
 ALL_PINS = [pin_brute_force_rows, pin_rows_sum_to_one, pin_causal_future_invariance,
             pin_finite_differences, pin_closed_forms, pin_invariances, pin_gradient_sum_rules,
             pin_torch_sdpa, pin_hand_examples, pin_decode_split_combine,
             pin_paged_gqa_brute_force, pin_paged_invariances, pin_varlen_brute_force,
-            pin_varlen_padding_and_truncation, pin_varlen_finite_differences]
+            pin_varlen_padding_and_truncation, pin_varlen_finite_differences,
+            pin_philox_against_numpy, pin_philox_constants, pin_dropout_mask_statistics,
+            pin_dropout_mask_layout, pin_dropout_brute_force,
+            pin_dropout_expectation_and_identities, pin_dropout_finite_differences]

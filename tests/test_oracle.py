@@ -6,6 +6,7 @@ import pytest
 
 import oracle
 import oracle.attention as A
+import oracle.dropout as DR
 from tests import oracle_pins as P
 
 
@@ -200,6 +201,67 @@ def _bwd_varlen_do_unaligned(q, k, v, do, seq_lens_q, seq_lens_k, scale, causal)
 _orig_visible_varlen = A.visible_varlen
 
 
+_orig_philox = DR.philox
+_orig_keep = DR.dropout_keep
+_orig_fwd_drop = DR.forward_dropout
+_orig_bwd_drop = DR.backward_dropout
+
+
+def _philox_no_key_schedule(counters, key, word_bits=32, rounds=10):
+    saved = DR.PHILOX_W[word_bits]
+    DR.PHILOX_W[word_bits] = (0, 0)
+    try:
+        return _orig_philox(counters, key, word_bits, rounds)
+    finally:
+        DR.PHILOX_W[word_bits] = saved
+
+
+def _philox_outputs_reversed(counters, key, word_bits=32, rounds=10):
+    return _orig_philox(counters, key, word_bits, rounds)[:, ::-1]
+
+
+def _keep_transposed(seed, offset, bh, n_q, n_k, p):
+    return _orig_keep(seed, offset, bh, n_k, n_q, p).T
+
+
+def _keep_high_half_first(seed, offset, bh, n_q, n_k, p):
+    n8 = (n_k + 7) // 8 * 8
+    m = _orig_keep(seed, offset, bh, n_q, n8, p)
+    m = m.reshape(n_q, n8 // 2, 2)[:, :, ::-1].reshape(n_q, n8)
+    return m[:, :n_k]
+
+
+def _keep_threshold_rounded(p):
+    if not (0.0 <= p < 1.0):
+        raise ValueError
+    return int(round((1.0 - p) * 65536.0))
+
+
+def _fwd_drop_renormalised(q, k, v, scale, causal, p, seed, offset):
+    B, H, n_q, _ = np.shape(q)
+    n_k = np.shape(k)[2]
+    o = np.empty((B, H, n_q, np.shape(v)[3]))
+    lse = np.empty((B, H, n_q))
+    for b in range(B):
+        for h in range(H):
+            P, lse[b, h] = A.softmax_rows(A.scores(q[b, h], k[b, h], scale, causal))
+            Pz = P * DR.dropout_keep(seed, offset, b * H + h, n_q, n_k, p)
+            o[b, h] = (Pz / np.maximum(Pz.sum(axis=1, keepdims=True), 1e-300)) @ v[b, h]
+    return o, lse
+
+
+def _fwd_drop_no_inverse_scale(q, k, v, scale, causal, p, seed, offset):
+    o, lse = _orig_fwd_drop(q, k, v, scale, causal, p, seed, offset)
+    return o * (1.0 - p), lse
+
+
+def _bwd_drop_unmasked_dp(q, k, v, do, scale, causal, p, seed, offset):
+    # the mask applied to dV only, not to dP
+    dq, dk, dv = _orig_bwd_drop(q, k, v, do, scale, causal, p, seed, offset)
+    gq, gk, _ = A.backward(q, k, v, do, scale, causal)
+    return gq, gk, dv
+
+
 MUTANTS = {
     "paged_block_and_row_swapped": ("gather_paged", _gather_block_and_row_swapped),
     "paged_ignores_block_table": ("gather_paged", _gather_physical_order),
@@ -208,6 +270,14 @@ MUTANTS = {
     "varlen_empty_rows_see_key0": ("visible_varlen", _visible_varlen_padded_shift),
     "varlen_ignores_key_lengths": ("forward_varlen", _fwd_varlen_full_keys),
     "varlen_bwd_do_unaligned": ("backward_varlen", _bwd_varlen_do_unaligned),
+    "philox_no_key_schedule": ("philox", _philox_no_key_schedule, DR),
+    "philox_outputs_reversed": ("philox", _philox_outputs_reversed, DR),
+    "dropout_mask_transposed": ("dropout_keep", _keep_transposed, DR),
+    "dropout_high_half_first": ("dropout_keep", _keep_high_half_first, DR),
+    "dropout_threshold_rounded": ("keep_threshold", _keep_threshold_rounded, DR),
+    "dropout_renormalised": ("forward_dropout", _fwd_drop_renormalised, DR),
+    "dropout_no_inverse_scale": ("forward_dropout", _fwd_drop_no_inverse_scale, DR),
+    "dropout_bwd_unmasked_dp": ("backward_dropout", _bwd_drop_unmasked_dp, DR),
     "scores_no_scale": ("scores", _scores_no_scale),
     "scores_transposed": ("scores", _scores_transposed),
     "mask_off_by_one": ("visible", _visible_off_by_one),
@@ -224,8 +294,8 @@ MUTANTS = {
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(name, monkeypatch):
-    attr, fn = MUTANTS[name]
-    monkeypatch.setattr(A, attr, fn)
+    attr, fn, *mod = MUTANTS[name]
+    monkeypatch.setattr(mod[0] if mod else A, attr, fn)
     caught = []
     for pin in P.ALL_PINS:
         try:
