@@ -9,10 +9,10 @@ One step = one pass over every kernel of the path on synthetic bf16 inputs alrea
 4 B H N^2 d, halved for the causal mask, times 3.5 for forward plus 2.5x backward), from the HIP
 events around those kernels; `ms_per_step` is the wall time of the whole step including the decode.
 The decode is reported in GB/s of K and V read. Every kernel's own rate and roofline fraction is
-listed, and `roofline` repeats the entry of the step's kernel that takes the most time. Two more
-entries are timed apart from the step: the paged-cache decode with grouped query heads, and a
+listed, and `roofline` repeats the entry of the step's kernel that takes the most time. Further
+entries are timed apart from the step: the paged-cache decode with grouped query heads, a
 causal forward + backward over a batch of eight sequences of different lengths (TFLOP/s of the
-valid rows and keys only).
+valid rows and keys only), and the forward + backward workload with dropout on P.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -36,6 +36,7 @@ PAGED = dict(H_kv=8, block_size=16, seed=9)  # paged GQA decode: the decode work
                                              # K/V heads as a shuffled block cache, 4 q heads each
 VARLEN = dict(B=8, H=16, N=8192, d=128, n_min=1024, causal=True, seed=21)  # variable lengths,
                                              # uniform on [n_min, N], padded to N
+DROPOUT = dict(p=0.1, seed=0x5EED, offset=0)  # dropout on P over the forward+backward workload
 
 
 def log(msg: str) -> None:
@@ -336,6 +337,31 @@ def main() -> int:
     kernels["bwd_varlen"] = mfma_entry(2.5 * vf_flops, vb_ms,
                                        vnote + "; preprocess + dK/dV + dQ, 2.5x the forward")
     del vq, vk, vv, vdo, vo, vgrads, vws
+
+    # ---- dropout on P: the forward + backward workload again (timed on its own, outside the step)
+    dp_, dseed, doff = DROPOUT["p"], DROPOUT["seed"], DROPOUT["offset"]
+    run_df = lambda: fa.fwd_dropout(q, k, v, dp_, dseed, doff, causal=causal, out=(o, lse))  # noqa: E731
+    run_db = lambda: fa.bwd_dropout(q, k, v, o, lse, do, dp_, dseed, doff, causal=causal,  # noqa: E731
+                                    workspace=ws, out=(dq, dk, dv))
+    for _ in range(max(args.warmup, 3)):
+        run_df()
+        run_db()
+    torch.cuda.synchronize()
+    dev_ = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in dev_:
+        e[0].record()
+        run_df()
+        e[1].record()
+        run_db()
+        e[2].record()
+    torch.cuda.synchronize()
+    df_ms = sum(e[0].elapsed_time(e[1]) for e in dev_) / len(dev_)
+    db_ms = sum(e[1].elapsed_time(e[2]) for e in dev_) / len(dev_)
+    log(f"dropout fwd {df_ms:.3f} ms, bwd {db_ms:.3f} ms (p = {dp_})")
+    dnote = (f"causal B{B} H{H} N{N} d{d}, dropout p = {dp_} (mask regenerated by "
+             f"Philox-4x32-10 in every kernel)")
+    kernels["fwd_dropout"] = mfma_entry(f_fwd, df_ms, dnote)
+    kernels["bwd_dropout"] = mfma_entry(f_bwd, db_ms, dnote + "; preprocess + dK/dV + dQ")
 
     if args.cpu_heads > 0:
         log(f"oracle CPU baseline on {args.cpu_heads} head(s) ...")

@@ -19,6 +19,7 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 
 
 # Every entry point include/fa.h declares: name -> (restype, argtypes)
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_U64, _U32 = ctypes.c_uint64, ctypes.c_uint32
 SIGNATURES = {
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -30,6 +31,8 @@ SIGNATURES = {
     "fa_decode_num_splits": (_I, [_I, _I, _I, _I]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_fwd_dropout": (_I, [_P] * 5 + [_I] * 5 + [_F, _I, _F, _U64, _U32, _P]),
+    "fa_bwd_dropout": (_I, [_P] * 10 + [_Z] + [_I] * 5 + [_F, _I, _F, _U64, _U32, _P]),
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_varlen": (_I, [_P] * 12 + [_Z, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_paged_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
@@ -304,4 +307,56 @@ def bwd_varlen(q, k, v, o, lse, dout, seq_lens_q, seq_lens_k, causal: bool = Fal
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                               B, H, Nq, Nk, d, _scale(scale, d), int(bool(causal)), _stream(q))
     _check("fa_bwd_varlen", st)
+    return dq, dk, dv
+
+
+def fwd_dropout(q, k, v, p_drop: float, seed: int, offset: int = 0, causal: bool = False,
+                scale: float | None = None, out=None):
+    """Forward with dropout on P (mask regenerated from (seed, offset), never stored):
+    o = (P * Z / (1 - p_drop)) V; lse as for fwd."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _need(q, "q", (B, H, Nq, d), torch.bfloat16)
+    _need(k, "k", (B, H, Nk, d), torch.bfloat16)
+    _need(v, "v", (B, H, Nk, d), torch.bfloat16)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _need(o, "o", (B, H, Nq, d), torch.bfloat16)
+        _need(lse, "lse", (B, H, Nq), torch.float32)
+    st = load().fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               lse.data_ptr(), B, H, Nq, Nk, d, _scale(scale, d),
+                               int(bool(causal)), float(p_drop), int(seed) & (2**64 - 1),
+                               int(offset) & (2**32 - 1), _stream(q))
+    _check("fa_fwd_dropout", st)
+    return o, lse
+
+
+def bwd_dropout(q, k, v, o, lse, dout, p_drop: float, seed: int, offset: int = 0,
+                causal: bool = False, scale: float | None = None, workspace=None, out=None):
+    """Gradients (dq, dk, dv) of fwd_dropout with the same (p_drop, seed, offset)."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for t, n, shp in ((q, "q", (B, H, Nq, d)), (k, "k", (B, H, Nk, d)), (v, "v", (B, H, Nk, d)),
+                      (o, "o", (B, H, Nq, d)), (dout, "dout", (B, H, Nq, d))):
+        _need(t, n, shp, torch.bfloat16)
+    _need(lse, "lse", (B, H, Nq), torch.float32)
+    nbytes = bwd_workspace_bytes(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    st = load().fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                               dv.data_ptr(), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), B, H, Nq, Nk, d,
+                               _scale(scale, d), int(bool(causal)), float(p_drop),
+                               int(seed) & (2**64 - 1), int(offset) & (2**32 - 1), _stream(q))
+    _check("fa_bwd_dropout", st)
     return dq, dk, dv

@@ -76,7 +76,7 @@ fa_status bwd_checked(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, cons
                       fa_bf16* dv, void* workspace, size_t workspace_bytes, int B, int H,
                       int N_q, int N_k, int d, float scale, int causal, hipStream_t stream,
                       unsigned need, unsigned phases, const int32_t* lens_q = nullptr,
-                      const int32_t* lens_k = nullptr) {
+                      const int32_t* lens_k = nullptr, const fa::DropoutParams* drop = nullptr) {
   const bool varlen = lens_q != nullptr;
   const bool use_o = need & 1u, use_qkv = need & 2u, use_kv_out = need & 4u, use_q_out = need & 8u;
   if (!dout || (use_o && (!o || !lse)) || (use_qkv && (!q || !k || !v)) ||
@@ -96,6 +96,7 @@ fa_status bwd_checked(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, cons
   fa::BwdArgs a{bf(q), bf(k), bf(v), bf(o), lse, bf(dout), bf(dq), bf(dk), bf(dv),
                 static_cast<float*>(workspace), B, H, N_q, N_k, d, scale, causal != 0, stream,
                 lens_q, lens_k};
+  if (drop) a.drop = *drop;
   return from_hip(fa::launch_bwd(a, phases));
 }
 
@@ -232,6 +233,51 @@ fa_status fa_decode_paged(const fa_bf16* q, const fa_bf16* k_cache, const fa_bf1
 namespace {
 bool lens_ok(const int32_t* p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 }  // namespace
+
+namespace {
+// Dropout parameters from the drop probability: threshold t = floor((1 - p) 65536) in double
+// precision (a 16-bit draw keeps iff below t), scale 1 / (1 - p); p = 0 gives t = 65536 (no
+// dropout, the plain kernels).
+fa_status dropout_params(float p_drop, uint64_t seed, uint32_t offset, fa::DropoutParams* out) {
+  if (!(p_drop >= 0.f) || !(p_drop < 1.f)) return FA_ERR_ARG;
+  const double keep = 1.0 - (double)p_drop;
+  out->key0 = (unsigned)(seed & 0xFFFFFFFFull);
+  out->key1 = (unsigned)(seed >> 32);
+  out->offset = offset;
+  out->thresh = (unsigned)floor(keep * 65536.0);
+  out->inv_keep = (float)(1.0 / keep);
+  return FA_OK;
+}
+}  // namespace
+
+fa_status fa_fwd_dropout(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
+                         float* lse, int B, int H, int N_q, int N_k, int d, float scale,
+                         int causal, float p_drop, uint64_t seed, uint32_t offset,
+                         hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status s = check_common(B, H, N_q, N_k, d, scale, causal);
+  if (s != FA_OK) return s;
+  fa::DropoutParams dp;
+  s = dropout_params(p_drop, seed, offset, &dp);
+  if (s != FA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a{bf(q), bf(k), bf(v), bf(o), lse, B, H, N_q, N_k, d, scale, causal != 0, stream};
+  a.drop = dp;
+  return from_hip(fa::launch_fwd(a));
+}
+
+fa_status fa_bwd_dropout(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                         const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk,
+                         fa_bf16* dv, void* workspace, size_t workspace_bytes, int B, int H,
+                         int N_q, int N_k, int d, float scale, int causal, float p_drop,
+                         uint64_t seed, uint32_t offset, hipStream_t stream) {
+  fa::DropoutParams dp;
+  const fa_status s = dropout_params(p_drop, seed, offset, &dp);
+  if (s != FA_OK) return s;
+  return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N_q,
+                     N_k, d, scale, causal, stream, 15u, 7u, nullptr, nullptr, &dp);
+}
 
 fa_status fa_fwd_varlen(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
                         float* lse, const int32_t* seq_lens_q, const int32_t* seq_lens_k, int B,

@@ -173,12 +173,19 @@ struct DkdvLds {
 
 // VL: per-sequence lengths lens_q[b] <= Nq, lens_k[b] <= Nk inside the padded tensors; the
 // gradients of padding rows are zero.
-template <int D, bool CAUSAL, bool VL>
+// DROP: dropout on P, regenerated from the forward's seed and offset: dV = (P Z)^T dO / (1 - p),
+// dS = P (Z dP / (1 - p) - D).
+// MODE: kDkDv computes both; kDvOnly / kDkOnly one of them (two launches then cover the
+// gradients with fewer live registers: the dropout's generator work does not fit beside both
+// sets of accumulators at d = 128).
+constexpr int kDkDv = 0, kDvOnly = 1, kDkOnly = 2;
+template <int D, bool CAUSAL, bool VL, bool DROP, int MODE>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
     bf16* __restrict__ dK, bf16* __restrict__ dV, const int* __restrict__ lens_q,
-    const int* __restrict__ lens_k, int BH, int H, int Nq, int Nk, float c, float scale) {
+    const int* __restrict__ lens_k, int BH, int H, int Nq, int Nk, float c, float scale,
+    DropoutParams drop) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using SM = DkdvLds<D>;
   constexpr int ST = SM::ST;
@@ -186,6 +193,9 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   // of the other and need no wait before those reads
   __shared__ __attribute__((aligned(16))) unsigned char buf0[SM::kBuf];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[SM::kBuf];
+  // DROP: per-wave staging (64 bytes) that hands the keep bits from lane = query row to
+  // lane = key
+  __shared__ __attribute__((aligned(16))) unsigned char xbuf[DROP ? 4 * 64 : 16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -268,6 +278,32 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
       // keep the two 32-query blocks apart: overlapping them would double the live scores and
       // push the register allocator into copying through AGPRs
       __builtin_amdgcn_sched_barrier(0);
+      // DROP: keep bits of the 8 x 8 (query, key) blocks of this lane's key group: half h covers
+      // queries q0 + 32 qb + 16 h + 8 hi + 0..7 (byte e = query e, bit x = key 8 (l32 >> 3) + x).
+      u32x2 mbits[2];
+      if constexpr (DROP) {
+        // Lane (x = l32 & 7, group l32 >> 3, hi) draws the call of query row 16 h + 8 hi + x and
+        // key group (kw >> 3) + (l32 >> 3), turns its eight numbers into eight keep bits and
+        // stores them as byte x of the group's 8-byte block in LDS; every lane of the group then
+        // reads the whole block (its key's bits are bit x of each byte).
+        const int x = l32 & 7;
+        typedef __attribute__((address_space(3))) unsigned char lds_u8;
+        lds_u8* xb = (lds_u8*)xbuf + wave * 64 + ((l32 >> 3) * 2 + hi) * 8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 w = philox4x32_10((uint32_t)(kw >> 3) + (uint32_t)(l32 >> 3),
+                                        (uint32_t)(q0 + qb * 32 + 16 * h + 8 * hi + x),
+                                        (uint32_t)bh, drop.offset, drop.key0, drop.key1);
+          uint32_t bits = 0;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const uint32_t u = (k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu);
+            bits |= (u < drop.thresh ? 1u : 0u) << k;
+          }
+          xb[x] = (unsigned char)bits;
+          mbits[h] = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(xb);
+        }
+      }
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -299,8 +335,18 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * half + e;
           const float pv = exp2_fast(__builtin_fmaf(s[r], c, -(e < 4 ? la[e] : lb[e - 4])));
-          p[e] = pv;
-          ds[e] = pv * (dp[r] - (e < 4 ? da[e] : db4[e - 4]));
+          const float dv_row = e < 4 ? da[e] : db4[e - 4];
+          if constexpr (DROP) {
+            // bit x of byte e: 0 or all ones after the sign-extending extract
+            const uint32_t km = (uint32_t)__builtin_amdgcn_sbfe(
+                (int)mbits[half][e >> 2], 8 * (e & 3) + (l32 & 7), 1);
+            p[e] = __uint_as_float(__float_as_uint(pv) & km);
+            ds[e] = pv * __builtin_fmaf(__uint_as_float(__float_as_uint(drop.inv_keep) & km),
+                                         dp[r], -dv_row);
+          } else {
+            p[e] = pv;
+            ds[e] = pv * (dp[r] - dv_row);
+          }
         }
         pf[half] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
         dsf[half] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
@@ -339,9 +385,11 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   }
   if (t < t1) step(I0(), BF(), t);
 
+  // (in a one-gradient mode the other gradient's products are dead code and compile away)
   if (key < nk) {
-    store_row<D>(dK + ((size_t)bh * Nk + key) * D, dk, scale, hi);
-    store_row<D>(dV + ((size_t)bh * Nk + key) * D, dv, 1.f, hi);
+    if (MODE != kDvOnly) store_row<D>(dK + ((size_t)bh * Nk + key) * D, dk, scale, hi);
+    if (MODE != kDkOnly)
+      store_row<D>(dV + ((size_t)bh * Nk + key) * D, dv, DROP ? drop.inv_keep : 1.f, hi);
   } else if (VL && key < Nk) {  // padding keys
     store_zero_row<D>(dK + ((size_t)bh * Nk + key) * D, hi);
     store_zero_row<D>(dV + ((size_t)bh * Nk + key) * D, hi);
@@ -361,12 +409,12 @@ struct DqLds {
   using VTile = PaddedTile<D, VST>;
 };
 
-template <int D, bool CAUSAL, bool VL>
+template <int D, bool CAUSAL, bool VL, bool DROP>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
     bf16* __restrict__ dQ, const int* __restrict__ lens_q, const int* __restrict__ lens_k,
-    int BH, int H, int Nq, int Nk, float c, float scale) {
+    int BH, int H, int Nq, int Nk, float c, float scale, DropoutParams drop) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using SM = DqLds<D>;
   // one array per buffer: the LDS copies into one buffer then provably do not alias the reads of
@@ -476,10 +524,25 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float ds[16];
+      // DROP: registers 8 tt .. 8 tt + 7 hold keys kbase + 32 kb + 16 tt + 8 hi + 0..7, the
+      // eight keys of one generator call
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = exp2_fast(__builtin_fmaf(s[kb][r], c, -lq));
-        ds[r] = pv * (dp[kb][r] - dq_d);
+      for (int tt = 0; tt < 2; ++tt) {
+        u32x4 mw;
+        if constexpr (DROP)
+          mw = philox4x32_10((uint32_t)(kbase >> 3) + (uint32_t)(4 * kb + 2 * tt + hi),
+                             (uint32_t)qi, (uint32_t)bh, drop.offset, drop.key0, drop.key1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * tt + e;
+          const float pv = exp2_fast(__builtin_fmaf(s[kb][r], c, -lq));
+          if constexpr (DROP) {
+            const float z = keep_factor(mw[e >> 1], e & 1, drop.thresh, drop.inv_keep);
+            ds[r] = pv * __builtin_fmaf(z, dp[kb][r], -dq_d);
+          } else {
+            ds[r] = pv * (dp[kb][r] - dq_d);
+          }
+        }
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
@@ -527,7 +590,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool VL>
+template <int D, bool CAUSAL, bool VL, bool DROP>
 hipError_t launch(const BwdArgs& a, unsigned phases) {
   const int BH = a.B * a.H;
   const float c = a.scale * kLog2e;
@@ -544,18 +607,27 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
   if (phases & 2u) {
     const long long grid = (long long)BH * ((a.Nk + kBKV - 1) / kBKV);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL>), dim3((unsigned)grid), dim3(kNT), 0,
-                       a.stream, a.q, a.k, a.v, a.dout, lse2, a.delta, a.dk, a.dv, a.lens_q,
-                       a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale);
+    constexpr bool split = DROP && D == 128;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, split ? kDvOnly : kDkDv>),
+                       dim3((unsigned)grid), dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, lse2,
+                       a.delta, a.dk, a.dv, a.lens_q, a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale,
+                       a.drop);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if constexpr (split) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, kDkOnly>), dim3((unsigned)grid),
+                         dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, lse2, a.delta, a.dk,
+                         a.dv, a.lens_q, a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale, a.drop);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (phases & 4u) {
     const long long grid = (long long)BH * ((a.Nq + kBR - 1) / kBR);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VL>), dim3((unsigned)grid), dim3(kNT), 0,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VL, DROP>), dim3((unsigned)grid), dim3(kNT), 0,
                        a.stream, a.q, a.k, a.v, a.dout, lse2, a.delta, a.dq, a.lens_q, a.lens_k,
-                       BH, a.H, a.Nq, a.Nk, c, a.scale);
+                       BH, a.H, a.Nq, a.Nk, c, a.scale, a.drop);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -569,15 +641,21 @@ size_t bwd_lse2_offset(int B, int H, int Nq) {
   return (((size_t)B * H * Nq + 3) / 4) * 4;
 }
 
-template <int D, bool VL>
+template <int D, bool VL, bool DROP>
 hipError_t launch_d(const BwdArgs& a, unsigned phases) {
-  return a.causal ? launch<D, true, VL>(a, phases) : launch<D, false, VL>(a, phases);
+  return a.causal ? launch<D, true, VL, DROP>(a, phases) : launch<D, false, VL, DROP>(a, phases);
+}
+
+template <int D>
+hipError_t launch_variant(const BwdArgs& a, unsigned phases) {
+  // per-sequence lengths and dropout are separate variants (not combined)
+  if (a.drop.thresh < 65536u) return launch_d<D, false, true>(a, phases);
+  return a.lens_q != nullptr ? launch_d<D, true, false>(a, phases)
+                             : launch_d<D, false, false>(a, phases);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, unsigned phases) {
-  const bool vl = a.lens_q != nullptr;
-  if (a.d == 128) return vl ? launch_d<128, true>(a, phases) : launch_d<128, false>(a, phases);
-  return vl ? launch_d<64, true>(a, phases) : launch_d<64, false>(a, phases);
+  return a.d == 128 ? launch_variant<128>(a, phases) : launch_variant<64>(a, phases);
 }
 
 }  // namespace fa

@@ -196,8 +196,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* dst,
                                               int voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
-                                           voffset, 0, 0, 0);
+  // the LDS address is the low half of the flat address of an LDS location; going through the
+  // integer avoids the null check a pointer cast from the generic space would carry
+  typedef __attribute__((address_space(3))) void lds_void;
+  lds_void* lds = (lds_void*)(uintptr_t)(uint32_t)(uintptr_t)dst;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voffset, 0, 0, 0);
 #else
   (void)r;
   (void)dst;
@@ -207,5 +210,49 @@ __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, unsigned
 // Wait until this thread's outstanding vector-memory operations (including the LDS copies
 // above) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ---- dropout on the probabilities ------------------------------------------------------------
+// The mask is never stored: every kernel that needs it regenerates it from a counter-based
+// generator (the seed-and-offset scheme of "Maskeleme ve Dropout"). Generator: Philox-4x32-10
+// (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds over a 4-word counter; each round forms the two
+// 64-bit products of words 0 and 2 with fixed odd multipliers and outputs
+// (hi(product of word 2) ^ word 1 ^ key 0, lo(product of word 2),
+//  hi(product of word 0) ^ word 3 ^ key 1, lo(product of word 0)); the key grows by the Weyl
+// constants (golden ratio and sqrt(3) fractions) between rounds.
+// Call layout: the call with counter (j / 8, i, b*H + h, offset) decides scores (i, 8 (j/8) .. +7);
+// key j uses 16-bit half (j & 1) (low half first) of output word (j & 7) / 2; it is kept iff that
+// number is below the threshold t = floor((1 - p) 65536) < 65536.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c0 = n0;
+    c1 = (uint32_t)p1;
+    c2 = n2;
+    c3 = (uint32_t)p0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// 0xFFFF in each 16-bit half of w whose number is below t (t < 65536), 0 elsewhere: ANDed with a
+// word of two packed bf16 probabilities, it zeroes the dropped ones.
+__device__ __forceinline__ uint32_t keep_halves(uint32_t w, uint32_t t) {
+  const uint32_t lo = (w & 0xFFFFu) < t ? 0x0000FFFFu : 0u;
+  const uint32_t hi = (w >> 16) < t ? 0xFFFF0000u : 0u;
+  return lo | hi;
+}
+
+// Per-element factor of the dropout: inv_keep where the number in half `h` of w is below t,
+// else 0.
+__device__ __forceinline__ float keep_factor(uint32_t w, int h, uint32_t t, float inv_keep) {
+  const uint32_t u = h ? (w >> 16) : (w & 0xFFFFu);
+  return u < t ? inv_keep : 0.f;
+}
 
 }  // namespace fa

@@ -59,11 +59,13 @@ struct FwdLds {
 // VL: per-sequence lengths lens_q[b] <= Nq, lens_k[b] <= Nk inside the padded [B, H, N, d]
 // tensors; query rows past a sequence's length, and rows that see no key, get O = 0 and
 // LSE = -inf.
-template <int D, int NW, bool CAUSAL, bool VL>
+// DROP: dropout on P ("Maskeleme ve Dropout"): the row sums (and so the normaliser and L) use
+// every probability; the PV product sees the kept ones, and O is scaled by 1 / (1 - p).
+template <int D, int NW, bool CAUSAL, bool VL, bool DROP>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64) void fwd_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int* __restrict__ lens_q,
-    const int* __restrict__ lens_k, int BH, int H, int Nq, int Nk, float c) {
+    const int* __restrict__ lens_k, int BH, int H, int Nq, int Nk, float c, DropoutParams drop) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using L = FwdLds<D>;
   constexpr int BR = NW * 32;  // query rows per workgroup
@@ -252,6 +254,19 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     pf[2] = pack_bf16x8(sc1[0], sc1[1], sc1[2], sc1[3], sc1[4], sc1[5], sc1[6], sc1[7]);
     pf[3] = pack_bf16x8(sc1[8], sc1[9], sc1[10], sc1[11], sc1[12], sc1[13], sc1[14], sc1[15]);
     lq_run = sum_bf16x8(pf[3], sum_bf16x8(pf[2], sum_bf16x8(pf[1], sum_bf16x8(pf[0], lq_run))));
+    if constexpr (DROP) {
+      // pf[st] holds keys kbase + 16 st + 8 hi + 0..7: one generator call each
+      const uint32_t g0 = (uint32_t)(kbase >> 3) + (uint32_t)hi;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const u32x4 w = philox4x32_10(g0 + 2u * st, (uint32_t)qi, (uint32_t)bh, drop.offset,
+                                      drop.key0, drop.key1);
+        u32x4 x = as_u32x4(pf[st]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) x[m] &= keep_halves(w[m], drop.thresh);
+        pf[st] = as_bf16x8(x);
+      }
+    }
     const unsigned char* vt = P ? vb1 : vb0;
 #pragma unroll
     for (int st = 0; st < kBC / 16; ++st)
@@ -280,7 +295,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
   const float lq_tot = halves_sum(lq_run);
   if (qi < Nq) {
     const bool empty = VL && (qi >= nq || lq_tot == 0.f);  // padding, or a row that sees no key
-    const float inv = empty ? 0.f : 1.f / lq_tot;
+    const float inv = empty ? 0.f : (DROP ? drop.inv_keep : 1.f) / lq_tot;
     bf16* orow = O + ((size_t)bh * Nq + qi) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -296,30 +311,35 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
 #endif
 }
 
-template <int D, int NW, bool CAUSAL, bool VL>
+template <int D, int NW, bool CAUSAL, bool VL, bool DROP>
 hipError_t launch(const FwdArgs& a) {
   constexpr int BR = NW * 32;
   const int nqt = (a.Nq + BR - 1) / BR;
   const long long grid = (long long)a.B * a.H * nqt;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float c = a.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_kernel<D, NW, CAUSAL, VL>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     a.stream, a.q, a.k, a.v, a.o, a.lse, a.lens_q, a.lens_k, a.B * a.H, a.H,
-                     a.Nq, a.Nk, c);
+  hipLaunchKernelGGL((fwd_kernel<D, NW, CAUSAL, VL, DROP>), dim3((unsigned)grid), dim3(NW * 64),
+                     0, a.stream, a.q, a.k, a.v, a.o, a.lse, a.lens_q, a.lens_k, a.B * a.H, a.H,
+                     a.Nq, a.Nk, c, a.drop);
   return hipGetLastError();
 }
 
 }  // namespace
 
-template <int D, bool VL>
+template <int D, bool VL, bool DROP>
 hipError_t launch_d(const FwdArgs& a) {
-  return a.causal ? launch<D, 8, true, VL>(a) : launch<D, 8, false, VL>(a);
+  return a.causal ? launch<D, 8, true, VL, DROP>(a) : launch<D, 8, false, VL, DROP>(a);
+}
+
+template <int D>
+hipError_t launch_variant(const FwdArgs& a) {
+  // per-sequence lengths and dropout are separate variants (not combined)
+  if (a.drop.thresh < 65536u) return launch_d<D, false, true>(a);
+  return a.lens_q != nullptr ? launch_d<D, true, false>(a) : launch_d<D, false, false>(a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  const bool vl = a.lens_q != nullptr;
-  if (a.d == 128) return vl ? launch_d<128, true>(a) : launch_d<128, false>(a);
-  return vl ? launch_d<64, true>(a) : launch_d<64, false>(a);
+  return a.d == 128 ? launch_variant<128>(a) : launch_variant<64>(a);
 }
 
 }  // namespace fa

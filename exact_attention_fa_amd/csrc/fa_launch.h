@@ -6,6 +6,14 @@
 
 namespace fa {
 
+// Dropout on the attention probabilities (Philox-4x32-10 keyed by the 64-bit seed; the call
+// layout and the keep rule are stated beside the generator in fa_device.h). thresh = 65536
+// means no dropout.
+struct DropoutParams {
+  unsigned key0 = 0, key1 = 0, offset = 0, thresh = 65536;
+  float inv_keep = 1.f;
+};
+
 struct FwdArgs {
   const __bf16* q;
   const __bf16* k;
@@ -18,6 +26,7 @@ struct FwdArgs {
   hipStream_t stream;
   const int* lens_q = nullptr;  // per-sequence lengths (both or neither), device int32 [B]
   const int* lens_k = nullptr;
+  DropoutParams drop{};
 };
 
 struct BwdArgs {
@@ -37,6 +46,7 @@ struct BwdArgs {
   hipStream_t stream;
   const int* lens_q = nullptr;  // per-sequence lengths (both or neither), device int32 [B]
   const int* lens_k = nullptr;
+  DropoutParams drop{};
 };
 
 struct DecodeArgs {

@@ -113,6 +113,30 @@ fa_status fa_bwd_dq(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const 
                     fa_bf16* dq, void* workspace, size_t workspace_bytes, int B, int H, int N_q,
                     int N_k, int d, float scale, int causal, hipStream_t stream);
 
+/* ---- Dropout on the attention probabilities ---------------------------------------------------
+ *
+ * [MW] "Maskeleme ve Dropout": dropout acts on P; since P is never stored, neither is the mask:
+ * the kernels regenerate it from a seed and an offset, in the forward and again in the backward.
+ * Output: o = (P * Z / (1 - p_drop)) V, with P the softmax of fa_fwd and Z the keep mask; lse is
+ * that of the scores (the softmax is normalised before dropout), as fa_fwd writes it.
+ * The mask: Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with key (seed mod 2^32,
+ * seed div 2^32); the call with counter (j / 8, i, b*H + h, offset) yields eight 16-bit numbers
+ * for keys 8 (j/8) .. 8 (j/8) + 7 of query row i (key j: output word (j mod 8) / 2, low half for
+ * even j); (i, j) is kept iff its number is below t = floor((1 - p_drop) 65536) (double
+ * precision). p_drop in [0, 1) (else FA_ERR_ARG); p_drop = 0 is exactly fa_fwd / fa_bwd.
+ * Callers give each dropout layer and step its own (seed, offset) pair, and pass the forward's
+ * pair to the backward. Other arguments and errors as for fa_fwd / fa_bwd.
+ */
+fa_status fa_fwd_dropout(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
+                         float* lse, int B, int H, int N_q, int N_k, int d, float scale,
+                         int causal, float p_drop, uint64_t seed, uint32_t offset,
+                         hipStream_t stream);
+fa_status fa_bwd_dropout(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                         const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk,
+                         fa_bf16* dv, void* workspace, size_t workspace_bytes, int B, int H,
+                         int N_q, int N_k, int d, float scale, int causal, float p_drop,
+                         uint64_t seed, uint32_t offset, hipStream_t stream);
+
 /* ---- Variable-length batches ------------------------------------------------------------------
  *
  * Batches whose sequences have different lengths, kept in the padded layouts above: sequence b

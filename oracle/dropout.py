@@ -92,29 +92,39 @@ def dropout_keep(seed: int, offset: int, bh: int, n_q: int, n_k: int, p: float) 
     return u.reshape(n_q, ngroups * 8)[:, :n_k] < t
 
 
-def forward_dropout(q, k, v, scale: float, causal: bool, p: float, seed: int, offset: int):
+def _head_ids(B: int, H: int, head_ids):
+    return np.arange(B * H).reshape(B, H) if head_ids is None else np.asarray(head_ids)
+
+
+def forward_dropout(q, k, v, scale: float, causal: bool, p: float, seed: int, offset: int,
+                    head_ids=None):
     """O = (P * Z / (1 - p)) V and the (dropout-free) L per head; q [B,H,n_q,d], k/v [B,H,n_k,d].
     P and L as in oracle.attention (the textbook definition, [MW] "Attention'ın Cebiri");
-    Z = dropout_keep of the head ([MW] "Maskeleme ve Dropout")."""
+    Z = dropout_keep of the head ([MW] "Maskeleme ve Dropout"). head_ids [B, H]: the generator's
+    head index of each head (default b*H + h; a caller checking a slice of a larger batch passes
+    the slice's own indices)."""
     B, H, n_q, _ = np.shape(q)
     n_k = np.shape(k)[2]
+    ids = _head_ids(B, H, head_ids)
     o = np.empty((B, H, n_q, np.shape(v)[3]), dtype=np.float64)
     lse = np.empty((B, H, n_q), dtype=np.float64)
     for b in range(B):
         for h in range(H):
             P, lse[b, h] = A.softmax_rows(A.scores(q[b, h], k[b, h], scale, causal))
-            Z = dropout_keep(seed, offset, b * H + h, n_q, n_k, p)
+            Z = dropout_keep(seed, offset, int(ids[b, h]), n_q, n_k, p)
             o[b, h] = (P * Z / (1.0 - p)) @ np.asarray(v[b, h], dtype=np.float64)
     return o, lse
 
 
-def backward_dropout(q, k, v, do, scale: float, causal: bool, p: float, seed: int, offset: int):
+def backward_dropout(q, k, v, do, scale: float, causal: bool, p: float, seed: int, offset: int,
+                     head_ids=None):
     """Gradients of forward_dropout's O with the mask fixed, by the chain rule of [MW]
     "Geri Yayılım" through the extra elementwise factor Z / (1 - p):
     dV = Pd^T dO with Pd = P Z / (1 - p); dP = (dO V^T) Z / (1 - p);
     dS = P (dP - rowsum(P dP)); dQ = scale dS K; dK = scale dS^T Q."""
     B, H, n_q, _ = np.shape(q)
     n_k = np.shape(k)[2]
+    ids = _head_ids(B, H, head_ids)
     dq = np.empty(np.shape(q), dtype=np.float64)
     dk = np.empty(np.shape(k), dtype=np.float64)
     dv = np.empty(np.shape(v), dtype=np.float64)
@@ -123,7 +133,7 @@ def backward_dropout(q, k, v, do, scale: float, causal: bool, p: float, seed: in
             qh, kh = np.asarray(q[b, h], np.float64), np.asarray(k[b, h], np.float64)
             vh, doh = np.asarray(v[b, h], np.float64), np.asarray(do[b, h], np.float64)
             P, _ = A.softmax_rows(A.scores(qh, kh, scale, causal))
-            zs = dropout_keep(seed, offset, b * H + h, n_q, n_k, p) / (1.0 - p)
+            zs = dropout_keep(seed, offset, int(ids[b, h]), n_q, n_k, p) / (1.0 - p)
             dv[b, h] = (P * zs).T @ doh
             dP = (doh @ vh.T) * zs
             dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
