@@ -111,6 +111,28 @@ def test_varlen_validation(lib):
     assert bwd(d=32) == 3
 
 
+def test_dropout_validation(lib):
+    def fwd(p=0.1, q=FAKE, d=64, causal=0, Nq=8):
+        return lib.fa_fwd_dropout(q, FAKE, FAKE, FAKE, FAKE, 1, 2, Nq, 8, d, 0.125, causal, p,
+                                  2**64 - 1, 7, None)
+    assert fwd(p=-0.1) == 8
+    assert fwd(p=1.0) == 8
+    assert fwd(p=float("nan")) == 8
+    assert fwd(p=float("inf")) == 8
+    assert fwd(q=None) == 1
+    assert fwd(d=96) == 3
+    assert fwd(causal=1, Nq=9) == 5
+    assert fwd(q=FAKE + 4) == 4
+    ws = lib.fa_bwd_workspace_bytes(1, 2, 8, 8, 64)
+
+    def bwd(p=0.1, ws_bytes=ws, dv=FAKE):
+        return lib.fa_bwd_dropout(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dv, FAKE,
+                                  ws_bytes, 1, 2, 8, 8, 64, 0.125, 0, p, 1, 0, None)
+    assert bwd(p=1.5) == 8
+    assert bwd(dv=None) == 1
+    assert bwd(ws_bytes=ws - 16) == 6
+
+
 def test_bwd_phase_validation(lib):
     ws = lib.fa_bwd_workspace_bytes(1, 2, 64, 64, 128)
     assert ws == 2 * 2 * 64 * 4
