@@ -45,7 +45,8 @@ def log(msg: str) -> None:
 
 KERNEL_SOURCES = {"fwd": ["fa_fwd.hip", "fa_device.h"], "bwd": ["fa_bwd.hip", "fa_device.h"],
                   "decode": ["fa_decode.hip", "fa_device.h"]}
-KERNEL_FAMILY = {"fwd": "fwd", "bwd_preprocess": "bwd", "bwd_dkdv": "bwd", "bwd_dq": "bwd",
+KERNEL_FAMILY = {"fwd": "fwd", "fwd_varlen": "fwd", "fwd_dropout": "fwd",
+                 "bwd_preprocess": "bwd", "bwd_dkdv": "bwd", "bwd_dq": "bwd",
                  "decode": "decode", "decode_paged_gqa": "decode"}
 TRAFFIC_KEY = {"decode": "decode_split", "decode_paged_gqa": "decode_paged_split"}
 
@@ -336,6 +337,8 @@ def main() -> int:
     kernels["fwd_varlen"] = mfma_entry(vf_flops, vf_ms, vnote)
     kernels["bwd_varlen"] = mfma_entry(2.5 * vf_flops, vb_ms,
                                        vnote + "; preprocess + dK/dV + dQ, 2.5x the forward")
+    if "fwd_varlen" in traffic:
+        kernels["fwd_varlen"]["traffic"] = traffic["fwd_varlen"]
     del vq, vk, vv, vdo, vo, vgrads, vws
 
     # ---- dropout on P: the forward + backward workload again (timed on its own, outside the step)
@@ -362,6 +365,8 @@ def main() -> int:
              f"Philox-4x32-10 in every kernel)")
     kernels["fwd_dropout"] = mfma_entry(f_fwd, df_ms, dnote)
     kernels["bwd_dropout"] = mfma_entry(f_bwd, db_ms, dnote + "; preprocess + dK/dV + dQ")
+    if "fwd_dropout" in traffic:
+        kernels["fwd_dropout"]["traffic"] = traffic["fwd_dropout"]
 
     if args.cpu_heads > 0:
         log(f"oracle CPU baseline on {args.cpu_heads} head(s) ...")
