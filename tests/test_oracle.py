@@ -7,6 +7,7 @@ import pytest
 import oracle
 import oracle.attention as A
 import oracle.dropout as DR
+import oracle.fp8 as F8
 from tests import oracle_pins as P
 
 
@@ -262,6 +263,49 @@ def _bwd_drop_unmasked_dp(q, k, v, do, scale, causal, p, seed, offset):
     return gq, gk, dv
 
 
+_orig_e4m3_round = F8.e4m3_round
+_orig_rotate = F8.rotate_f32
+_orig_att_codes = F8.attention_from_codes
+
+
+def _e4m3_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    step = np.where(a >= 2.0 ** -6, np.exp2(e - 3), 2.0 ** -9)
+    r = np.floor(a / step + 0.5) * step
+    return np.copysign(np.where(r > 448, np.nan, r), x)
+
+
+def _rotate_unnormalised(x, signs):
+    return _orig_rotate(x, signs) * np.float32(np.sqrt(np.shape(x)[-1]))
+
+
+def _rotate_no_signs(x, signs):
+    return _orig_rotate(x, np.ones_like(np.asarray(signs)))
+
+
+def _att_codes_unshifted_p(prep, scale, causal):
+    saved = F8.P_SCALE
+    F8.P_SCALE = 1.0
+    try:
+        return _orig_att_codes(prep, scale, causal)
+    finally:
+        F8.P_SCALE = saved
+
+
+def _att_codes_quantized_normaliser(prep, scale, causal):
+    qh = F8.dequantize_rows(prep["q8"], prep["sq"], F8.Q_BLOCK_ROWS)
+    kh = F8.dequantize_rows(prep["k8"], prep["sk"], F8.K_BLOCK_ROWS)
+    vh = F8.dequantize_rows(prep["v8"], prep["sv"], None)
+    s = A.scores(qh, kh, scale, causal)
+    m = np.max(s, axis=1, keepdims=True)
+    p = np.exp(s - m)
+    ph = F8.e4m3_round(256 * p) / 256
+    return (ph @ vh) / ph.sum(axis=1, keepdims=True), (m + np.log(p.sum(axis=1, keepdims=True)))[:, 0]
+
+
 MUTANTS = {
     "paged_block_and_row_swapped": ("gather_paged", _gather_block_and_row_swapped),
     "paged_ignores_block_table": ("gather_paged", _gather_physical_order),
@@ -278,6 +322,12 @@ MUTANTS = {
     "dropout_renormalised": ("forward_dropout", _fwd_drop_renormalised, DR),
     "dropout_no_inverse_scale": ("forward_dropout", _fwd_drop_no_inverse_scale, DR),
     "dropout_bwd_unmasked_dp": ("backward_dropout", _bwd_drop_unmasked_dp, DR),
+    "fp8_ties_away_from_zero": ("e4m3_round", _e4m3_ties_away, F8),
+    "fp8_rotation_unnormalised": ("rotate_f32", _rotate_unnormalised, F8),
+    "fp8_rotation_without_signs": ("rotate_f32", _rotate_no_signs, F8),
+    "fp8_q_blocks_of_64": ("Q_BLOCK_ROWS", 64, F8),
+    "fp8_p_unshifted": ("attention_from_codes", _att_codes_unshifted_p, F8),
+    "fp8_normaliser_from_quantized_p": ("attention_from_codes", _att_codes_quantized_normaliser, F8),
     "scores_no_scale": ("scores", _scores_no_scale),
     "scores_transposed": ("scores", _scores_transposed),
     "mask_off_by_one": ("visible", _visible_off_by_one),
