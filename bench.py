@@ -12,7 +12,8 @@ The decode is reported in GB/s of K and V read. Every kernel's own rate and roof
 listed, and `roofline` repeats the entry of the step's kernel that takes the most time. Further
 entries are timed apart from the step: the paged-cache decode with grouped query heads, a
 causal forward + backward over a batch of eight sequences of different lengths (TFLOP/s of the
-valid rows and keys only), and the forward + backward workload with dropout on P.
+valid rows and keys only), the forward + backward workload with dropout on P, and the FP8
+forward with incoherent processing (against the dense fp8 peak).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -37,6 +38,7 @@ PAGED = dict(H_kv=8, block_size=16, seed=9)  # paged GQA decode: the decode work
 VARLEN = dict(B=8, H=16, N=8192, d=128, n_min=1024, causal=True, seed=21)  # variable lengths,
                                              # uniform on [n_min, N], padded to N
 DROPOUT = dict(p=0.1, seed=0x5EED, offset=0)  # dropout on P over the forward+backward workload
+FP8 = dict(incoherent=True, seed=0xF8)          # FP8 forward over the forward workload
 
 
 def log(msg: str) -> None:
@@ -367,6 +369,31 @@ def main() -> int:
     kernels["bwd_dropout"] = mfma_entry(f_bwd, db_ms, dnote + "; preprocess + dK/dV + dQ")
     if "fwd_dropout" in traffic:
         kernels["fwd_dropout"]["traffic"] = traffic["fwd_dropout"]
+
+    # ---- FP8 forward with incoherent processing (rotation + quantization + attention on the
+    # codes), the forward workload again, timed on its own
+    f8ws = torch.empty(fa.fwd_fp8_workspace_bytes(B, H, N, N, d), dtype=torch.uint8, device=dev)
+    run_f8 = lambda: fa.fwd_fp8(q, k, v, causal=causal, incoherent=FP8["incoherent"],  # noqa: E731
+                                seed=FP8["seed"], workspace=f8ws, out=(o, lse))
+    for _ in range(max(args.warmup, 3)):
+        run_f8()
+    torch.cuda.synchronize()
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a_, b_ in fev:
+        a_.record()
+        run_f8()
+        b_.record()
+    torch.cuda.synchronize()
+    f8_ms = sum(a_.elapsed_time(b_) for a_, b_ in fev) / len(fev)
+    log(f"fp8 forward {f8_ms:.3f} ms (rotation + quantization + attention)")
+    e8 = mfma_entry(f_fwd, f8_ms, f"causal B{B} H{H} N{N} d{d}: signed Hadamard rotation of Q, K, "
+                                  f"E4M3 quantization of Q, K, V and attention on the codes, "
+                                  f"against the dense fp8 peak")
+    e8["peak"] = metrics.MI355X_FP8_DENSE_TFLOPS
+    e8["frac"] = e8["achieved"] / e8["peak"]
+    kernels["fwd_fp8"] = e8
+    del f8ws
 
     if args.cpu_heads > 0:
         log(f"oracle CPU baseline on {args.cpu_heads} head(s) ...")

@@ -31,6 +31,8 @@ SIGNATURES = {
     "fa_decode_num_splits": (_I, [_I, _I, _I, _I]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_fwd_fp8_workspace_bytes": (_Z, [_I] * 5),
+    "fa_fwd_fp8": (_I, [_P] * 5 + [_I] * 5 + [_F, _I, _I, _U64, _P, _Z, _P]),
     "fa_fwd_dropout": (_I, [_P] * 5 + [_I] * 5 + [_F, _I, _F, _U64, _U32, _P]),
     "fa_bwd_dropout": (_I, [_P] * 10 + [_Z] + [_I] * 5 + [_F, _I, _F, _U64, _U32, _P]),
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -360,3 +362,55 @@ def bwd_dropout(q, k, v, o, lse, dout, p_drop: float, seed: int, offset: int = 0
                                int(seed) & (2**64 - 1), int(offset) & (2**32 - 1), _stream(q))
     _check("fa_bwd_dropout", st)
     return dq, dk, dv
+
+
+def fwd_fp8_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load().fa_fwd_fp8_workspace_bytes(B, H, Nq, Nk, d))
+
+
+def fwd_fp8(q, k, v, causal: bool = False, incoherent: bool = True, seed: int = 0,
+            scale: float | None = None, workspace=None, out=None):
+    """FP8 forward with incoherent processing: bf16 q, k, v -> (o bf16, lse fp32, workspace).
+    The workspace (uint8, device) holds the FP8 codes and scales afterwards (layout in fa.h)."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _need(q, "q", (B, H, Nq, d), torch.bfloat16)
+    _need(k, "k", (B, H, Nk, d), torch.bfloat16)
+    _need(v, "v", (B, H, Nk, d), torch.bfloat16)
+    nbytes = fwd_fp8_workspace_bytes(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _need(o, "o", (B, H, Nq, d), torch.bfloat16)
+        _need(lse, "lse", (B, H, Nq), torch.float32)
+    st = load().fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                           lse.data_ptr(), B, H, Nq, Nk, d, _scale(scale, d), int(bool(causal)),
+                           int(bool(incoherent)), int(seed) & (2**64 - 1), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), _stream(q))
+    _check("fa_fwd_fp8", st)
+    return o, lse, workspace
+
+
+def fp8_workspace_views(workspace, B: int, H: int, Nq: int, Nk: int, d: int) -> dict:
+    """Views of the FP8 codes and scales inside a workspace written by fwd_fp8 (layout of fa.h):
+    q8 [B,H,Nq,d], k8 [B,H,Nk,d], v8t [B,H,d,Nkp] uint8; sq, sk, vpart, sv fp32."""
+    import torch
+    al = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    nq32, nk64 = (Nq + 31) // 32, (Nk + 63) // 64
+    sizes = [("q8", B * H * Nq * d, (B, H, Nq, d), torch.uint8),
+             ("k8", B * H * Nk * d, (B, H, Nk, d), torch.uint8),
+             ("v8t", B * H * d * nk64 * 64, (B, H, d, nk64 * 64), torch.uint8),
+             ("sq", B * H * nq32 * 4, (B, H, nq32), torch.float32),
+             ("sk", B * H * nk64 * 4, (B, H, nk64), torch.float32),
+             ("vpart", B * H * nk64 * 4, (B, H, nk64), torch.float32),
+             ("sv", B * H * 4, (B, H), torch.float32)]
+    out, off = {}, 0
+    for name, nbytes, shape, dt in sizes:
+        out[name] = workspace[off:off + nbytes].view(dt).view(shape)
+        off += al(nbytes)
+    return out

@@ -279,6 +279,48 @@ fa_status fa_bwd_dropout(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, c
                      N_k, d, scale, causal, stream, 15u, 7u, nullptr, nullptr, &dp);
 }
 
+size_t fa_fwd_fp8_workspace_bytes(int B, int H, int N_q, int N_k, int d) {
+  if (B < 1 || H < 1 || N_q < 1 || N_k < 1 || (d != 64 && d != 128)) return 0;
+  size_t bytes = 0;
+  fa::fp8_workspace_layout(nullptr, B, H, N_q, N_k, d, &bytes);
+  return bytes;
+}
+
+fa_status fa_fwd_fp8(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
+                     float* lse, int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                     int incoherent, uint64_t seed, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status s = check_common(B, H, N_q, N_k, d, scale, causal);
+  if (s != FA_OK) return s;
+  // the transposed V codes are [B, H, d, N_k padded to 64]: keep their byte count in range
+  if ((long long)B * H * d * ((N_k + 63) / 64 * 64) >= (1LL << 31)) return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < fa_fwd_fp8_workspace_bytes(B, H, N_q, N_k, d))
+    return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  fa::Fp8Args a{};
+  a.q = bf(q);
+  a.k = bf(k);
+  a.v = bf(v);
+  a.o = bf(o);
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.Nq = N_q;
+  a.Nk = N_k;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.incoherent = incoherent != 0;
+  a.key0 = (unsigned)(seed & 0xFFFFFFFFull);
+  a.key1 = (unsigned)(seed >> 32);
+  a.ws = fa::fp8_workspace_layout(workspace, B, H, N_q, N_k, d, nullptr);
+  a.stream = stream;
+  return from_hip(fa::launch_fwd_fp8(a));
+}
+
 fa_status fa_fwd_varlen(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
                         float* lse, const int32_t* seq_lens_q, const int32_t* seq_lens_k, int B,
                         int H, int N_q, int N_k, int d, float scale, int causal,

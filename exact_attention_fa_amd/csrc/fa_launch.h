@@ -77,6 +77,36 @@ struct DecodePagedArgs {
   hipStream_t stream;
 };
 
+// FP8 forward: device buffers inside the caller's workspace (see fp8_workspace_layout)
+struct Fp8Workspace {
+  unsigned char* q8 = nullptr;   // [B, H, Nq, d] E4M3 codes of (rotated) Q
+  unsigned char* k8 = nullptr;   // [B, H, Nk, d] E4M3 codes of (rotated) K
+  unsigned char* v8t = nullptr;  // [B, H, d, Nk padded to 64] E4M3 codes of V, transposed
+  float* sq = nullptr;           // [B, H, ceil(Nq / 32)] Q block scales
+  float* sk = nullptr;           // [B, H, ceil(Nk / 64)] K block scales
+  float* vpart = nullptr;        // [B, H, ceil(Nk / 64)] max |V| per 64 keys
+  float* sv = nullptr;           // [B, H] V scale per head
+};
+
+struct Fp8Args {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float* lse;
+  int B, H, Nq, Nk, d;
+  float scale;
+  bool causal;
+  bool incoherent;
+  unsigned key0, key1;  // seed of the random signs
+  Fp8Workspace ws;
+  hipStream_t stream;
+};
+
+// Carves the FP8 buffers out of `base` (nullptr: only computes the size); *bytes = total size.
+Fp8Workspace fp8_workspace_layout(void* base, int B, int H, int Nq, int Nk, int d, size_t* bytes);
+hipError_t launch_fwd_fp8(const Fp8Args& a);
+
 hipError_t launch_fwd(const FwdArgs& a);
 // Offset (in floats) of L2 after D in the backward workspace.
 size_t bwd_lse2_offset(int B, int H, int Nq);

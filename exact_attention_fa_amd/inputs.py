@@ -121,3 +121,18 @@ def fill_padding(u16: np.ndarray, lens, pattern: int = BF16_NAN) -> np.ndarray:
     for b, n in enumerate(np.asarray(lens)):
         out[b, :, max(int(n), 0):] = pattern
     return out
+
+
+def outlier_bf16(seed: int, tensor: str, B: int, H: int, n: int, d: int, frac: float = 1e-2,
+                 mag: float = 10.0) -> np.ndarray:
+    """Synthetic outlier features as bf16 bit patterns [B, H, n, d]: N(0, 1) entries, a random
+    fraction `frac` of them plus N(0, mag^2)."""
+    out = np.empty((B, H, n, d), dtype=np.uint16)
+    for b in range(B):
+        for h in range(H):
+            g = Generator(PCG64(SeedSequence([seed, TENSOR_ID[tensor], b, h, 13])))
+            x = g.standard_normal((n, d))
+            hit = g.random((n, d)) < frac
+            x[hit] += mag * g.standard_normal(int(hit.sum()))
+            out[b, h] = bf16_round(x.astype(np.float32))
+    return out

@@ -11,6 +11,7 @@ Conventions (the attention pages' own accounting):
 from __future__ import annotations
 
 MI355X_BF16_DENSE_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 bf16 FLOP per CU-clock
+MI355X_FP8_DENSE_TFLOPS = 5033.2  # twice the bf16 rate (dense, no sparsity)
 MI355X_HBM_GBPS = 8000.0
 
 

@@ -113,6 +113,37 @@ fa_status fa_bwd_dq(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const 
                     fa_bf16* dq, void* workspace, size_t workspace_bytes, int B, int H, int N_q,
                     int N_k, int d, float scale, int causal, hipStream_t stream);
 
+/* ---- FP8 forward with incoherent processing ---------------------------------------------------
+ *
+ * Page "FlashAttention-3 (TR)", on using FP8 while reducing the quantization error: Q and K are
+ * multiplied by a random orthogonal matrix (random signs times a Hadamard matrix), which spreads
+ * outlier coordinates and leaves Q K^T unchanged, then quantized to FP8; the FlashAttention-3
+ * paragraph of "Bellek Duvarının Fiziği" adds block-wise scaling. Here:
+ *   - M = diag(sigma) H_d / sqrt(d) (H_d Sylvester-Hadamard); sigma_i = -1 iff bit i of the
+ *     Philox-4x32-10 output for counter (0, 0, 0, 0) and key (seed mod 2^32, seed div 2^32) is
+ *     set (bit i mod 32 of word i div 32). incoherent = 0 skips the rotation (plain FP8).
+ *   - FP8 = OCP E4M3 (largest finite 448). Scales: Q per 32 rows, K per 64 rows, V per head,
+ *     scale = max|x| / 448 (1 if all zero), code = E4M3(clamp(x / scale, -448, 448)), rounded to
+ *     nearest even, all in fp32 (the rotation by the fast Walsh-Hadamard butterfly, spans 1, 2,
+ *     4, ..., d/2, then times 1/sqrt(d) rounded to fp32).
+ *   - S = scale (dequantized Q)(dequantized K)^T on FP8 matrix cores; P = exp(S - m) quantized as
+ *     E4M3(2^8 P) for the P V product on FP8 matrix cores, m the running row maximum (moved
+ *     whenever a score exceeds it by more than 0.5 in log2 units); o = sum P^ V^ / sum P, bf16;
+ *     lse = ln sum exp(S) of the dequantized scores, fp32.
+ * Inputs q, k, v are bf16 as for fa_fwd (d in {64, 128}); causal needs N_q <= N_k.
+ * workspace: device, 16-byte aligned, at least fa_fwd_fp8_workspace_bytes(); after the call it
+ * holds, at 256-byte aligned offsets in this order: the E4M3 codes of Q [B,H,N_q,d] and of K
+ * [B,H,N_k,d] (after the rotation), of V transposed [B,H,d,N_kp] (N_kp = N_k rounded up to a
+ * multiple of 64, padding zero), the fp32 scales of Q [B,H,ceil(N_q/32)] and of K
+ * [B,H,ceil(N_k/64)], the per-64-key maxima of |V| [B,H,ceil(N_k/64)] and the V scales [B,H].
+ * Errors as for fa_fwd, plus FA_ERR_WORKSPACE.
+ */
+size_t fa_fwd_fp8_workspace_bytes(int B, int H, int N_q, int N_k, int d);
+fa_status fa_fwd_fp8(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
+                     float* lse, int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                     int incoherent, uint64_t seed, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
 /* ---- Dropout on the attention probabilities ---------------------------------------------------
  *
  * [MW] "Maskeleme ve Dropout": dropout acts on P; since P is never stored, neither is the mask:
