@@ -133,6 +133,25 @@ def test_dropout_validation(lib):
     assert bwd(ws_bytes=ws - 16) == 6
 
 
+def test_fp8_validation(lib):
+    ws = lib.fa_fwd_fp8_workspace_bytes(2, 3, 100, 130, 128)
+    assert ws >= 2 * 3 * (100 + 130 + 128 * 192) and ws % 256 == 0
+    assert lib.fa_fwd_fp8_workspace_bytes(2, 3, 100, 130, 96) == 0
+    assert lib.fa_fwd_fp8_workspace_bytes(0, 3, 100, 130, 64) == 0
+
+    def call(q=FAKE, ws_ptr=FAKE, ws_bytes=ws, d=128, causal=0, Nq=100, scale=0.1):
+        return lib.fa_fwd_fp8(q, FAKE, FAKE, FAKE, FAKE, 2, 3, Nq, 130, d, scale, causal, 1,
+                              2**64 - 1, ws_ptr, ws_bytes, None)
+    assert call(q=None) == 1
+    assert call(d=96) == 3
+    assert call(causal=1, Nq=131) == 5
+    assert call(scale=0.0) == 7
+    assert call(ws_ptr=None) == 6
+    assert call(ws_bytes=ws - 1) == 6
+    assert call(ws_ptr=FAKE + 8) == 4
+    assert call(q=FAKE + 2) == 4
+
+
 def test_bwd_phase_validation(lib):
     ws = lib.fa_bwd_workspace_bytes(1, 2, 64, 64, 128)
     assert ws == 2 * 2 * 64 * 4
