@@ -296,3 +296,52 @@ def backward_varlen(q, k, v, do, seq_lens_q, seq_lens_k, scale: float, causal: b
             dq[b, h, live] = scale * (ds @ ks)
             dk[b, h, :lk] = scale * (ds.T @ qs)
     return dq, dk, dv
+
+
+def forward_bias(q, k, v, bias, scale: float, causal: bool):
+    """Forward with an additive bias on the scores (notation section 0.2 of "FlashAttention'ı
+    Anlamak Bölüm 1": S = Q K^T / sqrt(d) + B, B an optional mask or bias; here the scale is a
+    caller argument): S = scale Q K^T + bias, masked entries -inf. bias broadcasts to
+    [B, H, n_q, n_k] and may hold -inf (a mask). A row with no finite score has no softmax
+    (reading as for variable lengths): o = 0, lse = -inf. Returns (o, lse) fp64."""
+    B, H, n_q, _ = np.shape(q)
+    n_k = np.shape(k)[2]
+    bias = np.broadcast_to(np.asarray(bias, dtype=np.float64), (B, H, n_q, n_k))
+    o = np.zeros((B, H, n_q, np.shape(v)[3]), dtype=np.float64)
+    lse = np.full((B, H, n_q), -np.inf, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            s = scores(q[b, h], k[b, h], scale, causal) + bias[b, h]
+            live = np.flatnonzero(np.any(np.isfinite(s), axis=1))
+            if live.size == 0:
+                continue
+            p, l_ = softmax_rows(s[live])
+            o[b, h, live] = p @ _f64(v[b, h])
+            lse[b, h, live] = l_
+    return o, lse
+
+
+def backward_bias(q, k, v, do, bias, scale: float, causal: bool):
+    """Gradients of forward_bias's o with respect to q, k, v (the bias is a constant input; no
+    gradient is formed for it), by the chain rule of [MW] "Geri Yayılım" on the rows that have a
+    softmax; rows without one contribute nothing."""
+    B, H, n_q, _ = np.shape(q)
+    n_k = np.shape(k)[2]
+    bias = np.broadcast_to(np.asarray(bias, dtype=np.float64), (B, H, n_q, n_k))
+    dq = np.zeros(np.shape(q), dtype=np.float64)
+    dk = np.zeros(np.shape(k), dtype=np.float64)
+    dv = np.zeros(np.shape(v), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh, doh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), _f64(do[b, h])
+            s = scores(qh, kh, scale, causal) + bias[b, h]
+            live = np.flatnonzero(np.any(np.isfinite(s), axis=1))
+            if live.size == 0:
+                continue
+            p, _ = softmax_rows(s[live])
+            dv[b, h] = p.T @ doh[live]
+            dp = doh[live] @ vh.T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dq[b, h, live] = scale * (ds @ kh)
+            dk[b, h] = scale * (ds.T @ qh[live])
+    return dq, dk, dv

@@ -688,6 +688,77 @@ def pin_fp8_incoherent_claim():
     assert ratio > 2.0, ratio
 
 
+
+def pin_bias_brute_force():
+    """Direct loops: s_ij = scale q_i k_j + bias_ij over the visible keys, softmax over the finite
+    ones; a row whose scores are all -inf is o = 0, lse = -inf."""
+    rng = _rng(25)
+    for n_q, n_k, d, causal in [(5, 7, 4, True), (6, 6, 8, False)]:
+        q, k, v = (rng.standard_normal((1, 2, n, d)) for n in (n_q, n_k, n_k))
+        bias = rng.standard_normal((1, 2, n_q, n_k)) * 2
+        bias[0, 1, 2, :] = -np.inf                   # a fully masked row
+        bias[0, 0, 1, ::2] = -np.inf                 # a partially masked row
+        o, lse = A.forward_bias(q, k, v, bias, 0.4, causal)
+        for h in range(2):
+            for i in range(n_q):
+                js = [j for j in range(n_k) if (not causal or j <= i + n_k - n_q)
+                      and bias[0, h, i, j] != -np.inf]
+                if not js:
+                    assert np.all(o[0, h, i] == 0) and lse[0, h, i] == -np.inf
+                    continue
+                s = [0.4 * sum(q[0, h, i, t] * k[0, h, j, t] for t in range(d)) + bias[0, h, i, j]
+                     for j in js]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                z = sum(w)
+                for t in range(d):
+                    ref = sum(w[a] * v[0, h, j, t] for a, j in enumerate(js)) / z
+                    assert abs(o[0, h, i, t] - ref) <= 1e-12 * (1 + abs(ref))
+                assert abs(lse[0, h, i] - (mx + math.log(z))) <= 1e-12 * (1 + abs(mx))
+
+
+def pin_bias_special_cases():
+    """A zero bias is the plain forward; a bias of -inf above the diagonal is the causal mask
+    (taken through the oracle's own mask path); adding a constant to a row of the bias changes
+    o and the gradients by nothing and lse by that constant; the gradients match central
+    differences."""
+    rng = _rng(26)
+    q, k, v, do = (rng.standard_normal((2, 2, 9, 4)) for _ in range(4))
+    o0, l0 = A.forward(q, k, v, 0.5, True)
+    ob, lb = A.forward_bias(q, k, v, np.zeros((9, 9)), 0.5, True)
+    assert np.allclose(o0, ob, atol=1e-14) and np.allclose(l0, lb, atol=1e-14)
+    tri = np.where(np.arange(9)[None, :] > np.arange(9)[:, None], -np.inf, 0.0)
+    om, lm = A.forward_bias(q, k, v, tri, 0.5, False)
+    assert np.allclose(o0, om, atol=1e-14) and np.allclose(l0, lm, atol=1e-14)
+    g0 = A.backward(q, k, v, do, 0.5, True)
+    gm = A.backward_bias(q, k, v, do, tri, 0.5, False)
+    assert all(np.allclose(a, b, atol=1e-13) for a, b in zip(g0, gm))
+    bias = rng.standard_normal((2, 1, 9, 9))
+    shift = rng.standard_normal((2, 1, 9, 1))
+    o1, l1 = A.forward_bias(q, k, v, bias, 0.5, False)
+    o2, l2 = A.forward_bias(q, k, v, bias + shift, 0.5, False)
+    assert np.allclose(o1, o2, atol=1e-13) and np.allclose(l2 - l1, np.broadcast_to(shift[..., 0], l1.shape), atol=1e-13)
+    ga = A.backward_bias(q, k, v, do, bias, 0.5, False)
+    gb = A.backward_bias(q, k, v, do, bias + shift, 0.5, False)
+    assert all(np.allclose(a, b, atol=1e-12) for a, b in zip(ga, gb))
+    # central differences (one head, a partially masked bias)
+    qs, ks, vs, w = (x[:1, :1, :5].copy() for x in (q, k, v, do))
+    bs = rng.standard_normal((5, 5))
+    bs[3, 1] = -np.inf
+    dq, dk, dv = A.backward_bias(qs, ks, vs, w, bs, 0.7, False)
+    h = 1e-6
+    for x, gx in ((qs, dq), (ks, dk), (vs, dv)):
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            fp = np.sum(A.forward_bias(qs, ks, vs, bs, 0.7, False)[0] * w)
+            x[idx] = old - h
+            fm = np.sum(A.forward_bias(qs, ks, vs, bs, 0.7, False)[0] * w)
+            x[idx] = old
+            fd = (fp - fm) / (2 * h)
+            assert abs(fd - gx[idx]) <= 1e-6 * (1 + abs(fd)), (idx, fd, gx[idx])
+
+
 ALL_PINS = [pin_brute_force_rows, pin_rows_sum_to_one, pin_causal_future_invariance,
             pin_finite_differences, pin_closed_forms, pin_invariances, pin_gradient_sum_rules,
             pin_torch_sdpa, pin_hand_examples, pin_decode_split_combine,
@@ -697,4 +768,5 @@ ALL_PINS = [pin_brute_force_rows, pin_rows_sum_to_one, pin_causal_future_invaria
             pin_dropout_mask_layout, pin_dropout_brute_force,
             pin_dropout_expectation_and_identities, pin_dropout_finite_differences,
             pin_e4m3_against_torch, pin_hadamard_rotation, pin_fp8_quantization,
-            pin_fp8_forward_brute_force, pin_fp8_incoherent_claim]
+            pin_fp8_forward_brute_force, pin_fp8_incoherent_claim, pin_bias_brute_force,
+            pin_bias_special_cases]

@@ -306,6 +306,24 @@ def _att_codes_quantized_normaliser(prep, scale, causal):
     return (ph @ vh) / ph.sum(axis=1, keepdims=True), (m + np.log(p.sum(axis=1, keepdims=True)))[:, 0]
 
 
+_orig_fwd_bias = A.forward_bias
+_orig_bwd_bias = A.backward_bias
+
+
+def _fwd_bias_scaled(q, k, v, bias, scale, causal):
+    # the bias multiplied by the scale as well
+    return _orig_fwd_bias(q, k, v, np.asarray(bias, dtype=np.float64) * scale, scale, causal)
+
+
+def _fwd_bias_transposed(q, k, v, bias, scale, causal):
+    b = np.asarray(bias, dtype=np.float64)
+    n_q, n_k = np.shape(q)[2], np.shape(k)[2]
+    b = np.broadcast_to(b, (np.shape(q)[0], np.shape(q)[1], n_q, n_k))
+    if n_q == n_k:
+        b = np.swapaxes(b, -1, -2)
+    return _orig_fwd_bias(q, k, v, b, scale, causal)
+
+
 MUTANTS = {
     "paged_block_and_row_swapped": ("gather_paged", _gather_block_and_row_swapped),
     "paged_ignores_block_table": ("gather_paged", _gather_physical_order),
@@ -323,6 +341,8 @@ MUTANTS = {
     "dropout_no_inverse_scale": ("forward_dropout", _fwd_drop_no_inverse_scale, DR),
     "dropout_bwd_unmasked_dp": ("backward_dropout", _bwd_drop_unmasked_dp, DR),
     "fp8_ties_away_from_zero": ("e4m3_round", _e4m3_ties_away, F8),
+    "bias_scaled_with_scores": ("forward_bias", _fwd_bias_scaled),
+    "bias_transposed": ("forward_bias", _fwd_bias_transposed),
     "fp8_rotation_unnormalised": ("rotate_f32", _rotate_unnormalised, F8),
     "fp8_rotation_without_signs": ("rotate_f32", _rotate_no_signs, F8),
     "fp8_q_blocks_of_64": ("Q_BLOCK_ROWS", 64, F8),
