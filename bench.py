@@ -12,8 +12,8 @@ The decode is reported in GB/s of K and V read. Every kernel's own rate and roof
 listed, and `roofline` repeats the entry of the step's kernel that takes the most time. Further
 entries are timed apart from the step: the paged-cache decode with grouped query heads, a
 causal forward + backward over a batch of eight sequences of different lengths (TFLOP/s of the
-valid rows and keys only), the forward + backward workload with dropout on P, and the FP8
-forward with incoherent processing (against the dense fp8 peak).
+valid rows and keys only), the forward + backward workload with dropout on P, with an additive
+bias, and the FP8 forward with incoherent processing (against the dense fp8 peak).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -39,6 +39,7 @@ VARLEN = dict(B=8, H=16, N=8192, d=128, n_min=1024, causal=True, seed=21)  # var
                                              # uniform on [n_min, N], padded to N
 DROPOUT = dict(p=0.1, seed=0x5EED, offset=0)  # dropout on P over the forward+backward workload
 FP8 = dict(incoherent=True, seed=0xF8)          # FP8 forward over the forward workload
+BIAS = dict(seed=0xB1A5)  # additive bias [1, H, N, N] (shared by the batch), 2 N(0, 1) in bf16
 
 
 def log(msg: str) -> None:
@@ -369,6 +370,32 @@ def main() -> int:
     kernels["bwd_dropout"] = mfma_entry(f_bwd, db_ms, dnote + "; preprocess + dK/dV + dQ")
     if "fwd_dropout" in traffic:
         kernels["fwd_dropout"]["traffic"] = traffic["fwd_dropout"]
+
+    # ---- additive bias [1, H, N, N] on the forward + backward workload, timed on its own
+    gen_b = torch.Generator(device=dev).manual_seed(BIAS["seed"])
+    bias_t = (2 * torch.randn((1, H, N, N), generator=gen_b, device=dev)).to(torch.bfloat16)
+    run_bf = lambda: fa.fwd_bias(q, k, v, bias_t, causal=causal, out=(o, lse))  # noqa: E731
+    run_bb = lambda: fa.bwd_bias(q, k, v, o, lse, do, bias_t, causal=causal,  # noqa: E731
+                                 workspace=ws, out=(dq, dk, dv))
+    for _ in range(max(args.warmup, 3)):
+        run_bf()
+        run_bb()
+    torch.cuda.synchronize()
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in bev:
+        e[0].record()
+        run_bf()
+        e[1].record()
+        run_bb()
+        e[2].record()
+    torch.cuda.synchronize()
+    bf_ms = sum(e[0].elapsed_time(e[1]) for e in bev) / len(bev)
+    bb_ms = sum(e[1].elapsed_time(e[2]) for e in bev) / len(bev)
+    log(f"bias fwd {bf_ms:.3f} ms, bwd {bb_ms:.3f} ms")
+    bnote = f"causal B{B} H{H} N{N} d{d} plus a bf16 bias [1, {H}, {N}, {N}] read from HBM"
+    kernels["fwd_bias"] = mfma_entry(f_fwd, bf_ms, bnote)
+    kernels["bwd_bias"] = mfma_entry(f_bwd, bb_ms, bnote + "; preprocess + dK/dV + dQ")
+    del bias_t
 
     # ---- FP8 forward with incoherent processing (rotation + quantization + attention on the
     # codes), the forward workload again, timed on its own

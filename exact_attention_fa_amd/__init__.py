@@ -1,14 +1,15 @@
 """Exact attention for MI355X (gfx950): fused forward, backward by recomputation, and split-KV
 decoding (contiguous, or over a paged KV cache with grouped query heads), also for batches of
-different-length sequences, with dropout on the probabilities, and an FP8 forward with
-incoherent processing, as hand-written HIP kernels behind a C ABI (include/fa.h).
+different-length sequences, with an additive bias or mask, with dropout on the probabilities,
+and an FP8 forward with incoherent processing, as hand-written HIP kernels behind a C ABI
+(include/fa.h).
 
     from exact_attention_fa_amd import fwd, bwd, decode, decode_paged, fwd_varlen, bwd_varlen
 """
-from ._lib import (FaError, bwd, bwd_dropout, bwd_varlen, decode, decode_num_splits,
-                   decode_paged, decode_paged_num_splits, fwd, fwd_dropout, fwd_fp8, fwd_varlen,
-                   load)
+from ._lib import (FaError, bwd, bwd_bias, bwd_dropout, bwd_varlen, decode, decode_num_splits,
+                   decode_paged, decode_paged_num_splits, fwd, fwd_bias, fwd_dropout, fwd_fp8,
+                   fwd_varlen, load)
 
-__all__ = ["FaError", "bwd", "bwd_dropout", "bwd_varlen", "decode", "decode_num_splits",
-           "decode_paged", "decode_paged_num_splits", "fwd", "fwd_dropout", "fwd_fp8",
-           "fwd_varlen", "load"]
+__all__ = ["FaError", "bwd", "bwd_bias", "bwd_dropout", "bwd_varlen", "decode",
+           "decode_num_splits", "decode_paged", "decode_paged_num_splits", "fwd", "fwd_bias",
+           "fwd_dropout", "fwd_fp8", "fwd_varlen", "load"]

@@ -19,7 +19,7 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 
 
 # Every entry point include/fa.h declares: name -> (restype, argtypes)
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-_U64, _U32 = ctypes.c_uint64, ctypes.c_uint32
+_U64, _U32, _I64 = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64
 SIGNATURES = {
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -31,6 +31,8 @@ SIGNATURES = {
     "fa_decode_num_splits": (_I, [_I, _I, _I, _I]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_fwd_bias": (_I, [_P] * 6 + [_I64] * 3 + [_I] * 5 + [_F, _I, _P]),
+    "fa_bwd_bias": (_I, [_P] * 10 + [_I64] * 3 + [_P, _Z] + [_I] * 5 + [_F, _I, _P]),
     "fa_fwd_fp8_workspace_bytes": (_Z, [_I] * 5),
     "fa_fwd_fp8": (_I, [_P] * 5 + [_I] * 5 + [_F, _I, _I, _U64, _P, _Z, _P]),
     "fa_fwd_dropout": (_I, [_P] * 5 + [_I] * 5 + [_F, _I, _F, _U64, _U32, _P]),
@@ -414,3 +416,77 @@ def fp8_workspace_views(workspace, B: int, H: int, Nq: int, Nk: int, d: int) -> 
         out[name] = workspace[off:off + nbytes].view(dt).view(shape)
         off += al(nbytes)
     return out
+
+
+def _bias_strides(bias, B: int, H: int, Nq: int, Nk: int):
+    """Element strides (b, h, q) of a bf16 bias broadcastable to [B, H, Nq, Nk] whose last
+    dimension is contiguous; size-1 (or missing) leading dimensions broadcast (stride 0)."""
+    import torch
+    if bias.dtype != torch.bfloat16:
+        raise FaError(f"bias: dtype {bias.dtype}, expected torch.bfloat16")
+    while bias.dim() < 4:
+        bias = bias.unsqueeze(0)
+    shape = tuple(bias.shape)
+    want = (B, H, Nq, Nk)
+    for i, (s_, w) in enumerate(zip(shape, want)):
+        if s_ not in (1, w) or (i == 3 and s_ != w):
+            raise FaError(f"bias: shape {shape} does not broadcast to {want}")
+    st = [0 if shape[i] == 1 else bias.stride(i) for i in range(3)]
+    if bias.stride(3) != 1 or any(x % 8 for x in st) or bias.data_ptr() % 16:
+        # the library reads 16-byte rows: re-lay the bias out with rows padded to 8 elements
+        # (a copy; callers who keep their bias in this layout pass it through unchanged)
+        nk8 = (Nk + 7) // 8 * 8
+        padded = torch.zeros(shape[:3] + (nk8,), dtype=bias.dtype, device=bias.device)
+        padded[..., :Nk] = bias
+        bias = padded[..., :Nk]
+        st = [0 if shape[i] == 1 else bias.stride(i) for i in range(3)]
+    return bias, st
+
+
+def fwd_bias(q, k, v, bias, causal: bool = False, scale: float | None = None, out=None):
+    """Forward with an additive bf16 bias on the scores (broadcastable to [B,H,Nq,Nk], -inf
+    entries mask) -> (o, lse)."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _need(q, "q", (B, H, Nq, d), torch.bfloat16)
+    _need(k, "k", (B, H, Nk, d), torch.bfloat16)
+    _need(v, "v", (B, H, Nk, d), torch.bfloat16)
+    bias, (sb, sh, sq) = _bias_strides(bias, B, H, Nq, Nk)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    st = load().fa_fwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            bias.data_ptr(), sb, sh, sq, B, H, Nq, Nk, d, _scale(scale, d),
+                            int(bool(causal)), _stream(q))
+    _check("fa_fwd_bias", st)
+    return o, lse
+
+
+def bwd_bias(q, k, v, o, lse, dout, bias, causal: bool = False, scale: float | None = None,
+             workspace=None, out=None):
+    """Gradients (dq, dk, dv) of fwd_bias (the bias is a constant)."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for t, n, shp in ((q, "q", (B, H, Nq, d)), (k, "k", (B, H, Nk, d)), (v, "v", (B, H, Nk, d)),
+                      (o, "o", (B, H, Nq, d)), (dout, "dout", (B, H, Nq, d))):
+        _need(t, n, shp, torch.bfloat16)
+    _need(lse, "lse", (B, H, Nq), torch.float32)
+    bias, (sb, sh, sq) = _bias_strides(bias, B, H, Nq, Nk)
+    nbytes = bwd_workspace_bytes(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    st = load().fa_bwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                            dv.data_ptr(), bias.data_ptr(), sb, sh, sq, workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), B, H, Nq, Nk, d,
+                            _scale(scale, d), int(bool(causal)), _stream(q))
+    _check("fa_bwd_bias", st)
+    return dq, dk, dv

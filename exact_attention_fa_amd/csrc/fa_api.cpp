@@ -76,7 +76,8 @@ fa_status bwd_checked(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, cons
                       fa_bf16* dv, void* workspace, size_t workspace_bytes, int B, int H,
                       int N_q, int N_k, int d, float scale, int causal, hipStream_t stream,
                       unsigned need, unsigned phases, const int32_t* lens_q = nullptr,
-                      const int32_t* lens_k = nullptr, const fa::DropoutParams* drop = nullptr) {
+                      const int32_t* lens_k = nullptr, const fa::DropoutParams* drop = nullptr,
+                      const fa::BiasParams* bias = nullptr) {
   const bool varlen = lens_q != nullptr;
   const bool use_o = need & 1u, use_qkv = need & 2u, use_kv_out = need & 4u, use_q_out = need & 8u;
   if (!dout || (use_o && (!o || !lse)) || (use_qkv && (!q || !k || !v)) ||
@@ -97,6 +98,7 @@ fa_status bwd_checked(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, cons
                 static_cast<float*>(workspace), B, H, N_q, N_k, d, scale, causal != 0, stream,
                 lens_q, lens_k};
   if (drop) a.drop = *drop;
+  if (bias) a.bias = *bias;
   return from_hip(fa::launch_bwd(a, phases));
 }
 
@@ -319,6 +321,53 @@ fa_status fa_fwd_fp8(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf
   a.ws = fa::fp8_workspace_layout(workspace, B, H, N_q, N_k, d, nullptr);
   a.stream = stream;
   return from_hip(fa::launch_fwd_fp8(a));
+}
+
+namespace {
+// Bias strides: non-negative multiples of 8 elements (16-byte rows), pointer 16-byte aligned, and
+// one head's extent ((N_q - 1) sq + N_k elements) within 2^30 so byte offsets stay 32-bit.
+fa_status bias_params(const fa_bf16* bias, int64_t sb, int64_t sh, int64_t sq, int N_q, int N_k,
+                      fa::BiasParams* out) {
+  if (!bias) return FA_ERR_NULL;
+  if (!aligned16(bias)) return FA_ERR_ALIGN;
+  if (sb < 0 || sh < 0 || sq < 0 || (sb % 8) || (sh % 8) || (sq % 8)) return FA_ERR_ARG;
+  if ((long double)(N_q - 1) * sq + N_k >= (long double)(1LL << 30)) return FA_ERR_SHAPE;
+  out->ptr = reinterpret_cast<const __bf16*>(bias);
+  out->sb = sb;
+  out->sh = sh;
+  out->sq = sq;
+  return FA_OK;
+}
+}  // namespace
+
+fa_status fa_fwd_bias(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
+                      float* lse, const fa_bf16* bias, int64_t bias_stride_b,
+                      int64_t bias_stride_h, int64_t bias_stride_q, int B, int H, int N_q, int N_k,
+                      int d, float scale, int causal, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status s = check_common(B, H, N_q, N_k, d, scale, causal);
+  if (s != FA_OK) return s;
+  fa::BiasParams bp;
+  s = bias_params(bias, bias_stride_b, bias_stride_h, bias_stride_q, N_q, N_k, &bp);
+  if (s != FA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a{bf(q), bf(k), bf(v), bf(o), lse, B, H, N_q, N_k, d, scale, causal != 0, stream};
+  a.bias = bp;
+  return from_hip(fa::launch_fwd(a));
+}
+
+fa_status fa_bwd_bias(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                      const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk,
+                      fa_bf16* dv, const fa_bf16* bias, int64_t bias_stride_b,
+                      int64_t bias_stride_h, int64_t bias_stride_q, void* workspace,
+                      size_t workspace_bytes, int B, int H, int N_q, int N_k, int d, float scale,
+                      int causal, hipStream_t stream) {
+  fa::BiasParams bp;
+  const fa_status s = bias_params(bias, bias_stride_b, bias_stride_h, bias_stride_q, N_q, N_k, &bp);
+  if (s != FA_OK) return s;
+  return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N_q,
+                     N_k, d, scale, causal, stream, 15u, 7u, nullptr, nullptr, nullptr, &bp);
 }
 
 fa_status fa_fwd_varlen(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,

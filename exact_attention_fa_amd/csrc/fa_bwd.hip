@@ -178,14 +178,16 @@ struct DkdvLds {
 // MODE: kDkDv computes both; kDvOnly / kDkOnly one of them (two launches then cover the
 // gradients with fewer live registers: the dropout's generator work does not fit beside both
 // sets of accumulators at d = 128).
+// BIAS: the forward's additive bias is added again when P is rebuilt (no gradient is formed for
+// the bias itself).
 constexpr int kDkDv = 0, kDvOnly = 1, kDkOnly = 2;
-template <int D, bool CAUSAL, bool VL, bool DROP, int MODE>
+template <int D, bool CAUSAL, bool VL, bool DROP, int MODE, bool BIAS>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
     bf16* __restrict__ dK, bf16* __restrict__ dV, const int* __restrict__ lens_q,
     const int* __restrict__ lens_k, int BH, int H, int Nq, int Nk, float c, float scale,
-    DropoutParams drop) {
+    DropoutParams drop, BiasParams bias) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using SM = DkdvLds<D>;
   constexpr int ST = SM::ST;
@@ -259,6 +261,25 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 
   // One query tile t from buffer P; the copies of tile t+1 go to the other buffer. MASKED: tiles
   // that cross the causal diagonal of some wave (a wave whose keys all lie past the tile skips it).
+  // BIAS: the bias of key `key` for the 16 queries of a 32-query block, packed in bf16 pairs;
+  // the lane part of the offset is formed once, the per-register row offsets are uniform
+  const auto brs = bias_rsrc(
+      bias.ptr + (long long)(bh / H) * bias.sb + (long long)(bh % H) * bias.sh, Nq, Nk, bias.sq);
+  auto load_bias = [&](int t, int qb, uint32_t (&out)[8]) {
+    const int qb0 = t * kBQ + qb * 32 + 8 * hi;
+    const int lo_off = (int)(((long long)qb0 * bias.sq + key) * 2);
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const int dr = 16 * (r >> 3) + (r & 7);  // key_of_reg(r, hi) - 8 hi
+      const int so = (int)((long long)dr * bias.sq * 2);
+      const uint32_t lo = (key < nk && qb0 + dr < nq) ? bias_ld2(brs, lo_off, so) : 0u;
+      const uint32_t hi16 =
+          (key < nk && qb0 + dr + 1 < nq) ? bias_ld2(brs, lo_off, so + (int)(bias.sq * 2)) : 0u;
+      out[r >> 1] = lo | (hi16 << 16);
+    }
+  };
+  uint32_t bwn[8];
+
   auto step = [&](auto PAR, auto MASKED, int t) {
     constexpr int P = decltype(PAR)::value;
     constexpr bool MK = decltype(MASKED)::value;
@@ -304,6 +325,22 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
           mbits[h] = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(xb);
         }
       }
+      // BIAS: the bias of this lane's key for the 16 queries of its registers, as bf16 pairs.
+      // In the unmasked loop it is prefetched one 32-query block ahead (an HBM latency is longer
+      // than one block's products); the few diagonal tiles load their own.
+      uint32_t bw[8];
+      if constexpr (BIAS) {
+        if (MK || (qb == 0 && t == tm)) {
+          load_bias(t, qb, bw);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) bw[i] = bwn[i];
+        }
+        if (!MK) {
+          if (qb == 0) load_bias(t, 1, bwn);
+          else if (t + 1 < t1) load_bias(t + 1, 0, bwn);
+        }
+      }
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -334,7 +371,12 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * half + e;
-          const float pv = exp2_fast(__builtin_fmaf(s[r], c, -(e < 4 ? la[e] : lb[e - 4])));
+          float lr = -(e < 4 ? la[e] : lb[e - 4]);
+          if constexpr (BIAS) {
+            const uint32_t w = bw[r >> 1];
+            lr = __builtin_fmaf((r & 1) ? bf16_hi(w) : bf16_lo(w), kLog2e, lr);
+          }
+          const float pv = exp2_fast(__builtin_fmaf(s[r], c, lr));
           const float dv_row = e < 4 ? da[e] : db4[e - 4];
           if constexpr (DROP) {
             // bit x of byte e: 0 or all ones after the sign-extending extract
@@ -409,12 +451,12 @@ struct DqLds {
   using VTile = PaddedTile<D, VST>;
 };
 
-template <int D, bool CAUSAL, bool VL, bool DROP>
+template <int D, bool CAUSAL, bool VL, bool DROP, bool BIAS>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
     bf16* __restrict__ dQ, const int* __restrict__ lens_q, const int* __restrict__ lens_k,
-    int BH, int H, int Nq, int Nk, float c, float scale, DropoutParams drop) {
+    int BH, int H, int Nq, int Nk, float c, float scale, DropoutParams drop, BiasParams bias) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using SM = DqLds<D>;
   // one array per buffer: the LDS copies into one buffer then provably do not alias the reads of
@@ -498,6 +540,28 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
     }
     const int kbase = t * kBC;
     if (MK && kbase > horizon) return;
+    // BIAS: keys kbase + 32 kb + 16 tt + 8 hi + 0..7 of this lane's query row, issued before the
+    // products
+    u32x4 bv[4];
+    if constexpr (BIAS) {
+      const auto brs = bias_rsrc(
+          bias.ptr + (long long)(bh / H) * bias.sb + (long long)(bh % H) * bias.sh, Nq, Nk,
+          bias.sq);
+      const int boff = (int)((long long)min(qi, Nq - 1) * bias.sq * 2);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j0 = kbase + 16 * g + 8 * hi;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (qi < nq && j0 + 8 <= nk) {
+          w = bias_ld16(brs, boff + 2 * j0);
+        } else if (qi < nq && j0 < nk) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (j0 + e < nk) w[e >> 1] |= bias_ld2(brs, boff + 2 * (j0 + e), 0) << (16 * (e & 1));
+        }
+        bv[g] = w;
+      }
+    }
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -535,7 +599,12 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * tt + e;
-          const float pv = exp2_fast(__builtin_fmaf(s[kb][r], c, -lq));
+          float lr = -lq;
+          if constexpr (BIAS) {
+            const uint32_t w = bv[2 * kb + tt][e >> 1];
+            lr = __builtin_fmaf((e & 1) ? bf16_hi(w) : bf16_lo(w), kLog2e, lr);
+          }
+          const float pv = exp2_fast(__builtin_fmaf(s[kb][r], c, lr));
           if constexpr (DROP) {
             const float z = keep_factor(mw[e >> 1], e & 1, drop.thresh, drop.inv_keep);
             ds[r] = pv * __builtin_fmaf(z, dp[kb][r], -dq_d);
@@ -590,7 +659,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool VL, bool DROP>
+template <int D, bool CAUSAL, bool VL, bool DROP, bool BIAS>
 hipError_t launch(const BwdArgs& a, unsigned phases) {
   const int BH = a.B * a.H;
   const float c = a.scale * kLog2e;
@@ -607,17 +676,18 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
   if (phases & 2u) {
     const long long grid = (long long)BH * ((a.Nk + kBKV - 1) / kBKV);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    constexpr bool split = DROP && D == 128;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, split ? kDvOnly : kDkDv>),
+    constexpr bool split = (DROP || BIAS) && D == 128;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, split ? kDvOnly : kDkDv, BIAS>),
                        dim3((unsigned)grid), dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, lse2,
                        a.delta, a.dk, a.dv, a.lens_q, a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale,
-                       a.drop);
+                       a.drop, a.bias);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (split) {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, kDkOnly>), dim3((unsigned)grid),
-                         dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, lse2, a.delta, a.dk,
-                         a.dv, a.lens_q, a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale, a.drop);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, kDkOnly, BIAS>),
+                         dim3((unsigned)grid), dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, lse2,
+                         a.delta, a.dk, a.dv, a.lens_q, a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale,
+                         a.drop, a.bias);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -625,9 +695,9 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
   if (phases & 4u) {
     const long long grid = (long long)BH * ((a.Nq + kBR - 1) / kBR);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VL, DROP>), dim3((unsigned)grid), dim3(kNT), 0,
-                       a.stream, a.q, a.k, a.v, a.dout, lse2, a.delta, a.dq, a.lens_q, a.lens_k,
-                       BH, a.H, a.Nq, a.Nk, c, a.scale, a.drop);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VL, DROP, BIAS>), dim3((unsigned)grid),
+                       dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, lse2, a.delta, a.dq, a.lens_q,
+                       a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale, a.drop, a.bias);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -641,17 +711,19 @@ size_t bwd_lse2_offset(int B, int H, int Nq) {
   return (((size_t)B * H * Nq + 3) / 4) * 4;
 }
 
-template <int D, bool VL, bool DROP>
+template <int D, bool VL, bool DROP, bool BIAS>
 hipError_t launch_d(const BwdArgs& a, unsigned phases) {
-  return a.causal ? launch<D, true, VL, DROP>(a, phases) : launch<D, false, VL, DROP>(a, phases);
+  return a.causal ? launch<D, true, VL, DROP, BIAS>(a, phases)
+                  : launch<D, false, VL, DROP, BIAS>(a, phases);
 }
 
 template <int D>
 hipError_t launch_variant(const BwdArgs& a, unsigned phases) {
-  // per-sequence lengths and dropout are separate variants (not combined)
-  if (a.drop.thresh < 65536u) return launch_d<D, false, true>(a, phases);
-  return a.lens_q != nullptr ? launch_d<D, true, false>(a, phases)
-                             : launch_d<D, false, false>(a, phases);
+  // per-sequence lengths, dropout and bias are separate variants (not combined)
+  if (a.bias.ptr != nullptr) return launch_d<D, false, false, true>(a, phases);
+  if (a.drop.thresh < 65536u) return launch_d<D, false, true, false>(a, phases);
+  return a.lens_q != nullptr ? launch_d<D, true, false, false>(a, phases)
+                             : launch_d<D, false, false, false>(a, phases);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, unsigned phases) {

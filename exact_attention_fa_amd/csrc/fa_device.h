@@ -207,6 +207,32 @@ __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, unsigned
   (void)voffset;
 #endif
 }
+// Raw buffer resource over one head's additive bias (bf16, row stride sq elements) and the
+// loads the kernels take from it: 32-bit offsets, and no fault for any offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bias_rsrc(const __bf16* base, int Nq, int Nk,
+                                                            long long sq) {
+  return make_rsrc(base, (int)(((long long)(Nq - 1) * sq + Nk) * 2));
+}
+__device__ __forceinline__ u32x4 bias_ld16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+#else
+  (void)r;
+  (void)byte_off;
+  return u32x4{0u, 0u, 0u, 0u};
+#endif
+}
+__device__ __forceinline__ uint32_t bias_ld2(__amdgpu_buffer_rsrc_t r, int byte_off, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_raw_buffer_load_b16(r, byte_off, soff, 0);
+#else
+  (void)r;
+  (void)byte_off;
+  (void)soff;
+  return 0u;
+#endif
+}
+
 // Wait until this thread's outstanding vector-memory operations (including the LDS copies
 // above) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

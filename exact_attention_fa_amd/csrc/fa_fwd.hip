@@ -61,11 +61,15 @@ struct FwdLds {
 // LSE = -inf.
 // DROP: dropout on P ("Maskeleme ve Dropout"): the row sums (and so the normaliser and L) use
 // every probability; the PV product sees the kept ones, and O is scaled by 1 / (1 - p).
-template <int D, int NW, bool CAUSAL, bool VL, bool DROP>
+// BIAS: an additive bias on the scores (S = scale Q K^T + B of the notation of "FlashAttention'ı
+// Anlamak Bölüm 1", 0.2), read from HBM one tile ahead; -inf entries mask, and a row whose scores
+// are all -inf gets O = 0 and LSE = -inf.
+template <int D, int NW, bool CAUSAL, bool VL, bool DROP, bool BIAS>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64) void fwd_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int* __restrict__ lens_q,
-    const int* __restrict__ lens_k, int BH, int H, int Nq, int Nk, float c, DropoutParams drop) {
+    const int* __restrict__ lens_k, int BH, int H, int Nq, int Nk, float c, DropoutParams drop,
+    BiasParams bias) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using L = FwdLds<D>;
   constexpr int BR = NW * 32;  // query rows per workgroup
@@ -154,6 +158,31 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     if (qi < nq) x = ld16(Qh + (size_t)qi * D + ks * 16 + hi * 8);
     qf[ks] = as_bf16x8(x);
   }
+  // rows that may end up with no finite score: padding (VL) or a bias that masks a whole row
+  constexpr bool GUARD = VL || BIAS;
+  // BIAS: this lane's bias row; lane half h needs keys kbase + 8 h + 16 g + 0..7, g = 0..3
+  // (registers 8 (g & 1) .. + 7 of sc0 for g < 2, of sc1 for g >= 2)
+  // (built in every variant; without a bias nothing reads it and it compiles away)
+  const __amdgpu_buffer_rsrc_t brs = bias_rsrc(
+      bias.ptr + (long long)(bh / H) * bias.sb + (long long)(bh % H) * bias.sh, Nq, Nk, bias.sq);
+  const int boff = (int)((long long)min(qi, Nq - 1) * bias.sq * 2);
+  auto load_bias = [&](int t, u32x4 (&bv)[4]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int j0 = t * kBC + 8 * hi + 16 * g;
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (qi < nq && j0 + 8 <= nk) {
+        w = bias_ld16(brs, boff + 2 * j0);
+      } else if (qi < nq && j0 < nk) {  // ragged end of the keys: element by element
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (j0 + e < nk) w[e >> 1] |= bias_ld2(brs, boff + 2 * (j0 + e), 0) << (16 * (e & 1));
+      }
+      bv[g] = w;
+    }
+  };
+  u32x4 bnext[4];
+  const float cs = BIAS ? 1.f : c;  // with a bias the scores are turned into log2 units first
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -198,8 +227,24 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     __syncthreads();  // ... everyone's have, and everyone is done with K[t], V[t-1]
     if (t + 2 < ntiles) copy_k(t + 2, P ? kb1 : kb0);
     if (t + 1 < ntiles) copy_v(t + 1, P ? vb0 : vb1);
+    u32x4 bcur[4];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) bcur[g] = bnext[g];
+      if (t + 1 < ntiles) load_bias(t + 1, bnext);
+    }
     if (t > last_tile) return;  // every row of this wave is masked from here on
     const int kbase = t * kBC;
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t w0 = bcur[r >> 3][(r & 7) >> 1], w1 = bcur[2 + (r >> 3)][(r & 7) >> 1];
+        const float b0 = (r & 1) ? bf16_hi(w0) : bf16_lo(w0);
+        const float b1 = (r & 1) ? bf16_hi(w1) : bf16_lo(w1);
+        sc0[r] = __builtin_fmaf(b0, kLog2e, sc0[r] * c);
+        sc1[r] = __builtin_fmaf(b1, kLog2e, sc1[r] * c);
+      }
+    }
     const bool need_mask = (kbase + kBC > nk) || (CAUSAL && kbase + kBC - 1 > qw + shift);
     if (need_mask) {
       const int lim = CAUSAL ? min(nk - 1, qi + shift) : nk - 1;
@@ -216,13 +261,13 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
       ma = fmaxf(fmaxf(ma, sc0[r]), sc0[r + 1]);
       mb = fmaxf(fmaxf(mb, sc1[r]), sc1[r + 1]);
     }
-    const float mx = halves_max(fmaxf(fmaxf(ma, sc0[15]), fmaxf(mb, sc1[15]))) * c;
+    const float mx = halves_max(fmaxf(fmaxf(ma, sc0[15]), fmaxf(mb, sc1[15]))) * cs;
     if (__any(mx > m_run + kRescaleSlack)) {
       // finite for every row that sees a key: key 0 of tile 0 is visible to all of them
       const float m_new = fmaxf(m_run, mx);
       // a row that has seen no key yet has nothing to rescale; with per-sequence lengths it may
       // still have no key here (m_new = -inf), and exp2(-inf - -inf) would be NaN
-      const float alpha = (VL && m_new == kNegInf) ? 1.f : exp2_fast(m_run - m_new);
+      const float alpha = (GUARD && m_new == kNegInf) ? 1.f : exp2_fast(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
       lq_run *= alpha;
@@ -236,11 +281,11 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     qk(sn0, sn1, P ? kb0 : kb1);
     // a row that sees no key at all (possible only with per-sequence lengths) keeps m = -inf;
     // reference it to 0 so that its probabilities are exp2(-inf) = 0, not NaN
-    const float m_use = (VL && m_run == kNegInf) ? 0.f : m_run;
+    const float m_use = (GUARD && m_run == kNegInf) ? 0.f : m_run;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      sc0[r] = exp2_fast(__builtin_fmaf(sc0[r], c, -m_use));
-      sc1[r] = exp2_fast(__builtin_fmaf(sc1[r], c, -m_use));
+      sc0[r] = exp2_fast(__builtin_fmaf(sc0[r], cs, -m_use));
+      sc1[r] = exp2_fast(__builtin_fmaf(sc1[r], cs, -m_use));
     }
     float ps[4];
 #pragma unroll
@@ -277,6 +322,8 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
   f32x16 sa0, sa1, sb0, sb1;
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
+  if constexpr (BIAS)
+    if (ntiles > 0) load_bias(0, bnext);
   copy_k(0, kb0);
   copy_v(0, vb0);
   if (ntiles > 1) copy_k(1, kb1);
@@ -294,7 +341,8 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
   const float l_tot = halves_sum(l_run);
   const float lq_tot = halves_sum(lq_run);
   if (qi < Nq) {
-    const bool empty = VL && (qi >= nq || lq_tot == 0.f);  // padding, or a row that sees no key
+    // padding, or a row that sees no key / whose scores are all -inf
+    const bool empty = GUARD && (qi >= nq || lq_tot == 0.f);
     const float inv = empty ? 0.f : (DROP ? drop.inv_keep : 1.f) / lq_tot;
     bf16* orow = O + ((size_t)bh * Nq + qi) * D;
 #pragma unroll
@@ -311,31 +359,33 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
 #endif
 }
 
-template <int D, int NW, bool CAUSAL, bool VL, bool DROP>
+template <int D, int NW, bool CAUSAL, bool VL, bool DROP, bool BIAS>
 hipError_t launch(const FwdArgs& a) {
   constexpr int BR = NW * 32;
   const int nqt = (a.Nq + BR - 1) / BR;
   const long long grid = (long long)a.B * a.H * nqt;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float c = a.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_kernel<D, NW, CAUSAL, VL, DROP>), dim3((unsigned)grid), dim3(NW * 64),
-                     0, a.stream, a.q, a.k, a.v, a.o, a.lse, a.lens_q, a.lens_k, a.B * a.H, a.H,
-                     a.Nq, a.Nk, c, a.drop);
+  hipLaunchKernelGGL((fwd_kernel<D, NW, CAUSAL, VL, DROP, BIAS>), dim3((unsigned)grid),
+                     dim3(NW * 64), 0, a.stream, a.q, a.k, a.v, a.o, a.lse, a.lens_q, a.lens_k,
+                     a.B * a.H, a.H, a.Nq, a.Nk, c, a.drop, a.bias);
   return hipGetLastError();
 }
 
 }  // namespace
 
-template <int D, bool VL, bool DROP>
+template <int D, bool VL, bool DROP, bool BIAS>
 hipError_t launch_d(const FwdArgs& a) {
-  return a.causal ? launch<D, 8, true, VL, DROP>(a) : launch<D, 8, false, VL, DROP>(a);
+  return a.causal ? launch<D, 8, true, VL, DROP, BIAS>(a) : launch<D, 8, false, VL, DROP, BIAS>(a);
 }
 
 template <int D>
 hipError_t launch_variant(const FwdArgs& a) {
-  // per-sequence lengths and dropout are separate variants (not combined)
-  if (a.drop.thresh < 65536u) return launch_d<D, false, true>(a);
-  return a.lens_q != nullptr ? launch_d<D, true, false>(a) : launch_d<D, false, false>(a);
+  // per-sequence lengths, dropout and bias are separate variants (not combined)
+  if (a.bias.ptr != nullptr) return launch_d<D, false, false, true>(a);
+  if (a.drop.thresh < 65536u) return launch_d<D, false, true, false>(a);
+  return a.lens_q != nullptr ? launch_d<D, true, false, false>(a)
+                             : launch_d<D, false, false, false>(a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {

@@ -14,6 +14,13 @@ struct DropoutParams {
   float inv_keep = 1.f;
 };
 
+// Additive bias on the scores: element (b, h, i, j) at ptr[b sb + h sh + i sq + j] (bf16; strides
+// in elements, multiples of 8; -inf masks). ptr = nullptr: no bias.
+struct BiasParams {
+  const __bf16* ptr = nullptr;
+  long long sb = 0, sh = 0, sq = 0;
+};
+
 struct FwdArgs {
   const __bf16* q;
   const __bf16* k;
@@ -27,6 +34,7 @@ struct FwdArgs {
   const int* lens_q = nullptr;  // per-sequence lengths (both or neither), device int32 [B]
   const int* lens_k = nullptr;
   DropoutParams drop{};
+  BiasParams bias{};
 };
 
 struct BwdArgs {
@@ -47,6 +55,7 @@ struct BwdArgs {
   const int* lens_q = nullptr;  // per-sequence lengths (both or neither), device int32 [B]
   const int* lens_k = nullptr;
   DropoutParams drop{};
+  BiasParams bias{};
 };
 
 struct DecodeArgs {

@@ -113,6 +113,29 @@ fa_status fa_bwd_dq(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const 
                     fa_bf16* dq, void* workspace, size_t workspace_bytes, int B, int H, int N_q,
                     int N_k, int d, float scale, int causal, hipStream_t stream);
 
+/* ---- Additive bias on the scores --------------------------------------------------------------
+ *
+ * "FlashAttention'ı Anlamak Bölüm 1", notation 0.2: S = Q K^T / sqrt(d) + B with B an optional
+ * mask or bias. Here S = scale Q K^T + bias (the bias is not multiplied by the scale), on top of
+ * the causal mask when causal != 0. bias: bf16, element (b, h, i, j) at
+ * bias[b bias_stride_b + h bias_stride_h + i bias_stride_q + j] (strides in elements, >= 0,
+ * multiples of 8; 0 broadcasts, e.g. one [N_q, N_k] bias for all batches and heads, or a
+ * per-key bias with bias_stride_q = 0); 16-byte aligned; entries finite or -inf (a mask). A row
+ * whose scores are all -inf gets o = 0, lse = -inf and zero dq. The backward treats the bias as
+ * a constant (no gradient is formed for it). Errors as for fa_fwd / fa_bwd, plus FA_ERR_ARG for
+ * negative or unaligned strides and FA_ERR_SHAPE if one head's bias spans 2^30 elements or more.
+ */
+fa_status fa_fwd_bias(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
+                      float* lse, const fa_bf16* bias, int64_t bias_stride_b,
+                      int64_t bias_stride_h, int64_t bias_stride_q, int B, int H, int N_q, int N_k,
+                      int d, float scale, int causal, hipStream_t stream);
+fa_status fa_bwd_bias(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                      const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk,
+                      fa_bf16* dv, const fa_bf16* bias, int64_t bias_stride_b,
+                      int64_t bias_stride_h, int64_t bias_stride_q, void* workspace,
+                      size_t workspace_bytes, int B, int H, int N_q, int N_k, int d, float scale,
+                      int causal, hipStream_t stream);
+
 /* ---- FP8 forward with incoherent processing ---------------------------------------------------
  *
  * Page "FlashAttention-3 (TR)", on using FP8 while reducing the quantization error: Q and K are

@@ -152,6 +152,29 @@ def test_fp8_validation(lib):
     assert call(q=FAKE + 2) == 4
 
 
+def test_bias_validation(lib):
+    def fwd(bias=FAKE, sb=0, sh=0, sq=64, q=FAKE, d=64):
+        return lib.fa_fwd_bias(q, FAKE, FAKE, FAKE, FAKE, bias, sb, sh, sq, 1, 2, 8, 8, d, 0.125,
+                               0, None)
+    assert fwd(bias=None) == 1
+    assert fwd(bias=FAKE + 8) == 4
+    assert fwd(sq=12) == 8
+    assert fwd(sh=-8) == 8
+    assert fwd(sb=4) == 8
+    assert fwd(q=None) == 1
+    assert fwd(d=80) == 3
+    assert lib.fa_fwd_bias(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 1 << 28, 1, 1, 8, 8, 64,
+                           0.125, 0, None) == 2
+    ws = lib.fa_bwd_workspace_bytes(1, 2, 8, 8, 64)
+
+    def bwd(bias=FAKE, sq=8, ws_bytes=ws):
+        return lib.fa_bwd_bias(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, bias, 0, 0, sq,
+                               FAKE, ws_bytes, 1, 2, 8, 8, 64, 0.125, 1, None)
+    assert bwd(bias=None) == 1
+    assert bwd(sq=3) == 8
+    assert bwd(ws_bytes=ws - 16) == 6
+
+
 def test_bwd_phase_validation(lib):
     ws = lib.fa_bwd_workspace_bytes(1, 2, 64, 64, 128)
     assert ws == 2 * 2 * 64 * 4
