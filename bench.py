@@ -13,7 +13,8 @@ listed, and `roofline` repeats the entry of the step's kernel that takes the mos
 entries are timed apart from the step: the paged-cache decode with grouped query heads, a
 causal forward + backward over a batch of eight sequences of different lengths (TFLOP/s of the
 valid rows and keys only), the forward + backward workload with dropout on P, with an additive
-bias, and the FP8 forward with incoherent processing (against the dense fp8 peak).
+bias, and with d_v = 64, and the FP8 forward with incoherent processing (against the dense fp8
+peak).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -396,6 +397,36 @@ def main() -> int:
     kernels["fwd_bias"] = mfma_entry(f_fwd, bf_ms, bnote)
     kernels["bwd_bias"] = mfma_entry(f_bwd, bb_ms, bnote + "; preprocess + dK/dV + dQ")
     del bias_t
+
+    # ---- V with its own head dimension: d = 128, d_v = 64 on the forward + backward workload
+    vsmall = v[..., :64].contiguous()
+    dosmall = do[..., :64].contiguous()
+    o64 = torch.empty((B, H, N, 64), dtype=torch.bfloat16, device=dev)
+    dv64 = torch.empty_like(vsmall)
+    run_vf2 = lambda: fa.fwd_dv(q, k, vsmall, causal=causal, out=(o64, lse))  # noqa: E731
+    run_vb2 = lambda: fa.bwd_dv(q, k, vsmall, o64, lse, dosmall, causal=causal,  # noqa: E731
+                                workspace=ws, out=(dq, dk, dv64))
+    for _ in range(max(args.warmup, 3)):
+        run_vf2()
+        run_vb2()
+    torch.cuda.synchronize()
+    dvev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in dvev:
+        e[0].record()
+        run_vf2()
+        e[1].record()
+        run_vb2()
+        e[2].record()
+    torch.cuda.synchronize()
+    dvf_ms = sum(e[0].elapsed_time(e[1]) for e in dvev) / len(dvev)
+    dvb_ms = sum(e[1].elapsed_time(e[2]) for e in dvev) / len(dvev)
+    log(f"d_v = 64 fwd {dvf_ms:.3f} ms, bwd {dvb_ms:.3f} ms")
+    # FLOPs: QK^T with d = 128 and PV with d_v = 64 per visible pair; backward 2.5x
+    f_dv = metrics.attention_flops(B, H, N, N, (d + 64) // 2, causal=causal)
+    dvnote = f"causal B{B} H{H} N{N}, d = {d}, d_v = 64 (2 N^2 (d + d_v) FLOPs, causal-halved)"
+    kernels["fwd_dv64"] = mfma_entry(f_dv, dvf_ms, dvnote)
+    kernels["bwd_dv64"] = mfma_entry(2.5 * f_dv, dvb_ms, dvnote + "; preprocess + dK/dV + dQ")
+    del vsmall, dosmall, o64, dv64
 
     # ---- FP8 forward with incoherent processing (rotation + quantization + attention on the
     # codes), the forward workload again, timed on its own

@@ -6,10 +6,10 @@ and an FP8 forward with incoherent processing, as hand-written HIP kernels behin
 
     from exact_attention_fa_amd import fwd, bwd, decode, decode_paged, fwd_varlen, bwd_varlen
 """
-from ._lib import (FaError, bwd, bwd_bias, bwd_dropout, bwd_varlen, decode, decode_num_splits,
-                   decode_paged, decode_paged_num_splits, fwd, fwd_bias, fwd_dropout, fwd_fp8,
-                   fwd_varlen, load)
+from ._lib import (FaError, bwd, bwd_bias, bwd_dropout, bwd_dv, bwd_varlen, decode,
+                   decode_num_splits, decode_paged, decode_paged_num_splits, fwd, fwd_bias,
+                   fwd_dropout, fwd_dv, fwd_fp8, fwd_varlen, load)
 
-__all__ = ["FaError", "bwd", "bwd_bias", "bwd_dropout", "bwd_varlen", "decode",
+__all__ = ["FaError", "bwd", "bwd_bias", "bwd_dropout", "bwd_dv", "bwd_varlen", "decode",
            "decode_num_splits", "decode_paged", "decode_paged_num_splits", "fwd", "fwd_bias",
-           "fwd_dropout", "fwd_fp8", "fwd_varlen", "load"]
+           "fwd_dropout", "fwd_dv", "fwd_fp8", "fwd_varlen", "load"]

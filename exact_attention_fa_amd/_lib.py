@@ -31,6 +31,8 @@ SIGNATURES = {
     "fa_decode_num_splits": (_I, [_I, _I, _I, _I]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_fwd_dv": (_I, [_P] * 5 + [_I] * 6 + [_F, _I, _P]),
+    "fa_bwd_dv": (_I, [_P] * 10 + [_Z] + [_I] * 6 + [_F, _I, _P]),
     "fa_fwd_bias": (_I, [_P] * 6 + [_I64] * 3 + [_I] * 5 + [_F, _I, _P]),
     "fa_bwd_bias": (_I, [_P] * 10 + [_I64] * 3 + [_P, _Z] + [_I] * 5 + [_F, _I, _P]),
     "fa_fwd_fp8_workspace_bytes": (_Z, [_I] * 5),
@@ -489,4 +491,49 @@ def bwd_bias(q, k, v, o, lse, dout, bias, causal: bool = False, scale: float | N
                             workspace.numel() * workspace.element_size(), B, H, Nq, Nk, d,
                             _scale(scale, d), int(bool(causal)), _stream(q))
     _check("fa_bwd_bias", st)
+    return dq, dk, dv
+
+
+def fwd_dv(q, k, v, causal: bool = False, scale: float | None = None, out=None):
+    """Forward with V of its own head dimension: q, k [.., d], v [B,H,Nk,d_v] -> o [.., d_v]."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk, dv_ = k.shape[2], v.shape[3]
+    _need(q, "q", (B, H, Nq, d), torch.bfloat16)
+    _need(k, "k", (B, H, Nk, d), torch.bfloat16)
+    _need(v, "v", (B, H, Nk, dv_), torch.bfloat16)
+    if out is None:
+        o = torch.empty((B, H, Nq, dv_), dtype=torch.bfloat16, device=q.device)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    st = load().fa_fwd_dv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          B, H, Nq, Nk, d, dv_, _scale(scale, d), int(bool(causal)), _stream(q))
+    _check("fa_fwd_dv", st)
+    return o, lse
+
+
+def bwd_dv(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+           workspace=None, out=None):
+    """Gradients (dq, dk, dv) of fwd_dv."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk, dv_ = k.shape[2], v.shape[3]
+    for t, n, shp in ((q, "q", (B, H, Nq, d)), (k, "k", (B, H, Nk, d)),
+                      (v, "v", (B, H, Nk, dv_)), (o, "o", (B, H, Nq, dv_)),
+                      (dout, "dout", (B, H, Nq, dv_))):
+        _need(t, n, shp, torch.bfloat16)
+    _need(lse, "lse", (B, H, Nq), torch.float32)
+    nbytes = bwd_workspace_bytes(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    st = load().fa_bwd_dv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          B, H, Nq, Nk, d, dv_, _scale(scale, d), int(bool(causal)), _stream(q))
+    _check("fa_bwd_dv", st)
     return dq, dk, dv

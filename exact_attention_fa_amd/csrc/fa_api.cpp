@@ -77,7 +77,7 @@ fa_status bwd_checked(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, cons
                       int N_q, int N_k, int d, float scale, int causal, hipStream_t stream,
                       unsigned need, unsigned phases, const int32_t* lens_q = nullptr,
                       const int32_t* lens_k = nullptr, const fa::DropoutParams* drop = nullptr,
-                      const fa::BiasParams* bias = nullptr) {
+                      const fa::BiasParams* bias = nullptr, int d_v = 0) {
   const bool varlen = lens_q != nullptr;
   const bool use_o = need & 1u, use_qkv = need & 2u, use_kv_out = need & 4u, use_q_out = need & 8u;
   if (!dout || (use_o && (!o || !lse)) || (use_qkv && (!q || !k || !v)) ||
@@ -99,6 +99,7 @@ fa_status bwd_checked(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, cons
                 lens_q, lens_k};
   if (drop) a.drop = *drop;
   if (bias) a.bias = *bias;
+  a.d_v = d_v;
   return from_hip(fa::launch_bwd(a, phases));
 }
 
@@ -368,6 +369,30 @@ fa_status fa_bwd_bias(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, cons
   if (s != FA_OK) return s;
   return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N_q,
                      N_k, d, scale, causal, stream, 15u, 7u, nullptr, nullptr, nullptr, &bp);
+}
+
+fa_status fa_fwd_dv(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+                    int B, int H, int N_q, int N_k, int d, int d_v, float scale, int causal,
+                    hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status s = check_common(B, H, N_q, N_k, d, scale, causal);
+  if (s != FA_OK) return s;
+  if (d_v != 64 && d_v != 128) return FA_ERR_HEADDIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a{bf(q), bf(k), bf(v), bf(o), lse, B, H, N_q, N_k, d, scale, causal != 0, stream};
+  a.d_v = d_v;
+  return from_hip(fa::launch_fwd(a));
+}
+
+fa_status fa_bwd_dv(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                    const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+                    void* workspace, size_t workspace_bytes, int B, int H, int N_q, int N_k, int d,
+                    int d_v, float scale, int causal, hipStream_t stream) {
+  if (d_v != 64 && d_v != 128) return FA_ERR_HEADDIM;
+  return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N_q,
+                     N_k, d, scale, causal, stream, 15u, 7u, nullptr, nullptr, nullptr, nullptr,
+                     d_v);
 }
 
 fa_status fa_fwd_varlen(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,

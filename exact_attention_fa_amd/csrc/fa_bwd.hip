@@ -162,12 +162,13 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__
 constexpr int kBKV = 128;  // keys per workgroup (32 per wave)
 constexpr int kBQ = 64;    // queries per streamed tile
 
-template <int D>
+template <int D, int DV>
 struct DkdvLds {
-  static constexpr int ST = dual_stride<D>();
-  using Tile = PaddedTile<D, ST>;
+  static constexpr int ST = dual_stride<D>(), STO = dual_stride<DV>();
+  using Tile = PaddedTile<D, ST>;     // Q
+  using TileO = PaddedTile<DV, STO>;  // dO
   // one buffer: Q tile, dO tile, L2 and D of its 64 rows
-  static constexpr int kQ = 0, kDO = Tile::kBytes, kL = 2 * Tile::kBytes, kDl = kL + kBQ * 4;
+  static constexpr int kQ = 0, kDO = Tile::kBytes, kL = kDO + TileO::kBytes, kDl = kL + kBQ * 4;
   static constexpr int kBuf = kDl + kBQ * 4;
 };
 
@@ -180,8 +181,9 @@ struct DkdvLds {
 // sets of accumulators at d = 128).
 // BIAS: the forward's additive bias is added again when P is rebuilt (no gradient is formed for
 // the bias itself).
+// DV: head dimension of V, dO and dV (the notation's d_v; the same as D unless asked otherwise).
 constexpr int kDkDv = 0, kDvOnly = 1, kDkOnly = 2;
-template <int D, bool CAUSAL, bool VL, bool DROP, int MODE, bool BIAS>
+template <int D, bool CAUSAL, bool VL, bool DROP, int MODE, bool BIAS, int DV = D>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
@@ -189,8 +191,8 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
     const int* __restrict__ lens_k, int BH, int H, int Nq, int Nk, float c, float scale,
     DropoutParams drop, BiasParams bias) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using SM = DkdvLds<D>;
-  constexpr int ST = SM::ST;
+  using SM = DkdvLds<D, DV>;
+  constexpr int ST = SM::ST, STO = SM::STO;
   // one array per buffer, so that the LDS copies into one buffer provably do not alias the reads
   // of the other and need no wait before those reads
   __shared__ __attribute__((aligned(16))) unsigned char buf0[SM::kBuf];
@@ -212,30 +214,46 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   const int shift = nk - nq;  // causal: key j visible to query i iff j <= i + shift
 
   const bf16* Qh = Q + (size_t)bh * Nq * D;
-  const bf16* dOh = dO + (size_t)bh * Nq * D;
+  const bf16* dOh = dO + (size_t)bh * Nq * DV;
   const float* Lh = L2 + (size_t)bh * Nq;
   const float* Dh = Dl + (size_t)bh * Nq;
 
   // resident B operands: K^T and V^T columns (lane = key, 8 dims per k-step)
-  bf16x8 kf[D / 16], vf[D / 16];
+  bf16x8 kf[D / 16], vf[DV / 16];
+  if constexpr (D == DV) {
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (key < nk) {
-      a = ld16(K + ((size_t)bh * Nk + key) * D + ks * 16 + hi * 8);
-      b = ld16(V + ((size_t)bh * Nk + key) * D + ks * 16 + hi * 8);
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (key < nk) {
+        a = ld16(K + ((size_t)bh * Nk + key) * D + ks * 16 + hi * 8);
+        b = ld16(V + ((size_t)bh * Nk + key) * D + ks * 16 + hi * 8);
+      }
+      kf[ks] = as_bf16x8(a);
+      vf[ks] = as_bf16x8(b);
     }
-    kf[ks] = as_bf16x8(a);
-    vf[ks] = as_bf16x8(b);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 a = {0u, 0u, 0u, 0u};
+      if (key < nk) a = ld16(K + ((size_t)bh * Nk + key) * D + ks * 16 + hi * 8);
+      kf[ks] = as_bf16x8(a);
+    }
+#pragma unroll
+    for (int ks = 0; ks < DV / 16; ++ks) {
+      u32x4 b = {0u, 0u, 0u, 0u};
+      if (key < nk) b = ld16(V + ((size_t)bh * Nk + key) * DV + ks * 16 + hi * 8);
+      vf[ks] = as_bf16x8(b);
+    }
   }
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x16 dk[D / 32], dv[DV / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[db][r] = 0.f;
-      dv[db][r] = 0.f;
-    }
+    for (int r = 0; r < 16; ++r) dk[db][r] = 0.f;
+#pragma unroll
+  for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dv[db][r] = 0.f;
 
   // query tiles that can see any key of this workgroup; the first ones (causal) cross the
   // diagonal of some wave and are masked, from tm on every query sees every key of the workgroup
@@ -245,11 +263,16 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   if (CAUSAL) tm = min(t1, max(t0, (k0 + kBKV - 1 - shift + kBQ - 1) / kBQ));
 
   typename SM::Tile tile;
+  typename SM::TileO tileo;
   tile.init(wave, lane);
+  if constexpr (D != DV) tileo.init(wave, lane);
   auto copy = [&](int t, unsigned char* b) {
     const int q0 = t * kBQ;
     tile.copy(Qh, q0, nq, b + SM::kQ, wave);
-    tile.copy(dOh, q0, nq, b + SM::kDO, wave);
+    if constexpr (D == DV)
+      tile.copy(dOh, q0, nq, b + SM::kDO, wave);
+    else
+      tileo.copy(dOh, q0, nq, b + SM::kDO, wave);
     if (wave == 0) copy_row_vec(Lh, q0, nq, b + SM::kL, lane);
     if (wave == 1) copy_row_vec(Dh, q0, nq, b + SM::kDl, lane);
   };
@@ -258,6 +281,8 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 
   const int qrow = key_of_row(l32) * ST + hi * 16;  // A operand of S and dP: row reads
   const int trb = tr_base<ST>(lane);                 // A operand of dV^T and dK^T: transposed
+  const int orow = key_of_row(l32) * STO + hi * 16;  // the same for the dO tile (DV != D)
+  const int trbo = tr_base<STO>(lane);
 
   // One query tile t from buffer P; the copies of tile t+1 go to the other buffer. MASKED: tiles
   // that cross the causal diagonal of some wave (a wave whose keys all lie past the tile skips it).
@@ -347,11 +372,20 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
         s[r] = 0.f;
         dp[r] = 0.f;
       }
+      if constexpr (D == DV) {
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const int off = qrow + qb * 32 * ST + ks * 32;
-        s = mfma32(as_bf16x8(ld16(qt + off)), kf[ks], s);
-        dp = mfma32(as_bf16x8(ld16(ot + off)), vf[ks], dp);
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const int off = qrow + qb * 32 * ST + ks * 32;
+          s = mfma32(as_bf16x8(ld16(qt + off)), kf[ks], s);
+          dp = mfma32(as_bf16x8(ld16(ot + off)), vf[ks], dp);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+          s = mfma32(as_bf16x8(ld16(qt + qrow + qb * 32 * ST + ks * 32)), kf[ks], s);
+#pragma unroll
+        for (int ks = 0; ks < DV / 16; ++ks)
+          dp = mfma32(as_bf16x8(ld16(ot + orow + qb * 32 * STO + ks * 32)), vf[ks], dp);
       }
       // queries of register r: qb*32 + key_of_reg(r, hi) = qb*32 + 16 (r >> 3) + 8 hi + (r & 7)
       if (MK) {
@@ -394,14 +428,28 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
         dsf[half] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
       }
       // dV^T += dO^T P and dK^T += Q^T dS (A operands: transposed 32-dim x 16-query blocks)
+      if constexpr (D == DV) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int off = trb + (qb * 32 + 16 * st) * ST + db * 64;
-          dv[db] = mfma32(lds_read_tr_pair(ot + off, 4 * ST), pf[st], dv[db]);
-          dk[db] = mfma32(lds_read_tr_pair(qt + off, 4 * ST), dsf[st], dk[db]);
+          for (int db = 0; db < D / 32; ++db) {
+            const int off = trb + (qb * 32 + 16 * st) * ST + db * 64;
+            dv[db] = mfma32(lds_read_tr_pair(ot + off, 4 * ST), pf[st], dv[db]);
+            dk[db] = mfma32(lds_read_tr_pair(qt + off, 4 * ST), dsf[st], dk[db]);
+          }
+      } else {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int db = 0; db < DV / 32; ++db)
+            dv[db] = mfma32(lds_read_tr_pair(ot + trbo + (qb * 32 + 16 * st) * STO + db * 64,
+                                             4 * STO), pf[st], dv[db]);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            dk[db] = mfma32(lds_read_tr_pair(qt + trb + (qb * 32 + 16 * st) * ST + db * 64,
+                                             4 * ST), dsf[st], dk[db]);
         }
+      }
     }
   };
   using I0 = std::integral_constant<int, 0>;
@@ -431,10 +479,10 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   if (key < nk) {
     if (MODE != kDvOnly) store_row<D>(dK + ((size_t)bh * Nk + key) * D, dk, scale, hi);
     if (MODE != kDkOnly)
-      store_row<D>(dV + ((size_t)bh * Nk + key) * D, dv, DROP ? drop.inv_keep : 1.f, hi);
+      store_row<DV>(dV + ((size_t)bh * Nk + key) * DV, dv, DROP ? drop.inv_keep : 1.f, hi);
   } else if (VL && key < Nk) {  // padding keys
     store_zero_row<D>(dK + ((size_t)bh * Nk + key) * D, hi);
-    store_zero_row<D>(dV + ((size_t)bh * Nk + key) * D, hi);
+    store_zero_row<DV>(dV + ((size_t)bh * Nk + key) * DV, hi);
   }
 #endif
 }
@@ -444,21 +492,21 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 constexpr int kBR = 128;  // queries per workgroup (32 per wave)
 constexpr int kBC = 64;   // keys per streamed tile
 
-template <int D>
+template <int D, int DV>
 struct DqLds {
-  static constexpr int KST = dual_stride<D>(), VST = row_stride<D>();
+  static constexpr int KST = dual_stride<D>(), VST = row_stride<DV>();
   using KTile = PaddedTile<D, KST>;
-  using VTile = PaddedTile<D, VST>;
+  using VTile = PaddedTile<DV, VST>;
 };
 
-template <int D, bool CAUSAL, bool VL, bool DROP, bool BIAS>
+template <int D, bool CAUSAL, bool VL, bool DROP, bool BIAS, int DV = D>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
     bf16* __restrict__ dQ, const int* __restrict__ lens_q, const int* __restrict__ lens_k,
     int BH, int H, int Nq, int Nk, float c, float scale, DropoutParams drop, BiasParams bias) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using SM = DqLds<D>;
+  using SM = DqLds<D, DV>;
   // one array per buffer: the LDS copies into one buffer then provably do not alias the reads of
   // the other, so no wait for the copies in flight is needed before those reads
   __shared__ __attribute__((aligned(16))) unsigned char kb0[SM::KTile::kBytes];
@@ -481,19 +529,34 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   const int shift = nk - nq;
 
   const bf16* Kh = K + (size_t)bh * Nk * D;
-  const bf16* Vh = V + (size_t)bh * Nk * D;
+  const bf16* Vh = V + (size_t)bh * Nk * DV;
 
   // resident B operands: Q^T and dO^T columns (lane = query)
-  bf16x8 qf[D / 16], dof[D / 16];
+  bf16x8 qf[D / 16], dof[DV / 16];
+  if constexpr (D == DV) {
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (qi < nq) {
-      a = ld16(Q + ((size_t)bh * Nq + qi) * D + ks * 16 + hi * 8);
-      b = ld16(dO + ((size_t)bh * Nq + qi) * D + ks * 16 + hi * 8);
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (qi < nq) {
+        a = ld16(Q + ((size_t)bh * Nq + qi) * D + ks * 16 + hi * 8);
+        b = ld16(dO + ((size_t)bh * Nq + qi) * D + ks * 16 + hi * 8);
+      }
+      qf[ks] = as_bf16x8(a);
+      dof[ks] = as_bf16x8(b);
     }
-    qf[ks] = as_bf16x8(a);
-    dof[ks] = as_bf16x8(b);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 a = {0u, 0u, 0u, 0u};
+      if (qi < nq) a = ld16(Q + ((size_t)bh * Nq + qi) * D + ks * 16 + hi * 8);
+      qf[ks] = as_bf16x8(a);
+    }
+#pragma unroll
+    for (int ks = 0; ks < DV / 16; ++ks) {
+      u32x4 b = {0u, 0u, 0u, 0u};
+      if (qi < nq) b = ld16(dO + ((size_t)bh * Nq + qi) * DV + ks * 16 + hi * 8);
+      dof[ks] = as_bf16x8(b);
+    }
   }
   const float lq = qi < nq ? L2[(size_t)bh * Nq + qi] : 0.f;
   const float dq_d = qi < nq ? Dl[(size_t)bh * Nq + qi] : 0.f;
@@ -570,13 +633,26 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
         s[kb][r] = 0.f;
         dp[kb][r] = 0.f;
       }
+    if constexpr (D == DV) {
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+      for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = mfma32(as_bf16x8(ld16(kt + kro + kb * 32 * SM::KST + ks * 32)), qf[ks], s[kb]);
-        dp[kb] = mfma32(as_bf16x8(ld16(vt + vro + kb * 32 * SM::VST + ks * 32)), dof[ks], dp[kb]);
-      }
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = mfma32(as_bf16x8(ld16(kt + kro + kb * 32 * SM::KST + ks * 32)), qf[ks], s[kb]);
+          dp[kb] = mfma32(as_bf16x8(ld16(vt + vro + kb * 32 * SM::VST + ks * 32)), dof[ks], dp[kb]);
+        }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          s[kb] = mfma32(as_bf16x8(ld16(kt + kro + kb * 32 * SM::KST + ks * 32)), qf[ks], s[kb]);
+#pragma unroll
+      for (int ks = 0; ks < DV / 16; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          dp[kb] = mfma32(as_bf16x8(ld16(vt + vro + kb * 32 * SM::VST + ks * 32)), dof[ks], dp[kb]);
+    }
     if (MK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -659,16 +735,16 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool VL, bool DROP, bool BIAS>
+template <int D, bool CAUSAL, bool VL, bool DROP, bool BIAS, int DV = D>
 hipError_t launch(const BwdArgs& a, unsigned phases) {
   const int BH = a.B * a.H;
   const float c = a.scale * kLog2e;
   const int rows = BH * a.Nq;
   float* lse2 = a.delta + bwd_lse2_offset(a.B, a.H, a.Nq);
   if (phases & 1u) {
-    constexpr int RPB = 256 / (D / 8);
+    constexpr int RPB = 256 / (DV / 8);
     const int grid = (rows + RPB * 4 - 1) / (RPB * 4);
-    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3(grid), dim3(256), 0, a.stream, a.o, a.dout,
+    hipLaunchKernelGGL((bwd_delta_kernel<DV>), dim3(grid), dim3(256), 0, a.stream, a.o, a.dout,
                        a.lse, a.delta, lse2, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -677,14 +753,14 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
     const long long grid = (long long)BH * ((a.Nk + kBKV - 1) / kBKV);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     constexpr bool split = (DROP || BIAS) && D == 128;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, split ? kDvOnly : kDkDv, BIAS>),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, split ? kDvOnly : kDkDv, BIAS, DV>),
                        dim3((unsigned)grid), dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, lse2,
                        a.delta, a.dk, a.dv, a.lens_q, a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale,
                        a.drop, a.bias);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (split) {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, kDkOnly, BIAS>),
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, kDkOnly, BIAS, DV>),
                          dim3((unsigned)grid), dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, lse2,
                          a.delta, a.dk, a.dv, a.lens_q, a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale,
                          a.drop, a.bias);
@@ -695,7 +771,7 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
   if (phases & 4u) {
     const long long grid = (long long)BH * ((a.Nq + kBR - 1) / kBR);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VL, DROP, BIAS>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VL, DROP, BIAS, DV>), dim3((unsigned)grid),
                        dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, lse2, a.delta, a.dq, a.lens_q,
                        a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale, a.drop, a.bias);
     hipError_t e = hipGetLastError();
@@ -711,10 +787,10 @@ size_t bwd_lse2_offset(int B, int H, int Nq) {
   return (((size_t)B * H * Nq + 3) / 4) * 4;
 }
 
-template <int D, bool VL, bool DROP, bool BIAS>
+template <int D, bool VL, bool DROP, bool BIAS, int DV = D>
 hipError_t launch_d(const BwdArgs& a, unsigned phases) {
-  return a.causal ? launch<D, true, VL, DROP, BIAS>(a, phases)
-                  : launch<D, false, VL, DROP, BIAS>(a, phases);
+  return a.causal ? launch<D, true, VL, DROP, BIAS, DV>(a, phases)
+                  : launch<D, false, VL, DROP, BIAS, DV>(a, phases);
 }
 
 template <int D>
@@ -727,6 +803,10 @@ hipError_t launch_variant(const BwdArgs& a, unsigned phases) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a, unsigned phases) {
+  const int dv = a.d_v ? a.d_v : a.d;
+  if (dv != a.d)  // a V head dimension of its own: the plain variant only
+    return a.d == 128 ? launch_d<128, false, false, false, 64>(a, phases)
+                      : launch_d<64, false, false, false, 128>(a, phases);
   return a.d == 128 ? launch_variant<128>(a, phases) : launch_variant<64>(a, phases);
 }
 

@@ -46,10 +46,10 @@ namespace {
 constexpr int kBC = 64;               // keys per tile
 constexpr float kRescaleSlack = 8.f;  // log2 units
 
-template <int D>
+template <int D, int DV>
 struct FwdLds {
   static constexpr int KST = 2 * D + 16;                        // K row stride (bytes)
-  static constexpr int VST = 2 * D + (D == 128 ? 32 : 16);      // V row stride (bytes)
+  static constexpr int VST = 2 * DV + (DV == 128 ? 32 : 16);    // V row stride (bytes)
   static constexpr int KCPR = KST / 16, VCPR = VST / 16;        // 16-byte chunks per row
   static constexpr int KT = kBC * KST, VT = kBC * VST;          // tile bytes
   static constexpr int KI = kBC * KCPR / 64, VI = kBC * VCPR / 64;  // wave-wide copies per tile
@@ -64,14 +64,15 @@ struct FwdLds {
 // BIAS: an additive bias on the scores (S = scale Q K^T + B of the notation of "FlashAttention'ı
 // Anlamak Bölüm 1", 0.2), read from HBM one tile ahead; -inf entries mask, and a row whose scores
 // are all -inf gets O = 0 and LSE = -inf.
-template <int D, int NW, bool CAUSAL, bool VL, bool DROP, bool BIAS>
+// DV: head dimension of V and O (the notation's d_v; the same as D unless asked otherwise).
+template <int D, int DV, int NW, bool CAUSAL, bool VL, bool DROP, bool BIAS>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64) void fwd_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int* __restrict__ lens_q,
     const int* __restrict__ lens_k, int BH, int H, int Nq, int Nk, float c, DropoutParams drop,
     BiasParams bias) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using L = FwdLds<D>;
+  using L = FwdLds<D, DV>;
   constexpr int BR = NW * 32;  // query rows per workgroup
   constexpr int KIW = (L::KI + NW - 1) / NW, VIW = (L::VI + NW - 1) / NW;
   // one array per buffer: the LDS copies into one buffer then provably do not alias the reads of
@@ -110,7 +111,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
 
   const bf16* Qh = Q + (size_t)bh * Nq * D;
   const bf16* Kh = K + (size_t)bh * Nk * D;
-  const bf16* Vh = V + (size_t)bh * Nk * D;
+  const bf16* Vh = V + (size_t)bh * Nk * DV;
 
   int kend = nk;
   if (CAUSAL) kend = min(nk, min(q0 + BR, nq) + shift);
@@ -131,20 +132,20 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
 #pragma unroll
   for (int i = 0; i < VIW; ++i) {
     const int p = (wave + i * NW) * 64 + lane, row = p / L::VCPR, ch = p % L::VCPR;
-    voff[i] = row * D * 2 + (ch < D / 8 ? ch : 0) * 16;
+    voff[i] = row * DV * 2 + (ch < DV / 8 ? ch : 0) * 16;
   }
-  auto tile_rsrc = [&](const bf16* base, int t) {
+  auto tile_rsrc = [&](const bf16* base, int t, int w) {  // w: row width (elements)
     const int rows = max(0, nk - t * kBC);  // reads at or past the key length return zero
-    return make_rsrc(base + (size_t)t * kBC * D, rows * D * 2);
+    return make_rsrc(base + (size_t)t * kBC * w, rows * w * 2);
   };
   auto copy_k = [&](int t, unsigned char* dst) {
-    const auto r = tile_rsrc(Kh, t);
+    const auto r = tile_rsrc(Kh, t, D);
 #pragma unroll
     for (int i = 0; i < KIW; ++i)
       if (wave + i * NW < L::KI) buffer_to_lds(r, dst + (wave + i * NW) * 1024, koff[i]);
   };
   auto copy_v = [&](int t, unsigned char* dst) {
-    const auto r = tile_rsrc(Vh, t);
+    const auto r = tile_rsrc(Vh, t, DV);
 #pragma unroll
     for (int i = 0; i < VIW; ++i)
       if (wave + i * NW < L::VI) buffer_to_lds(r, dst + (wave + i * NW) * 1024, voff[i]);
@@ -183,9 +184,9 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
   };
   u32x4 bnext[4];
   const float cs = BIAS ? 1.f : c;  // with a bias the scores are turned into log2 units first
-  f32x16 oacc[D / 32];
+  f32x16 oacc[DV / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   // m in log2 units of the scaled scores; l: fp32 row sum; lq: sum of the bf16-rounded P
@@ -272,7 +273,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
       l_run *= alpha;
       lq_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
@@ -316,7 +317,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
 #pragma unroll
     for (int st = 0; st < kBC / 16; ++st)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32(vt_frag(vt, st, db), pf[st], oacc[db]);
+      for (int db = 0; db < DV / 32; ++db) oacc[db] = mfma32(vt_frag(vt, st, db), pf[st], oacc[db]);
   };
 
   f32x16 sa0, sa1, sb0, sb1;
@@ -344,9 +345,9 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     // padding, or a row that sees no key / whose scores are all -inf
     const bool empty = GUARD && (qi >= nq || lq_tot == 0.f);
     const float inv = empty ? 0.f : (DROP ? drop.inv_keep : 1.f) / lq_tot;
-    bf16* orow = O + ((size_t)bh * Nq + qi) * D;
+    bf16* orow = O + ((size_t)bh * Nq + qi) * DV;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         u32x2 w;
@@ -359,14 +360,14 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
 #endif
 }
 
-template <int D, int NW, bool CAUSAL, bool VL, bool DROP, bool BIAS>
+template <int D, int DV, int NW, bool CAUSAL, bool VL, bool DROP, bool BIAS>
 hipError_t launch(const FwdArgs& a) {
   constexpr int BR = NW * 32;
   const int nqt = (a.Nq + BR - 1) / BR;
   const long long grid = (long long)a.B * a.H * nqt;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float c = a.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_kernel<D, NW, CAUSAL, VL, DROP, BIAS>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((fwd_kernel<D, DV, NW, CAUSAL, VL, DROP, BIAS>), dim3((unsigned)grid),
                      dim3(NW * 64), 0, a.stream, a.q, a.k, a.v, a.o, a.lse, a.lens_q, a.lens_k,
                      a.B * a.H, a.H, a.Nq, a.Nk, c, a.drop, a.bias);
   return hipGetLastError();
@@ -374,9 +375,10 @@ hipError_t launch(const FwdArgs& a) {
 
 }  // namespace
 
-template <int D, bool VL, bool DROP, bool BIAS>
+template <int D, bool VL, bool DROP, bool BIAS, int DV = D>
 hipError_t launch_d(const FwdArgs& a) {
-  return a.causal ? launch<D, 8, true, VL, DROP, BIAS>(a) : launch<D, 8, false, VL, DROP, BIAS>(a);
+  return a.causal ? launch<D, DV, 8, true, VL, DROP, BIAS>(a)
+                  : launch<D, DV, 8, false, VL, DROP, BIAS>(a);
 }
 
 template <int D>
@@ -389,6 +391,10 @@ hipError_t launch_variant(const FwdArgs& a) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
+  const int dv = a.d_v ? a.d_v : a.d;
+  if (dv != a.d)  // a V head dimension of its own: the plain variant only
+    return a.d == 128 ? launch_d<128, false, false, false, 64>(a)
+                      : launch_d<64, false, false, false, 128>(a);
   return a.d == 128 ? launch_variant<128>(a) : launch_variant<64>(a);
 }
 

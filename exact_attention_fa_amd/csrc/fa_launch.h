@@ -35,6 +35,7 @@ struct FwdArgs {
   const int* lens_k = nullptr;
   DropoutParams drop{};
   BiasParams bias{};
+  int d_v = 0;  // head dimension of V and O; 0: the same as d
 };
 
 struct BwdArgs {
@@ -56,6 +57,7 @@ struct BwdArgs {
   const int* lens_k = nullptr;
   DropoutParams drop{};
   BiasParams bias{};
+  int d_v = 0;  // head dimension of V, O, dO and dV; 0: the same as d
 };
 
 struct DecodeArgs {

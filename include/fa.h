@@ -113,6 +113,21 @@ fa_status fa_bwd_dq(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const 
                     fa_bf16* dq, void* workspace, size_t workspace_bytes, int B, int H, int N_q,
                     int N_k, int d, float scale, int causal, hipStream_t stream);
 
+/* ---- V with its own head dimension -------------------------------------------------------------
+ *
+ * "FlashAttention'ı Anlamak Bölüm 1", notation 0.2: V in R^{N_k x d_v}, so O in R^{N_q x d_v},
+ * while Q, K have d columns. Layouts as for fa_fwd / fa_bwd with d_v columns for v, o, dout and
+ * dv: v, dv [B,H,N_k,d_v], o, dout [B,H,N_q,d_v]. d, d_v in {64, 128} (else FA_ERR_HEADDIM);
+ * d_v = d is the same as fa_fwd / fa_bwd. The backward's workspace is fa_bwd_workspace_bytes.
+ */
+fa_status fa_fwd_dv(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+                    int B, int H, int N_q, int N_k, int d, int d_v, float scale, int causal,
+                    hipStream_t stream);
+fa_status fa_bwd_dv(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                    const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+                    void* workspace, size_t workspace_bytes, int B, int H, int N_q, int N_k, int d,
+                    int d_v, float scale, int causal, hipStream_t stream);
+
 /* ---- Additive bias on the scores --------------------------------------------------------------
  *
  * "FlashAttention'ı Anlamak Bölüm 1", notation 0.2: S = Q K^T / sqrt(d) + B with B an optional

@@ -192,10 +192,13 @@ def pin_torch_sdpa():
     torch.logsumexp of the masked scores."""
     import torch
     rng = _rng(8)
-    for n_q, n_k, d in [(7, 7, 8), (5, 12, 16), (33, 33, 8)]:
+    # the last two cases give V its own head dimension d_v (the notation's V in R^{N_k x d_v})
+    for n_q, n_k, d, d_v in [(7, 7, 8, 8), (5, 12, 16, 16), (33, 33, 8, 8), (9, 11, 8, 16),
+                             (6, 6, 16, 4)]:
         for causal in (False, True):
-            q, k, v = _head(rng, n_q, n_k, d)
-            do = rng.standard_normal((n_q, d))
+            q, k, _ = _head(rng, n_q, n_k, d)
+            v = rng.standard_normal((n_k, d_v))
+            do = rng.standard_normal((n_q, d_v))
             scale = 1.0 / math.sqrt(d)
             tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
             mask = torch.tensor(np.tril(np.ones((n_q, n_k), dtype=bool), k=n_k - n_q)) if causal else None

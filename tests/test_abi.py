@@ -175,6 +175,20 @@ def test_bias_validation(lib):
     assert bwd(ws_bytes=ws - 16) == 6
 
 
+def test_dv_validation(lib):
+    def fwd(dv_=64, d=128, q=FAKE):
+        return lib.fa_fwd_dv(q, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 8, d, dv_, 0.125, 0, None)
+    assert fwd(dv_=96) == 3
+    assert fwd(d=80) == 3
+    assert fwd(q=None) == 1
+    assert fwd(q=FAKE + 4) == 4
+    ws = lib.fa_bwd_workspace_bytes(1, 2, 8, 8, 128)
+    assert lib.fa_bwd_dv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 1, 2, 8,
+                         8, 128, 32, 0.125, 0, None) == 3
+    assert lib.fa_bwd_dv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 16, 1,
+                         2, 8, 8, 128, 64, 0.125, 0, None) == 6
+
+
 def test_bwd_phase_validation(lib):
     ws = lib.fa_bwd_workspace_bytes(1, 2, 64, 64, 128)
     assert ws == 2 * 2 * 64 * 4
