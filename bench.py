@@ -49,10 +49,12 @@ def log(msg: str) -> None:
 
 KERNEL_SOURCES = {"fwd": ["fa_fwd.hip", "fa_device.h"], "bwd": ["fa_bwd.hip", "fa_device.h"],
                   "decode": ["fa_decode.hip", "fa_device.h"]}
-KERNEL_FAMILY = {"fwd": "fwd", "fwd_varlen": "fwd", "fwd_dropout": "fwd",
+KERNEL_FAMILY = {"fwd": "fwd", "fwd_varlen": "fwd", "fwd_dropout": "fwd", "fwd_bias": "fwd",
+                 "fwd_dv64": "fwd",
                  "bwd_preprocess": "bwd", "bwd_dkdv": "bwd", "bwd_dq": "bwd",
                  "decode": "decode", "decode_paged_gqa": "decode"}
-TRAFFIC_KEY = {"decode": "decode_split", "decode_paged_gqa": "decode_paged_split"}
+TRAFFIC_KEY = {"decode": "decode_split", "decode_paged_gqa": "decode_paged_split",
+               "fwd_dv64": "fwd_dv"}
 
 
 def measured_traffic() -> dict:
@@ -302,8 +304,6 @@ def main() -> int:
                        f"read once for {DH} query heads; q, o, lse, block table; timed apart "
                        f"from the step")
     kernels["decode_paged_gqa"]["splits"] = psplits
-    if "decode_paged_gqa" in traffic:
-        kernels["decode_paged_gqa"]["traffic"] = traffic["decode_paged_gqa"]
     del kcache, vcache
 
     # ---- variable-length batch: causal forward + backward (timed on its own, outside the step)
@@ -341,8 +341,6 @@ def main() -> int:
     kernels["fwd_varlen"] = mfma_entry(vf_flops, vf_ms, vnote)
     kernels["bwd_varlen"] = mfma_entry(2.5 * vf_flops, vb_ms,
                                        vnote + "; preprocess + dK/dV + dQ, 2.5x the forward")
-    if "fwd_varlen" in traffic:
-        kernels["fwd_varlen"]["traffic"] = traffic["fwd_varlen"]
     del vq, vk, vv, vdo, vo, vgrads, vws
 
     # ---- dropout on P: the forward + backward workload again (timed on its own, outside the step)
@@ -369,8 +367,6 @@ def main() -> int:
              f"Philox-4x32-10 in every kernel)")
     kernels["fwd_dropout"] = mfma_entry(f_fwd, df_ms, dnote)
     kernels["bwd_dropout"] = mfma_entry(f_bwd, db_ms, dnote + "; preprocess + dK/dV + dQ")
-    if "fwd_dropout" in traffic:
-        kernels["fwd_dropout"]["traffic"] = traffic["fwd_dropout"]
 
     # ---- additive bias [1, H, N, N] on the forward + backward workload, timed on its own
     gen_b = torch.Generator(device=dev).manual_seed(BIAS["seed"])
@@ -452,6 +448,10 @@ def main() -> int:
     e8["frac"] = e8["achieved"] / e8["peak"]
     kernels["fwd_fp8"] = e8
     del f8ws
+
+    for name, nbytes in traffic.items():  # the entries timed apart from the step
+        if name in kernels and kernels[name]["traffic"] is None:
+            kernels[name]["traffic"] = nbytes
 
     if args.cpu_heads > 0:
         log(f"oracle CPU baseline on {args.cpu_heads} head(s) ...")
