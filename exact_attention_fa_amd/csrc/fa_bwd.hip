@@ -286,24 +286,75 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 
   // One query tile t from buffer P; the copies of tile t+1 go to the other buffer. MASKED: tiles
   // that cross the causal diagonal of some wave (a wave whose keys all lie past the tile skips it).
-  // BIAS: the bias of key `key` for the 16 queries of a 32-query block, packed in bf16 pairs;
-  // the lane part of the offset is formed once, the per-register row offsets are uniform
+  // BIAS: the bias of key `key` for the 16 queries of a 32-query block. Read row-wise: lane
+  // (x = l32 & 7, group g = l32 >> 3, hi) loads 16 bytes, the 8 keys of its group, of query rows
+  // 8 hi + x and 16 + 8 hi + x of the block; an 8 x 8 transpose of 16-bit values inside each
+  // group of 8 lanes then hands lane x its key's values of those 8 + 8 rows, as bf16 pairs.
   const auto brs = bias_rsrc(
       bias.ptr + (long long)(bh / H) * bias.sb + (long long)(bh % H) * bias.sh, Nq, Nk, bias.sq);
-  auto load_bias = [&](int t, int qb, uint32_t (&out)[8]) {
-    const int qb0 = t * kBQ + qb * 32 + 8 * hi;
-    const int lo_off = (int)(((long long)qb0 * bias.sq + key) * 2);
+  auto load_bias = [&](int t, int qb, u32x4 (&raw)[2]) {
+    const int kg = kw + 8 * (l32 >> 3);  // first key of the lane's group
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const int dr = 16 * (r >> 3) + (r & 7);  // key_of_reg(r, hi) - 8 hi
-      const int so = (int)((long long)dr * bias.sq * 2);
-      const uint32_t lo = (key < nk && qb0 + dr < nq) ? bias_ld2(brs, lo_off, so) : 0u;
-      const uint32_t hi16 =
-          (key < nk && qb0 + dr + 1 < nq) ? bias_ld2(brs, lo_off, so + (int)(bias.sq * 2)) : 0u;
-      out[r >> 1] = lo | (hi16 << 16);
+    for (int j = 0; j < 2; ++j) {
+      const int row = t * kBQ + qb * 32 + 16 * j + 8 * hi + (l32 & 7);
+      u32x4 w = {0u, 0u, 0u, 0u};
+      const int off = (int)(((long long)row * bias.sq + kg) * 2);
+      if (row < nq && kg + 8 <= nk) {
+        w = bias_ld16(brs, off);
+      } else if (row < nq && kg < nk) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (kg + e < nk) w[e >> 1] |= bias_ld2(brs, off + 2 * e, 0) << (16 * (e & 1));
+      }
+      raw[j] = w;
     }
   };
-  uint32_t bwn[8];
+  // 8 x 8 transpose of 16-bit values across the 8 lanes x of a group: in, lane x holds row x
+  // (word m = columns 2m, 2m + 1); out, lane x holds column x (word m = rows 2m, 2m + 1).
+  const int tx = l32 & 7;
+  auto transpose8 = [&](u32x4 w) {
+    // stage 1: column bit 2 <-> row bit 2 (lane distance 4), 2-word halves
+    {
+      const bool b = tx & 4;
+      const uint32_t s0 = b ? w[0] : w[2], s1 = b ? w[1] : w[3];
+      const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 4), r1 = (uint32_t)__shfl_xor((int)s1, 4);
+      if (b) { w[0] = r0; w[1] = r1; } else { w[2] = r0; w[3] = r1; }
+    }
+    // now word 2 a + m holds rows (lane's row with bit 2 = a), columns 4 (tx >> 2) + 2 m, + 1
+    // stage 2: column bit 1 <-> row bit 1 (lane distance 2), single words
+    {
+      const bool b = tx & 2;
+      const uint32_t s0 = b ? w[0] : w[1], s1 = b ? w[2] : w[3];
+      const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 2), r1 = (uint32_t)__shfl_xor((int)s1, 2);
+      if (b) { w[0] = r0; w[2] = r1; } else { w[1] = r0; w[3] = r1; }
+    }
+    // now word 2 a + c holds rows (bit 2 = a, bit 1 = c, bit 0 = tx & 1), columns
+    // 4 (tx >> 2) + 2 ((tx >> 1) & 1), + 1
+    // stage 3: column bit 0 <-> row bit 0 (lane distance 1), 16-bit halves
+    const bool b = tx & 1;
+    // send the halves the partner needs: column (tx ^ 1), i.e. half (1 - b) of each word
+    const uint32_t s0 = b ? __builtin_amdgcn_perm(w[1], w[0], 0x05040100u)   // lo halves
+                          : __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);  // hi halves
+    const uint32_t s1 = b ? __builtin_amdgcn_perm(w[3], w[2], 0x05040100u)
+                          : __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
+    const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 1), r1 = (uint32_t)__shfl_xor((int)s1, 1);
+    // r0 = (partner's half for word 0, for word 1), r1 likewise for words 2, 3: rows with bit 0
+    // = 1 - b. Word m of the result: rows 2 m (low half) and 2 m + 1 (high half).
+    u32x4 o;
+    const uint32_t keep0 = b ? __builtin_amdgcn_perm(w[1], w[0], 0x07060302u)
+                             : __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
+    const uint32_t keep1 = b ? __builtin_amdgcn_perm(w[3], w[2], 0x07060302u)
+                             : __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
+    // keepK / rK hold (value for word 2K, value for word 2K + 1) in (lo, hi)
+    const uint32_t ev0 = b ? r0 : keep0, od0 = b ? keep0 : r0;  // rows with bit 0 = 0 / = 1
+    const uint32_t ev1 = b ? r1 : keep1, od1 = b ? keep1 : r1;
+    o[0] = __builtin_amdgcn_perm(od0, ev0, 0x05040100u);
+    o[1] = __builtin_amdgcn_perm(od0, ev0, 0x07060302u);
+    o[2] = __builtin_amdgcn_perm(od1, ev1, 0x05040100u);
+    o[3] = __builtin_amdgcn_perm(od1, ev1, 0x07060302u);
+    return o;
+  };
+  u32x4 bwn[2];
 
   auto step = [&](auto PAR, auto MASKED, int t) {
     constexpr int P = decltype(PAR)::value;
@@ -355,15 +406,22 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
       // than one block's products); the few diagonal tiles load their own.
       uint32_t bw[8];
       if constexpr (BIAS) {
+        u32x4 raw[2];
         if (MK || (qb == 0 && t == tm)) {
-          load_bias(t, qb, bw);
+          load_bias(t, qb, raw);
         } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) bw[i] = bwn[i];
+          raw[0] = bwn[0];
+          raw[1] = bwn[1];
         }
         if (!MK) {
           if (qb == 0) load_bias(t, 1, bwn);
           else if (t + 1 < t1) load_bias(t + 1, 0, bwn);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const u32x4 c = transpose8(raw[j]);  // rows 16 j + 8 hi + 0..7 of the lane's key
+#pragma unroll
+          for (int m = 0; m < 4; ++m) bw[4 * j + m] = c[m];
         }
       }
       f32x16 s, dp;
