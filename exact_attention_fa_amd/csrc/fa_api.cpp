@@ -63,7 +63,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N_q, int N_k, int d) {
   (void)N_k;
   (void)d;
   if (B < 1 || H < 1 || N_q < 1) return 0;
-  // D then L2 = LSE log2(e), each [B, H, N_q] fp32 padded to 16 bytes
+  // -D then -LSE / scale, each [B, H, N_q] fp32 padded to 16 bytes
   return 2 * round_up16((size_t)B * H * N_q * sizeof(float));
 }
 

@@ -7,11 +7,11 @@
 // dS = P * (dP - D) with dP = dO V^T. Then dV = P^T dO, dK = scale dS^T Q, dQ = scale dS K.
 //
 // Three kernels on one stream:
-//   1. bwd_delta:  D_i = sum_k dO_ik O_ik, and L2_i = L_i log2(e) (the log-sum-exp in the base-2
-//                  units the exponentials use); one pass over O and dO, HBM-bound;
+//   1. bwd_delta:  -D_i = -sum_k dO_ik O_ik, and -L_i / scale (the log-sum-exp in the units of the
+//                  unscaled scores q.k), both negated; one pass over O and dO, HBM-bound;
 //   2. bwd_dkdv:   one workgroup per (b, h, 128-key tile); each wave keeps 32 keys' K and V
 //                  fragments and fp32 dK, dV accumulators in registers and streams the query
-//                  tiles (Q, dO, L2, D) through LDS;
+//                  tiles (Q, dO, nLs, nD) through LDS;
 //   3. bwd_dq:     one workgroup per (b, h, 128-query tile); each wave keeps 32 queries' Q and dO
 //                  fragments and an fp32 dQ accumulator in registers and streams K/V tiles.
 // Splitting dQ into its own pass recomputes S and dP a second time (7 products where a fused
@@ -126,13 +126,17 @@ __device__ __forceinline__ int tr_base(int lane) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// 1. D = rowsum(dO * O) and L2 = L log2(e)
+// 1. nD = -rowsum(dO * O) and nLs = -L / scale.
+// Both are stored negated and in the units of the unscaled scores so that the dK/dV kernel can
+// start its score and dP accumulators at them: S - L/scale and dP - D then leave the matrix cores
+// directly, and P = exp2(c (S - L/scale)), dS = P (dP - D) take one multiply each.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__ O,
                                                         const bf16* __restrict__ dO,
                                                         const float* __restrict__ LSE,
-                                                        float* __restrict__ delta,
-                                                        float* __restrict__ lse2, int rows) {
+                                                        float* __restrict__ ndelta,
+                                                        float* __restrict__ nls, int rows,
+                                                        float inv_scale) {
   constexpr int G = D / 8;      // lanes per row
   constexpr int RPB = 256 / G;  // rows per block pass
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
@@ -148,11 +152,11 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__
     }
     s = group_sum<G>(s);
     if (gl == 0) {
-      delta[row] = s;
-      // a row that saw no key (LSE = -inf) gets L2 = +inf, so that every probability the
-      // backward rebuilds for it is exp2(S c - inf) = 0
+      ndelta[row] = -s;
+      // a row that saw no key (LSE = -inf) gets nLs = -inf, so that every probability the
+      // backward rebuilds for it is exp2(c (S - inf)) = 0
       const float l = LSE[row];
-      lse2[row] = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+      nls[row] = l == kNegInf ? kNegInf : -l * inv_scale;
     }
   }
 }
@@ -167,7 +171,7 @@ struct DkdvLds {
   static constexpr int ST = dual_stride<D>(), STO = dual_stride<DV>();
   using Tile = PaddedTile<D, ST>;     // Q
   using TileO = PaddedTile<DV, STO>;  // dO
-  // one buffer: Q tile, dO tile, L2 and D of its 64 rows
+  // one buffer: Q tile, dO tile, nLs and nD of its 64 rows
   static constexpr int kQ = 0, kDO = Tile::kBytes, kL = kDO + TileO::kBytes, kDl = kL + kBQ * 4;
   static constexpr int kBuf = kDl + kBQ * 4;
 };
@@ -186,7 +190,7 @@ constexpr int kDkDv = 0, kDvOnly = 1, kDkOnly = 2;
 template <int D, bool CAUSAL, bool VL, bool DROP, int MODE, bool BIAS, int DV = D>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
+    const bf16* __restrict__ dO, const float* __restrict__ NLs, const float* __restrict__ ND,
     bf16* __restrict__ dK, bf16* __restrict__ dV, const int* __restrict__ lens_q,
     const int* __restrict__ lens_k, int BH, int H, int Nq, int Nk, float c, float scale,
     DropoutParams drop, BiasParams bias) {
@@ -215,8 +219,8 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 
   const bf16* Qh = Q + (size_t)bh * Nq * D;
   const bf16* dOh = dO + (size_t)bh * Nq * DV;
-  const float* Lh = L2 + (size_t)bh * Nq;
-  const float* Dh = Dl + (size_t)bh * Nq;
+  const float* Lh = NLs + (size_t)bh * Nq;
+  const float* Dh = ND + (size_t)bh * Nq;
 
   // resident B operands: K^T and V^T columns (lane = key, 8 dims per k-step)
   bf16x8 kf[D / 16], vf[DV / 16];
@@ -267,16 +271,22 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   tile.init(wave, lane);
   if constexpr (D != DV) tileo.init(wave, lane);
   auto copy = [&](int t, unsigned char* b) {
+    // the wave index passes through an empty asm so that the copies' LDS addresses and wave
+    // conditions are formed here, per tile, from one register: hoisted out of the loop they
+    // would hold a score of scalar registers for the whole kernel and push live values into
+    // scratch memory
+    int w = wave;
+    asm volatile("" : "+s"(w));
     const int q0 = t * kBQ;
-    tile.copy(Qh, q0, nq, b + SM::kQ, wave);
+    tile.copy(Qh, q0, nq, b + SM::kQ, w);
     if constexpr (D == DV)
-      tile.copy(dOh, q0, nq, b + SM::kDO, wave);
+      tile.copy(dOh, q0, nq, b + SM::kDO, w);
     else
-      tileo.copy(dOh, q0, nq, b + SM::kDO, wave);
-    if (wave == 0) copy_row_vec(Lh, q0, nq, b + SM::kL, lane);
-    if (wave == 1) copy_row_vec(Dh, q0, nq, b + SM::kDl, lane);
+      tileo.copy(dOh, q0, nq, b + SM::kDO, w);
+    if (w == 0) copy_row_vec(Lh, q0, nq, b + SM::kL, lane);
+    if (w == 1) copy_row_vec(Dh, q0, nq, b + SM::kDl, lane);
   };
-  // rows past N_q read as zero: their Q and dO rows are zero and L2 = D = 0, so P = 1, dP = 0
+  // rows past N_q read as zero: their Q and dO rows are zero and nLs = nD = 0, so P = 1, dP = 0
   // and dS = 0: they add nothing to dK or dV.
 
   const int qrow = key_of_row(l32) * ST + hi * 16;  // A operand of S and dP: row reads
@@ -424,11 +434,32 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
           for (int m = 0; m < 4; ++m) bw[4 * j + m] = c[m];
         }
       }
+      // the accumulators start at -L/scale and (without dropout) -D of their query rows, so the
+      // products leave S - L/scale and dP - D; register r holds query
+      // qb*32 + key_of_reg(r, hi) = qb*32 + 16 (r >> 3) + 8 hi + (r & 7)
       f32x16 s, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
+      for (int half = 0; half < 2; ++half) {
+        const int qi0 = qb * 32 + 16 * half + 8 * hi;
+        const f32x4 la = *reinterpret_cast<const f32x4*>(ls + qi0);
+        const f32x4 lb = *reinterpret_cast<const f32x4*>(ls + qi0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[8 * half + e] = la[e];
+          s[8 * half + 4 + e] = lb[e];
+        }
+        if constexpr (DROP) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dp[8 * half + e] = 0.f;
+        } else {
+          const f32x4 da = *reinterpret_cast<const f32x4*>(dls + qi0);
+          const f32x4 db4 = *reinterpret_cast<const f32x4*>(dls + qi0 + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dp[8 * half + e] = da[e];
+            dp[8 * half + 4 + e] = db4[e];
+          }
+        }
       }
       if constexpr (D == DV) {
 #pragma unroll
@@ -454,32 +485,32 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
       bf16x8 pf[2], dsf[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int qi0 = qb * 32 + 16 * half + 8 * hi;
-        const f32x4 la = *reinterpret_cast<const f32x4*>(ls + qi0);
-        const f32x4 lb = *reinterpret_cast<const f32x4*>(ls + qi0 + 4);
-        const f32x4 da = *reinterpret_cast<const f32x4*>(dls + qi0);
-        const f32x4 db4 = *reinterpret_cast<const f32x4*>(dls + qi0 + 4);
+        f32x4 da, db4;  // DROP: -D of the rows, applied after the mask
+        if constexpr (DROP) {
+          const int qi0 = qb * 32 + 16 * half + 8 * hi;
+          da = *reinterpret_cast<const f32x4*>(dls + qi0);
+          db4 = *reinterpret_cast<const f32x4*>(dls + qi0 + 4);
+        }
         float p[8], ds[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * half + e;
-          float lr = -(e < 4 ? la[e] : lb[e - 4]);
+          float x = s[r] * c;  // log2 units: c (S - L/scale)
           if constexpr (BIAS) {
             const uint32_t w = bw[r >> 1];
-            lr = __builtin_fmaf((r & 1) ? bf16_hi(w) : bf16_lo(w), kLog2e, lr);
+            x = __builtin_fmaf((r & 1) ? bf16_hi(w) : bf16_lo(w), kLog2e, x);
           }
-          const float pv = exp2_fast(__builtin_fmaf(s[r], c, lr));
-          const float dv_row = e < 4 ? da[e] : db4[e - 4];
+          const float pv = exp2_fast(x);
           if constexpr (DROP) {
             // bit x of byte e: 0 or all ones after the sign-extending extract
             const uint32_t km = (uint32_t)__builtin_amdgcn_sbfe(
                 (int)mbits[half][e >> 2], 8 * (e & 3) + (l32 & 7), 1);
             p[e] = __uint_as_float(__float_as_uint(pv) & km);
             ds[e] = pv * __builtin_fmaf(__uint_as_float(__float_as_uint(drop.inv_keep) & km),
-                                         dp[r], -dv_row);
+                                         dp[r], e < 4 ? da[e] : db4[e - 4]);
           } else {
             p[e] = pv;
-            ds[e] = pv * (dp[r] - dv_row);
+            ds[e] = pv * dp[r];
           }
         }
         pf[half] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
@@ -560,7 +591,7 @@ struct DqLds {
 template <int D, bool CAUSAL, bool VL, bool DROP, bool BIAS, int DV = D>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
+    const bf16* __restrict__ dO, const float* __restrict__ NLs, const float* __restrict__ ND,
     bf16* __restrict__ dQ, const int* __restrict__ lens_q, const int* __restrict__ lens_k,
     int BH, int H, int Nq, int Nk, float c, float scale, DropoutParams drop, BiasParams bias) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -616,8 +647,9 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
       dof[ks] = as_bf16x8(b);
     }
   }
-  const float lq = qi < nq ? L2[(size_t)bh * Nq + qi] : 0.f;
-  const float dq_d = qi < nq ? Dl[(size_t)bh * Nq + qi] : 0.f;
+  // this lane's row: L in log2 units (+inf for a row that saw no key) and -D
+  const float lq = qi < nq ? -c * NLs[(size_t)bh * Nq + qi] : 0.f;
+  const float nd = qi < nq ? ND[(size_t)bh * Nq + qi] : 0.f;
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -656,8 +688,10 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
     wait_vmem();
     __syncthreads();
     if (t + 1 < ntiles) {
-      ktile.copy(Kh, (t + 1) * kBC, nk, P ? kb0 : kb1, wave);
-      vtile.copy(Vh, (t + 1) * kBC, nk, P ? vb0 : vb1, wave);
+      int w = wave;  // formed per tile, as in the dK/dV kernel
+      asm volatile("" : "+s"(w));
+      ktile.copy(Kh, (t + 1) * kBC, nk, P ? kb0 : kb1, w);
+      vtile.copy(Vh, (t + 1) * kBC, nk, P ? vb0 : vb1, w);
     }
     const int kbase = t * kBC;
     if (MK && kbase > horizon) return;
@@ -683,13 +717,17 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
         bv[g] = w;
       }
     }
+    // dP^T starts at -D, so the products leave dP - D (not with dropout, where D is subtracted
+    // after the mask, nor with a bias or d_v != d, where the early live range would not fit the
+    // registers)
+    constexpr bool fold_d = !DROP && !BIAS && D == DV;
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s[kb][r] = 0.f;
-        dp[kb][r] = 0.f;
+        dp[kb][r] = fold_d ? nd : 0.f;
       }
     if constexpr (D == DV) {
 #pragma unroll
@@ -741,9 +779,9 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
           const float pv = exp2_fast(__builtin_fmaf(s[kb][r], c, lr));
           if constexpr (DROP) {
             const float z = keep_factor(mw[e >> 1], e & 1, drop.thresh, drop.inv_keep);
-            ds[r] = pv * __builtin_fmaf(z, dp[kb][r], -dq_d);
+            ds[r] = pv * __builtin_fmaf(z, dp[kb][r], nd);
           } else {
-            ds[r] = pv * (dp[kb][r] - dq_d);
+            ds[r] = pv * (fold_d ? dp[kb][r] : dp[kb][r] + nd);
           }
         }
       }
@@ -798,12 +836,12 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
   const int BH = a.B * a.H;
   const float c = a.scale * kLog2e;
   const int rows = BH * a.Nq;
-  float* lse2 = a.delta + bwd_lse2_offset(a.B, a.H, a.Nq);
+  float* nls = a.delta + bwd_lse2_offset(a.B, a.H, a.Nq);
   if (phases & 1u) {
     constexpr int RPB = 256 / (DV / 8);
     const int grid = (rows + RPB * 4 - 1) / (RPB * 4);
     hipLaunchKernelGGL((bwd_delta_kernel<DV>), dim3(grid), dim3(256), 0, a.stream, a.o, a.dout,
-                       a.lse, a.delta, lse2, rows);
+                       a.lse, a.delta, nls, rows, 1.f / a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -812,14 +850,14 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     constexpr bool split = (DROP || BIAS) && D == 128;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, split ? kDvOnly : kDkDv, BIAS, DV>),
-                       dim3((unsigned)grid), dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, lse2,
+                       dim3((unsigned)grid), dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, nls,
                        a.delta, a.dk, a.dv, a.lens_q, a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale,
                        a.drop, a.bias);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (split) {
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, kDkOnly, BIAS, DV>),
-                         dim3((unsigned)grid), dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, lse2,
+                         dim3((unsigned)grid), dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, nls,
                          a.delta, a.dk, a.dv, a.lens_q, a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale,
                          a.drop, a.bias);
       e = hipGetLastError();
@@ -830,7 +868,7 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
     const long long grid = (long long)BH * ((a.Nq + kBR - 1) / kBR);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VL, DROP, BIAS, DV>), dim3((unsigned)grid),
-                       dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, lse2, a.delta, a.dq, a.lens_q,
+                       dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, nls, a.delta, a.dq, a.lens_q,
                        a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale, a.drop, a.bias);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -841,7 +879,7 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
 }  // namespace
 
 size_t bwd_lse2_offset(int B, int H, int Nq) {
-  // D first, then L2, each padded to a multiple of 16 bytes (counted in floats)
+  // nD first, then nLs, each padded to a multiple of 16 bytes (counted in floats)
   return (((size_t)B * H * Nq + 3) / 4) * 4;
 }
 

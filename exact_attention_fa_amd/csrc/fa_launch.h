@@ -48,7 +48,7 @@ struct BwdArgs {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  float* delta;  // workspace: D = rowsum(dO * O) [B, H, Nq], then L2 = LSE log2(e) [B, H, Nq]
+  float* delta;  // workspace: -D = -rowsum(dO * O) [B, H, Nq], then -LSE / scale [B, H, Nq]
   int B, H, Nq, Nk, d;
   float scale;
   bool causal;

@@ -98,7 +98,7 @@ fa_status fa_bwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_
  * Same layouts, workspace and validation as fa_bwd; they must run in this order on one stream,
  * since the later two read what the first writes into the workspace:
  *   fa_bwd_preprocess: D = rowsum(dO * O) ("Geri Yayılım": D is taken from the forward output)
- *                      and L2 = lse * log2(e) into the workspace; uses o, lse, dout;
+ *                      and lse / scale, both negated, into the workspace; uses o, lse, dout;
  *   fa_bwd_dkdv:       dK and dV; uses q, k, v, dout and the workspace;
  *   fa_bwd_dq:         dQ; uses q, k, v, dout and the workspace.
  */
