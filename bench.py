@@ -14,7 +14,8 @@ entries are timed apart from the step: the paged-cache decode with grouped query
 causal forward + backward over a batch of eight sequences of different lengths (TFLOP/s of the
 valid rows and keys only), the forward + backward workload with dropout on P, with an additive
 bias, and with d_v = 64, and the FP8 forward with incoherent processing (against the dense fp8
-peak).
+peak). Last, a plain 8192^3 bf16 GEMM on random data (the vendor library) gives the rate the
+matrix cores sustain on such data; every bf16 MFMA entry also carries its fraction of that rate.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -41,6 +42,7 @@ VARLEN = dict(B=8, H=16, N=8192, d=128, n_min=1024, causal=True, seed=21)  # var
 DROPOUT = dict(p=0.1, seed=0x5EED, offset=0)  # dropout on P over the forward+backward workload
 FP8 = dict(incoherent=True, seed=0xF8)          # FP8 forward over the forward workload
 BIAS = dict(seed=0xB1A5)  # additive bias [1, H, N, N] (shared by the batch), 2 N(0, 1) in bf16
+GEMM = dict(n=8192, seed=0x6E, reps=10)  # plain bf16 GEMM on random data: the sustained MFMA rate
 
 
 def log(msg: str) -> None:
@@ -203,7 +205,7 @@ def main() -> int:
     f_fwd = metrics.attention_flops(B, H, N, N, d, causal=causal)
     f_bwd = metrics.attention_flops(B, H, N, N, d, causal=causal, backward=True)
     gemm = f_fwd / 2  # one N x N x d product, causal-halved
-    pre_bytes = 2 * B * H * N * d * 2 + B * H * N * 12  # O, dO, LSE read; D, LSE*log2(e) written
+    pre_bytes = 2 * B * H * N * d * 2 + B * H * N * 12  # O, dO, LSE read; -D, -LSE/scale written
     dec_bytes = metrics.decode_bytes(DB, DH, DN, Dd)
 
     def mfma_entry(flops, t_ms, note):
@@ -221,7 +223,7 @@ def main() -> int:
         "bwd_dkdv": mfma_entry(4 * gemm, ms["bwd_dkdv"], "4 products (S, dP, dV, dK), causal"),
         "bwd_dq": mfma_entry(1 * gemm, ms["bwd_dq"],
                              "1 algorithmic product (dQ); it also re-runs S and dP"),
-        "bwd_preprocess": hbm_entry(pre_bytes, ms["bwd_preprocess"], "read O, dO and LSE, write D and LSE*log2(e)"),
+        "bwd_preprocess": hbm_entry(pre_bytes, ms["bwd_preprocess"], "read O, dO and LSE, write -D and -LSE/scale"),
         "decode": hbm_entry(dec_bytes, ms["decode"],
                             "K and V read once + q, o, lse (split + combine kernels)"),
     }
@@ -452,6 +454,35 @@ def main() -> int:
     for name, nbytes in traffic.items():  # the entries timed apart from the step
         if name in kernels and kernels[name]["traffic"] is None:
             kernels[name]["traffic"] = nbytes
+
+    # ---- the vendor GEMM on random bf16 data, for context beside the published-peak fractions:
+    # with operands like the attention's the card holds a shader clock well below the 2.4 GHz the
+    # published peak assumes, so this is what its matrix cores sustain on such data
+    gm = GEMM["n"]
+    gen_g = torch.Generator(device=dev).manual_seed(GEMM["seed"])
+    ga = torch.randn((gm, gm), generator=gen_g, device=dev).to(torch.bfloat16)
+    gb = torch.randn((gm, gm), generator=gen_g, device=dev).to(torch.bfloat16)
+    gc = torch.empty((gm, gm), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.matmul(ga, gb, out=gc)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(GEMM["reps"]):
+        torch.matmul(ga, gb, out=gc)
+    g1.record()
+    torch.cuda.synchronize()
+    g_ms = g0.elapsed_time(g1) / GEMM["reps"]
+    g_tf = 2.0 * gm ** 3 / (g_ms * 1e-3) / 1e12
+    log(f"bf16 GEMM {gm}^3 on N(0,1) data: {g_ms:.3f} ms, {g_tf:.0f} TFLOP/s")
+    out["gemm_bf16_random"] = {
+        "what": f"torch.matmul {gm} x {gm} x {gm} bf16 (hipBLASLt), iid N(0,1) operands",
+        "tflops": g_tf, "frac_peak": g_tf / peak_tf}
+    for e in kernels.values():
+        if e["unit"] == "TFLOP/s" and e["peak"] == peak_tf:
+            e["frac_of_gemm"] = e["achieved"] / g_tf
+    roof["frac_of_gemm"] = kernels[dominant].get("frac_of_gemm")
+    del ga, gb, gc
 
     if args.cpu_heads > 0:
         log(f"oracle CPU baseline on {args.cpu_heads} head(s) ...")
