@@ -323,14 +323,17 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
   f32x16 sa0, sa1, sb0, sb1;
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  if constexpr (BIAS)
-    if (ntiles > 0) load_bias(0, bnext);
-  copy_k(0, kb0);
-  copy_v(0, vb0);
-  if (ntiles > 1) copy_k(1, kb1);
-  wait_vmem();
-  __syncthreads();
-  qk(sa0, sa1, kb0);
+  // (ntiles is the same for every wave; a workgroup with no tile to visit, e.g. padding rows of a
+  // short sequence, goes straight to writing its empty rows)
+  if (ntiles > 0) {
+    if constexpr (BIAS) load_bias(0, bnext);
+    copy_k(0, kb0);
+    copy_v(0, vb0);
+    if (ntiles > 1) copy_k(1, kb1);
+    wait_vmem();
+    __syncthreads();
+    qk(sa0, sa1, kb0);
+  }
   int t = 0;
   for (; t + 1 < ntiles; t += 2) {
     step(I0(), sa0, sa1, sb0, sb1, t);
