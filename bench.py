@@ -55,7 +55,7 @@ KERNEL_FAMILY = {"fwd": "fwd", "fwd_varlen": "fwd", "fwd_dropout": "fwd", "fwd_b
                  "fwd_dv64": "fwd",
                  "bwd_preprocess": "bwd", "bwd_dkdv": "bwd", "bwd_dq": "bwd",
                  "decode": "decode", "decode_paged_gqa": "decode"}
-TRAFFIC_KEY = {"decode": "decode_split", "decode_paged_gqa": "decode_paged_split",
+TRAFFIC_KEY = {"decode": "decode_split", "decode_paged_gqa": "decode_paged_mfma",
                "fwd_dv64": "fwd_dv"}
 
 

@@ -187,154 +187,208 @@ hipError_t launch(const DecodeArgs& a) {
 }
 
 
-// Split-KV decode over a paged cache with grouped query heads. One workgroup per (b, group of HG
-// query heads that share one K/V head, split): every K/V row of the split is read once and
-// scored against the HG query rows, so the K/V bytes are shared by the group. Rows are found
-// through the block table (power-of-two block size: shift and mask); everything else is the
-// contiguous kernel above, with HG running (max, sum, output) triples per lane group.
-template <int D, int HG>
-__global__ __launch_bounds__(kDecWaves * 64) void decode_paged_split_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ Kc, const bf16* __restrict__ Vc,
-    const int* __restrict__ table, const int* __restrict__ lens, float* __restrict__ part_o,
-    float* __restrict__ part_lse, int H, int Hkv, int C, int chunk, int bs_log2, int num_blocks,
-    int max_blocks, float c) {
-  constexpr int G = D / 8;     // lanes per key row
-  constexpr int KPI = 64 / G;  // key rows per wave instruction
-  constexpr int U = HG >= 8 ? 4 : 8;
-  constexpr int KPW = KPI * U;
-  constexpr int NGRP = kDecWaves * KPI;
-  __shared__ float sm_m[NGRP], sm_l[NGRP];
-  __shared__ float sm_acc[NGRP][D];
+// Split-KV decode over a paged cache with grouped query heads, on the matrix cores: with several
+// query heads per K/V head the vector-ALU scheme above would spend a dot product, a lane
+// reduction and d/8 multiply-adds per row and per query head, while the matrix cores take a whole
+// group per instruction (measured at B8, 65536 positions, d128, against a vector-ALU kernel of
+// that scheme: as fast with one query head per K/V head, 1.06x with 4, 1.6x with 8, 2.1x with
+// 16, 2.9x with 32). One wave per (b, K/V head, block of up to 32 query
+// heads of its group, split): the block's query heads play the 32 query rows of the forward
+// kernel's transposed products, so S^T = K Q^T and O^T = V^T P^T run on
+// v_mfma_f32_32x32x16_bf16 with lane = query head. A tile is 32 positions: the wave reads its K
+// and V rows with whole-row 16-byte loads (d/8 consecutive lanes per row, as the vector kernel
+// does), keeps them in registers while the previous tile is computed, then writes them to two
+// private LDS tiles, from which the K rows come back in the A-operand order of the first product
+// and the V rows transposed (ds_read_b64_tr_b16) for the second, as in the forward kernel. The
+// block ids of a tile's rows are loaded one tile ahead, one row per lane, and handed to the lanes
+// that load each row by a lane shuffle. The online softmax is the forward's; each wave writes its
+// split's normalised output and log-sum-exp per query head, and the combine kernel merges the
+// splits. Heads past the group in the last block have zero queries and are never stored.
+template <int D>
+__global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(64) void
+decode_paged_mfma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ Kc,
+                         const bf16* __restrict__ Vc, const int* __restrict__ table,
+                         const int* __restrict__ lens, float* __restrict__ part_o,
+                         float* __restrict__ part_lse, int H, int Hkv, int C, int chunk,
+                         int bs_log2, int num_blocks, int max_blocks, float c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int KS = D / 16;          // 16-dim steps of the first product = row pieces per lane
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;       // rows per wave-wide load
+  constexpr int KST = 2 * D + 16;     // K row stride in LDS (bytes), as in the forward kernel
+  constexpr int VST = 2 * D + (D == 128 ? 32 : 16);  // V row stride, as in the forward kernel
+  __shared__ __attribute__((aligned(16))) unsigned char kt[32 * KST];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[32 * VST];
 
-  const int bid = blockIdx.x;
-  const int split = bid % C, bhg = bid / C;
-  const int ngroups = H / HG;
-  const int b = bhg / ngroups, h0 = (bhg % ngroups) * HG;
-  const int kvh = h0 / (H / Hkv);
+  const int G = H / Hkv, nhb = (G + 31) / 32;
+  int bid = blockIdx.x;
+  const int split = bid % C;
+  bid /= C;
+  const int hb = bid % nhb;
+  bid /= nhb;
+  const int kvh = bid % Hkv, b = bid / Hkv;
+  const int lane = threadIdx.x, l32 = lane & 31, hi = lane >> 5;
+  const int nheads = min(32, G - 32 * hb);  // query heads of this block
+  const int h0 = kvh * G + 32 * hb;          // first query head of the block
   const int len = min(max(lens[b], 0), max_blocks << bs_log2);
   const int k0 = split * chunk;
   const int k1 = min(len, k0 + chunk);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane / G, gl = lane % G;
+  const int ntiles = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
   const int bmask = (1 << bs_log2) - 1;
-  const size_t head_off = ((size_t)kvh << bs_log2) * D + gl * 8;  // this head inside a block
+  const size_t head_off = ((size_t)kvh << bs_log2) * D;  // this K/V head inside a block
   const size_t block_stride = ((size_t)Hkv << bs_log2) * D;
   const int* trow = table + (size_t)b * max_blocks;
 
-  u32x4 qv[HG];
+  // B operand of S^T = K Q^T: query head h0 + l32, dims 16 ks + 8 hi (zero past the block)
+  bf16x8 qf[KS];
 #pragma unroll
-  for (int j = 0; j < HG; ++j) qv[j] = ld16(Q + ((size_t)b * H + h0 + j) * D + gl * 8);
-  float m[HG], l[HG], acc[HG][8];
-#pragma unroll
-  for (int j = 0; j < HG; ++j) {
-    m[j] = kNegInf;
-    l[j] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (l32 < nheads) x = ld16(Q + ((size_t)b * H + h0 + l32) * D + ks * 16 + hi * 8);
+    qf[ks] = as_bf16x8(x);
   }
 
-  // block ids of the next iteration's rows are loaded one iteration ahead, so the table lookup
-  // latency overlaps the current rows' K/V loads instead of preceding them
-  auto block_of = [&](int key) -> unsigned {
+  // loads: piece j of this lane is chunk (lane % CPR) of tile row RPI j + lane / CPR
+  const int lrow = lane / CPR, lch = lane % CPR;
+  auto block_of = [&](int t) -> unsigned {  // block id of tile row l32 of tile t (k1: none)
+    const int key = k0 + 32 * t + l32;
     return key < k1 ? (unsigned)trow[key >> bs_log2] : 0xffffffffu;
   };
-  unsigned blk[U];
+  auto load_tile = [&](int t, unsigned blk_row, u32x4 (&kr)[KS], u32x4 (&vr)[KS]) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) blk[u] = block_of(k0 + wave * KPW + u * KPI + g);
-  for (int base = k0 + wave * KPW; base < k1; base += kDecWaves * KPW) {
-    u32x4 kr[U], vr[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int key = base + u * KPI + g;
+    for (int j = 0; j < KS; ++j) {
+      const int r = RPI * j + lrow;
+      const unsigned blk = (unsigned)__shfl((int)blk_row, r);
+      // past the split, or an id out of range: zero rows
+      const bool ok = blk < (unsigned)num_blocks;
+      const size_t off = blk * block_stride + head_off +
+                         (size_t)((k0 + 32 * t + r) & bmask) * D + lch * 8;
       const u32x4 z = {0u, 0u, 0u, 0u};
-      kr[u] = z;
-      vr[u] = z;
-      if (blk[u] < (unsigned)num_blocks) {  // past the chunk, or an id out of range: zero rows
-        const size_t off = blk[u] * block_stride + head_off + (size_t)(key & bmask) * D;
-        kr[u] = ld16_nt(Kc + off);
-        vr[u] = ld16_nt(Vc + off);
-      }
+      kr[j] = ok ? ld16_nt(Kc + off) : z;
+      vr[j] = ok ? ld16_nt(Vc + off) : z;
     }
+  };
+  // rows into the LDS tiles (the reads of the previous tile came earlier in this wave's program
+  // order, and one wave's LDS operations complete in order)
+  auto put_tile = [&](const u32x4 (&kr)[KS], const u32x4 (&vr)[KS]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) blk[u] = block_of(base + kDecWaves * KPW + u * KPI + g);
-#pragma unroll
-    for (int j = 0; j < HG; ++j) {
-      float s[U];
-      float mx = kNegInf;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float dot = group_sum<G>(dot8(kr[u], qv[j]));
-        s[u] = (base + u * KPI + g < k1) ? dot * c : kNegInf;
-        mx = fmaxf(mx, s[u]);
-      }
-      const float m_new = fmaxf(m[j], mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = exp2_fast(m[j] - m_use);
-      m[j] = m_new;
-      l[j] *= alpha;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[j][e] *= alpha;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float p = exp2_fast(s[u] - m_use);
-        l[j] += p;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t vw = vr[u][w];
-          acc[j][2 * w] = __builtin_fmaf(p, bf16_lo(vw), acc[j][2 * w]);
-          acc[j][2 * w + 1] = __builtin_fmaf(p, bf16_hi(vw), acc[j][2 * w + 1]);
-        }
-      }
+    for (int j = 0; j < KS; ++j) {
+      const int r = RPI * j + lrow;
+      st16(kt + r * KST + lch * 16, kr[j]);
+      st16(vt + r * VST + lch * 16, vr[j]);
     }
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  // m in log2 units of the scaled scores; l: fp32 sum (log-sum-exp); lq: sum of the bf16 P that
+  // feed the second product (the normaliser of the output)
+  float m_run = kNegInf, l_run = 0.f, lq_run = 0.f;
+
+  // A operand of S^T: K row key_of_row(l32), dims 16 ks + 8 hi; A operand of O^T (V^T rows =
+  // dims) by ds_read_b64_tr_b16, as in the forward kernel
+  const int kr0 = key_of_row(l32) * KST + hi * 16;
+  const int vj = lane & 15, vg = lane >> 4;
+  const int vr0 = (8 * (vg >> 1) + (vj >> 2)) * VST + (16 * (vg & 1) + 4 * (vj & 3)) * 2;
+
+  auto step = [&](int t) {
+    f32x16 sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sc = mfma32(as_bf16x8(ld16(kt + kr0 + ks * 32)), qf[ks], sc);
+    // register r holds key k0 + 32 t + key_of_reg(r, hi); keys at or past k1 are masked
+    const int kb = k0 + 32 * t;
+    if (kb + 32 > k1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kb + key_of_reg(r, hi) >= k1) sc[r] = kNegInf;
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+    // finite: every tile that is visited holds at least one key below k1
+    const float m_new = fmaxf(m_run, halves_max(mx) * c);
+    const float alpha = exp2_fast(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+    lq_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sc[r] = exp2_fast(__builtin_fmaf(sc[r], c, -m_new));
+      l_run += sc[r];
+    }
+    bf16x8 pf[2];
+    pf[0] = pack_bf16x8(sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7]);
+    pf[1] = pack_bf16x8(sc[8], sc[9], sc[10], sc[11], sc[12], sc[13], sc[14], sc[15]);
+    lq_run = sum_bf16x8(pf[1], sum_bf16x8(pf[0], lq_run));
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        acc[db] = mfma32(lds_read_tr_pair(vt + vr0 + st * 16 * VST + db * 64, 4 * VST), pf[st],
+                         acc[db]);
+  };
+
+  // tile t is computed from the LDS tiles while tile t + 1 loads into (kr, vr) (written to LDS
+  // after the products of tile t) and the block ids of tile t + 2 are fetched
+  u32x4 kr[KS], vr[KS];
+  unsigned blk_next = 0xffffffffu;
+  if (ntiles > 0) {
+    load_tile(0, block_of(0), kr, vr);
+    put_tile(kr, vr);
+    if (ntiles > 1) blk_next = block_of(1);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile(t + 1, blk_next, kr, vr);
+    blk_next = t + 2 < ntiles ? block_of(t + 2) : 0xffffffffu;
+    step(t);
+    if (more) put_tile(kr, vr);
   }
 
-  // ---- merge the lane groups of the workgroup, one query head at a time
-  const int grp = wave * KPI + g;
+  // ---- this split's partial for every query head of the block (rows of acc = dims)
+  const float l_tot = halves_sum(l_run);
+  const float lq_tot = halves_sum(lq_run);
+  if (l32 < nheads) {
+    const size_t pidx = ((size_t)b * H + h0 + l32) * C + split;
+    const bool empty = ntiles == 0;
+    const float inv = empty ? 0.f : 1.f / lq_tot;
+    float* orow = part_o + pidx * D;
 #pragma unroll
-  for (int j = 0; j < HG; ++j) {
-    __syncthreads();  // the previous head's reads of the LDS slots are done
-    if (gl == 0) {
-      sm_m[grp] = m[j];
-      sm_l[grp] = l[j];
-    }
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm_acc[grp][gl * 8 + e] = acc[j][e];
-    __syncthreads();
-    float M = kNegInf;
-#pragma unroll 4
-    for (int i = 0; i < NGRP; ++i) M = fmaxf(M, sm_m[i]);
-    const size_t pidx = ((size_t)b * H + h0 + j) * C + split;
-    for (int d = tid; d < D; d += kDecWaves * 64) {
-      if (M == kNegInf) {  // empty chunk: weight zero in the combine
-        part_o[pidx * D + d] = 0.f;
-        if (d == 0) part_lse[pidx] = kNegInf;
-        continue;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = acc[db][4 * q4 + e] * inv;
+        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * q4 + 4 * hi) = w;
       }
-      float L = 0.f, o = 0.f;
-      for (int i = 0; i < NGRP; ++i) {
-        const float w = exp2_fast(sm_m[i] - M);
-        L += sm_l[i] * w;
-        o += sm_acc[i][d] * w;
-      }
-      part_o[pidx * D + d] = o / L;
-      if (d == 0) part_lse[pidx] = (M + log2_fast(L)) * kLn2;
-    }
+    if (hi == 0) part_lse[pidx] = empty ? kNegInf : (m_run + log2_fast(l_tot)) * kLn2;
   }
+#endif
 }
 
-template <int D, int HG>
+template <int D>
 hipError_t launch_paged(const DecodePagedArgs& a) {
   const int C = a.splits;
   const int max_len = a.max_blocks * a.block_size;
   const int chunk = (max_len + C - 1) / C;
-  const long long grid = (long long)a.B * (a.H / HG) * C;
+  const int nhb = (a.H / a.Hkv + 31) / 32;
+  const long long grid = (long long)a.B * a.Hkv * nhb * C;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float c = a.scale * kLog2e;
   const int bs_log2 = __builtin_ctz((unsigned)a.block_size);
-  hipLaunchKernelGGL((decode_paged_split_kernel<D, HG>), dim3((unsigned)grid),
-                     dim3(kDecWaves * 64), 0, a.stream, a.q, a.k_cache, a.v_cache, a.block_table,
-                     a.seq_lens, a.part_o, a.part_lse, a.H, a.Hkv, C, chunk, bs_log2,
-                     a.num_blocks, a.max_blocks, c);
+  hipLaunchKernelGGL((decode_paged_mfma_kernel<D>), dim3((unsigned)grid), dim3(64), 0, a.stream,
+                     a.q, a.k_cache, a.v_cache, a.block_table, a.seq_lens, a.part_o, a.part_lse,
+                     a.H, a.Hkv, C, chunk, bs_log2, a.num_blocks, a.max_blocks, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.H), dim3(64), 0, a.stream,
@@ -342,15 +396,6 @@ hipError_t launch_paged(const DecodePagedArgs& a) {
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_paged_d(const DecodePagedArgs& a) {
-  switch (decode_paged_heads_per_group(a.H, a.Hkv)) {
-    case 8: return launch_paged<D, 8>(a);
-    case 4: return launch_paged<D, 4>(a);
-    case 2: return launch_paged<D, 2>(a);
-    default: return launch_paged<D, 1>(a);
-  }
-}
 }  // namespace
 
 int decode_auto_splits(int B, int H, int Nk, int d) {
@@ -369,22 +414,16 @@ hipError_t launch_decode(const DecodeArgs& a) {
   return a.d == 128 ? launch<128>(a) : launch<64>(a);
 }
 
-int decode_paged_heads_per_group(int H, int Hkv) {
-  const int g = H / Hkv;
-  for (int hg = 8; hg > 1; hg >>= 1)
-    if (g % hg == 0) return hg;
-  return 1;
-}
-
 int decode_paged_auto_splits(int B, int H, int Hkv, int max_len, int d) {
   (void)d;
-  const long long wgs = (long long)B * (H / decode_paged_heads_per_group(H, Hkv));
-  // workgroups: 4 per CU on 256 CUs. Measured at B8 H32 H_kv8, 65536 positions: 16 splits
-  // (1024 workgroups) 0.36 ms, 64 splits 0.38 ms, 256 splits 0.50 ms; the per-workgroup merge of
-  // several heads makes short chunks cost more than in the contiguous kernel.
-  const long long target = 1024;
-  long long c = (target + wgs - 1) / wgs;
-  const long long by_len = ((long long)max_len + 1023) / 1024;  // at least ~1024 positions
+  // one wave per split of each (b, K/V head, block of 32 query heads): about 8 waves per CU,
+  // with at least ~512 positions per split. Measured at B8, 65536 positions, d128: 4 query heads
+  // per K/V head (64 waves per split) 16 splits 0.353 ms, 32 splits 0.333 ms, 64 splits 0.354 ms;
+  // 32 heads on one K/V head (8 waves per split) 32 splits 0.145 ms, 64 0.097 ms, 128 0.092 ms,
+  // 256 0.129 ms (each split also writes and the combine reads one partial row per query head).
+  const long long waves = (long long)B * Hkv * ((H / Hkv + 31) / 32);
+  long long c = (2048 + waves - 1) / waves;
+  const long long by_len = ((long long)max_len + 511) / 512;
   if (c > by_len) c = by_len;
   if (c > 1024) c = 1024;
   if (c < 1) c = 1;
@@ -392,7 +431,7 @@ int decode_paged_auto_splits(int B, int H, int Hkv, int max_len, int d) {
 }
 
 hipError_t launch_decode_paged(const DecodePagedArgs& a) {
-  return a.d == 128 ? launch_paged_d<128>(a) : launch_paged_d<64>(a);
+  return a.d == 128 ? launch_paged<128>(a) : launch_paged<64>(a);
 }
 
 }  // namespace fa

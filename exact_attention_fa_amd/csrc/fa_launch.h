@@ -128,8 +128,6 @@ hipError_t launch_decode_paged(const DecodePagedArgs& a);
 
 // Split count used by the decode when the caller passes 0.
 int decode_auto_splits(int B, int H, int Nk, int d);
-// Query heads that one paged-decode workgroup serves together (a divisor of H / H_kv, <= 8).
-int decode_paged_heads_per_group(int H, int Hkv);
 // Split count used by the paged decode when the caller passes 0.
 int decode_paged_auto_splits(int B, int H, int Hkv, int max_len, int d);
 

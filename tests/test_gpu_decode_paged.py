@@ -43,6 +43,11 @@ CASES = [  # (B, H, H_kv, d, block_size, seq_lens)
     (1, 12, 4, 64, 1, [77]),                 # block size 1, 3 heads per group
     (2, 6, 2, 128, 64, [5000, 1]),           # 3 heads per group, long and single position
     (2, 4, 2, 64, 128, [129, 255]),          # positions straddling large blocks
+    # groups of 8 or more query heads run on the matrix cores
+    (2, 64, 8, 128, 16, [1000, 4097]),       # 8 query heads per K/V head
+    (2, 32, 1, 128, 16, [33, 2000]),         # MQA, one full block of 32 query heads
+    (1, 40, 1, 64, 8, [300]),                # 40 heads: a full block and a block of 8
+    (2, 16, 2, 64, 1, [77, 31]),             # block size 1, 8 heads per group
 ]
 
 
@@ -58,8 +63,10 @@ def test_decode_paged_parity(gpu, case, splits):
     assert_fwd_close(o, lse, o_ref, l_ref, f"paged {case} C{splits}")
 
 
-def test_decode_paged_split_invariance(gpu):
-    q16, kc, vc, table, sl = _case(81, 4, 32, 8, 128, 16, [9000, 17, 4096, 2500])
+@pytest.mark.parametrize("heads", [(32, 8), (64, 4)], ids=["group4", "group16"])
+def test_decode_paged_split_invariance(gpu, heads):
+    H, H_kv = heads
+    q16, kc, vc, table, sl = _case(81, 4, H, H_kv, 128, 16, [9000, 17, 4096, 2500])
     res = [_run(gpu, q16, kc, vc, table, sl, c) for c in (1, 3, 16, 100)]
     for o, l in res[1:]:
         assert np.max(np.abs(o - res[0][0])) <= 2 ** -7  # one bf16 ulp at |o| < 2
@@ -90,10 +97,11 @@ def test_decode_paged_matches_contiguous_decode(gpu):
     assert np.max(np.abs(l_p - l_c.cpu().numpy()[:, :, 0])) <= 1e-5
 
 
-def test_decode_paged_edge_cases(gpu):
+@pytest.mark.parametrize("heads", [(4, 2), (16, 2)], ids=["group2", "group8"])
+def test_decode_paged_edge_cases(gpu, heads):
     """A sequence with no position gives o = 0, lse = -inf; a block id outside [0, num_blocks)
     reads as zero rows (its positions score 0 and contribute v = 0)."""
-    B, H, H_kv, d, bs = 3, 4, 2, 128, 16
+    B, (H, H_kv), d, bs = 3, heads, 128, 16
     q16, kc, vc, table, sl = _case(93, B, H, H_kv, d, bs, [40, 40, 40])
     sl = sl.copy()
     sl[1] = 0
@@ -114,10 +122,11 @@ def test_decode_paged_edge_cases(gpu):
     assert bad >= 0
 
 
-def test_decode_paged_serving_size(gpu):
-    """B8 H32 H_kv8, 32768 positions per sequence (block size 16), d128: every (b, h) against
-    the oracle."""
-    B, H, H_kv, d, bs, n = 8, 32, 8, 128, 16, 32768
+@pytest.mark.parametrize("heads", [(32, 8), (64, 8)], ids=["group4", "group8"])
+def test_decode_paged_serving_size(gpu, heads):
+    """B8, 32768 positions per sequence (block size 16), d128, 4 or 8 query heads per K/V head:
+    every (b, h) against the oracle."""
+    B, (H, H_kv), d, bs, n = 8, heads, 128, 16, 32768
     q16, kc, vc, table, sl = _case(95, B, H, H_kv, d, bs, [n] * B)
     o, lse = _run(gpu, q16, kc, vc, table, sl)
     o_ref, l_ref = _oracle(q16, kc, vc, table, sl, default_scale(d))
