@@ -13,8 +13,8 @@ listed, and `roofline` repeats the entry of the step's kernel that takes the mos
 entries are timed apart from the step: the paged-cache decode with grouped query heads, a
 causal forward + backward over a batch of eight sequences of different lengths (TFLOP/s of the
 valid rows and keys only), the forward + backward workload with dropout on P, with an additive
-bias, and with d_v = 64, and the FP8 forward with incoherent processing (against the dense fp8
-peak). Last, a plain 8192^3 bf16 GEMM on random data (the vendor library) gives the rate the
+bias, with d_v = 64 and with 4 K/V heads (grouped query heads), and the FP8 forward with
+incoherent processing (against the dense fp8 peak). Last, a plain 8192^3 bf16 GEMM on random data (the vendor library) gives the rate the
 matrix cores sustain on such data; every bf16 MFMA entry also carries its fraction of that rate.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -42,6 +42,7 @@ VARLEN = dict(B=8, H=16, N=8192, d=128, n_min=1024, causal=True, seed=21)  # var
 DROPOUT = dict(p=0.1, seed=0x5EED, offset=0)  # dropout on P over the forward+backward workload
 FP8 = dict(incoherent=True, seed=0xF8)          # FP8 forward over the forward workload
 BIAS = dict(seed=0xB1A5)  # additive bias [1, H, N, N] (shared by the batch), 2 N(0, 1) in bf16
+GQA = dict(H_kv=4)  # grouped query heads: the forward+backward workload with 4 K/V heads
 GEMM = dict(n=8192, seed=0x6E, reps=10)  # plain bf16 GEMM on random data: the sustained MFMA rate
 
 
@@ -52,7 +53,7 @@ def log(msg: str) -> None:
 KERNEL_SOURCES = {"fwd": ["fa_fwd.hip", "fa_device.h"], "bwd": ["fa_bwd.hip", "fa_device.h"],
                   "decode": ["fa_decode.hip", "fa_device.h"]}
 KERNEL_FAMILY = {"fwd": "fwd", "fwd_varlen": "fwd", "fwd_dropout": "fwd", "fwd_bias": "fwd",
-                 "fwd_dv64": "fwd",
+                 "fwd_dv64": "fwd", "fwd_gqa": "fwd",
                  "bwd_preprocess": "bwd", "bwd_dkdv": "bwd", "bwd_dq": "bwd",
                  "decode": "decode", "decode_paged_gqa": "decode"}
 TRAFFIC_KEY = {"decode": "decode_split", "decode_paged_gqa": "decode_paged_mfma",
@@ -425,6 +426,34 @@ def main() -> int:
     kernels["fwd_dv64"] = mfma_entry(f_dv, dvf_ms, dvnote)
     kernels["bwd_dv64"] = mfma_entry(2.5 * f_dv, dvb_ms, dvnote + "; preprocess + dK/dV + dQ")
     del vsmall, dosmall, o64, dv64
+
+    # ---- grouped query heads: the forward + backward workload with H_kv = 4 (4 query heads per
+    # K/V head; K and V are the first 4 heads of the workload's), timed on its own
+    Hkv = GQA["H_kv"]
+    kg, vg = k[:, :Hkv].contiguous(), v[:, :Hkv].contiguous()
+    dkg, dvg = torch.empty_like(kg), torch.empty_like(vg)
+    run_gf = lambda: fa.fwd_gqa(q, kg, vg, causal=causal, out=(o, lse))  # noqa: E731
+    run_gb = lambda: fa.bwd_gqa(q, kg, vg, o, lse, do, causal=causal, workspace=ws,  # noqa: E731
+                                out=(dq, dkg, dvg))
+    for _ in range(max(args.warmup, 3)):
+        run_gf()
+        run_gb()
+    torch.cuda.synchronize()
+    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in gev:
+        e[0].record()
+        run_gf()
+        e[1].record()
+        run_gb()
+        e[2].record()
+    torch.cuda.synchronize()
+    gf_ms = sum(e[0].elapsed_time(e[1]) for e in gev) / len(gev)
+    gb_ms = sum(e[1].elapsed_time(e[2]) for e in gev) / len(gev)
+    log(f"grouped query heads fwd {gf_ms:.3f} ms, bwd {gb_ms:.3f} ms (H_kv = {Hkv})")
+    gnote = f"causal B{B} H{H} N{N} d{d} with {Hkv} K/V heads ({H // Hkv} query heads each)"
+    kernels["fwd_gqa"] = mfma_entry(f_fwd, gf_ms, gnote)
+    kernels["bwd_gqa"] = mfma_entry(f_bwd, gb_ms, gnote + "; preprocess + dK/dV + dQ")
+    del kg, vg, dkg, dvg
 
     # ---- FP8 forward with incoherent processing (rotation + quantization + attention on the
     # codes), the forward workload again, timed on its own

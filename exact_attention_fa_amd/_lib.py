@@ -33,6 +33,9 @@ SIGNATURES = {
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_fwd_dv": (_I, [_P] * 5 + [_I] * 6 + [_F, _I, _P]),
     "fa_bwd_dv": (_I, [_P] * 10 + [_Z] + [_I] * 6 + [_F, _I, _P]),
+    "fa_fwd_gqa": (_I, [_P] * 5 + [_I] * 6 + [_F, _I, _P]),
+    "fa_bwd_gqa": (_I, [_P] * 10 + [_Z] + [_I] * 6 + [_F, _I, _P]),
+    "fa_bwd_gqa_workspace_bytes": (_Z, [_I] * 6),
     "fa_fwd_bias": (_I, [_P] * 6 + [_I64] * 3 + [_I] * 5 + [_F, _I, _P]),
     "fa_bwd_bias": (_I, [_P] * 10 + [_I64] * 3 + [_P, _Z] + [_I] * 5 + [_F, _I, _P]),
     "fa_fwd_fp8_workspace_bytes": (_Z, [_I] * 5),
@@ -536,4 +539,58 @@ def bwd_dv(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = No
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           B, H, Nq, Nk, d, dv_, _scale(scale, d), int(bool(causal)), _stream(q))
     _check("fa_bwd_dv", st)
+    return dq, dk, dv
+
+
+def fwd_gqa(q, k, v, causal: bool = False, scale: float | None = None, out=None):
+    """Forward with grouped query heads: q [B,H,Nq,d], k/v [B,H_kv,Nk,d] (H a multiple of H_kv;
+    query head h reads K/V head h // (H // H_kv)) -> (o [B,H,Nq,d] bf16, lse [B,H,Nq] fp32)."""
+    import torch
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _need(q, "q", (B, H, Nq, d), torch.bfloat16)
+    _need(k, "k", (B, Hkv, Nk, d), torch.bfloat16)
+    _need(v, "v", (B, Hkv, Nk, d), torch.bfloat16)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _need(o, "o", (B, H, Nq, d), torch.bfloat16)
+        _need(lse, "lse", (B, H, Nq), torch.float32)
+    st = load().fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           B, H, Hkv, Nq, Nk, d, _scale(scale, d), int(bool(causal)), _stream(q))
+    _check("fa_fwd_gqa", st)
+    return o, lse
+
+
+def bwd_gqa_workspace_bytes(B: int, H: int, H_kv: int, Nq: int, Nk: int, d: int) -> int:
+    """Workspace bytes of bwd_gqa (more than bwd's when the dK/dV pass keeps partial rows)."""
+    return int(load().fa_bwd_gqa_workspace_bytes(B, H, H_kv, Nq, Nk, d))
+
+
+def bwd_gqa(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+            workspace=None, out=None):
+    """Gradients (dq, dk, dv) of fwd_gqa; dk, dv [B,H_kv,Nk,d] sum over each group's query
+    heads."""
+    import torch
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    for t, n, shp in ((q, "q", (B, H, Nq, d)), (k, "k", (B, Hkv, Nk, d)),
+                      (v, "v", (B, Hkv, Nk, d)), (o, "o", (B, H, Nq, d)),
+                      (dout, "dout", (B, H, Nq, d))):
+        _need(t, n, shp, torch.bfloat16)
+    _need(lse, "lse", (B, H, Nq), torch.float32)
+    nbytes = bwd_gqa_workspace_bytes(B, H, Hkv, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    st = load().fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           B, H, Hkv, Nq, Nk, d, _scale(scale, d), int(bool(causal)), _stream(q))
+    _check("fa_bwd_gqa", st)
     return dq, dk, dv

@@ -77,7 +77,7 @@ fa_status bwd_checked(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, cons
                       int N_q, int N_k, int d, float scale, int causal, hipStream_t stream,
                       unsigned need, unsigned phases, const int32_t* lens_q = nullptr,
                       const int32_t* lens_k = nullptr, const fa::DropoutParams* drop = nullptr,
-                      const fa::BiasParams* bias = nullptr, int d_v = 0) {
+                      const fa::BiasParams* bias = nullptr, int d_v = 0, int H_kv = 0) {
   const bool varlen = lens_q != nullptr;
   const bool use_o = need & 1u, use_qkv = need & 2u, use_kv_out = need & 4u, use_q_out = need & 8u;
   if (!dout || (use_o && (!o || !lse)) || (use_qkv && (!q || !k || !v)) ||
@@ -100,6 +100,7 @@ fa_status bwd_checked(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, cons
   if (drop) a.drop = *drop;
   if (bias) a.bias = *bias;
   a.d_v = d_v;
+  a.Hkv = H_kv;
   return from_hip(fa::launch_bwd(a, phases));
 }
 
@@ -419,6 +420,40 @@ fa_status fa_bwd_varlen(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, co
   if (!lens_ok(seq_lens_q) || !lens_ok(seq_lens_k)) return FA_ERR_ALIGN;
   return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N_q,
                      N_k, d, scale, causal, stream, 15u, 7u, seq_lens_q, seq_lens_k);
+}
+
+fa_status fa_fwd_gqa(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+                     int B, int H, int H_kv, int N_q, int N_k, int d, float scale, int causal,
+                     hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status s = check_common(B, H, N_q, N_k, d, scale, causal);
+  if (s != FA_OK) return s;
+  if (H_kv < 1 || H % H_kv != 0) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a{bf(q), bf(k), bf(v), bf(o), lse, B, H, N_q, N_k, d, scale, causal != 0, stream};
+  a.Hkv = H_kv;
+  return from_hip(fa::launch_fwd(a));
+}
+
+size_t fa_bwd_gqa_workspace_bytes(int B, int H, int H_kv, int N_q, int N_k, int d) {
+  const size_t base = fa_bwd_workspace_bytes(B, H, N_q, N_k, d);
+  if (base == 0 || H_kv < 1 || H % H_kv != 0 || N_k < 1 || (d != 64 && d != 128)) return 0;
+  if (!fa::bwd_gqa_uses_partials(B, H, H_kv, N_k)) return base;
+  // fp32 partial rows of dK and dV per query head
+  return base + 2 * round_up16((size_t)B * H * N_k * d * sizeof(float));
+}
+
+fa_status fa_bwd_gqa(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                     const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+                     void* workspace, size_t workspace_bytes, int B, int H, int H_kv, int N_q,
+                     int N_k, int d, float scale, int causal, hipStream_t stream) {
+  if (H_kv < 1 || (H >= 1 && H % H_kv != 0)) return FA_ERR_ARG;
+  const size_t need = fa_bwd_gqa_workspace_bytes(B, H, H_kv, N_q, N_k, d);
+  if (need != 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N_q,
+                     N_k, d, scale, causal, stream, 15u, 7u, nullptr, nullptr, nullptr, nullptr,
+                     0, H_kv);
 }
 
 }  // extern "C"

@@ -28,6 +28,7 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace fa {
@@ -105,15 +106,19 @@ __device__ __forceinline__ void store_zero_row(bf16* dst_row, int hi) {
     for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(dst_row + db * 32 + 8 * j + 4 * hi) = z;
 }
 
-__device__ __forceinline__ void xcd_map(int bid, int BH, int& bh, int& rank) {
-  if ((BH & 7) == 0) {
-    const int xcd = bid & 7, local = bid >> 3, per = BH >> 3;
-    bh = (local % per) * 8 + xcd;
-    rank = local / per;
-  } else {
-    bh = bid % BH;
-    rank = bid / BH;
-  }
+// The same rows in fp32 (partial sums that a later kernel adds up); live = false stores zeros.
+template <int D>
+__device__ __forceinline__ void store_row_f32(float* dst_row, const f32x16 (&acc)[D / 32],
+                                              float mul, bool live, int hi) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = live ? acc[db][4 * j + e] * mul : 0.f;
+      *reinterpret_cast<f32x4*>(dst_row + db * 32 + 8 * j + 4 * hi) = w;
+    }
 }
 
 // Per-lane base offset of the ds_read_b64_tr_b16 pair that assembles a transposed 16-row x
@@ -192,8 +197,9 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLs, const float* __restrict__ ND,
     bf16* __restrict__ dK, bf16* __restrict__ dV, const int* __restrict__ lens_q,
-    const int* __restrict__ lens_k, int BH, int H, int Nq, int Nk, float c, float scale,
-    DropoutParams drop, BiasParams bias) {
+    const int* __restrict__ lens_k, int BH, int H, int G, int GL, float* __restrict__ pK,
+    float* __restrict__ pV, int Nq, int Nk, float c, float scale, DropoutParams drop,
+    BiasParams bias) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using SM = DkdvLds<D, DV>;
   constexpr int ST = SM::ST, STO = SM::STO;
@@ -208,19 +214,28 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
-  int bh, rank;
-  xcd_map(blockIdx.x, BH, bh, rank);
+  // The workgroup's unit u and key tile: query heads u GL .. u GL + GL - 1, which read K/V head
+  // kvbh = u GL / G (G query heads per K/V head; G = 1 without grouped query heads). With
+  // GL = G the unit is the whole group and the K/V gradients sum over its heads here; with
+  // GL = 1 (pK != nullptr) each query head's contribution goes to fp32 partial rows pK, pV
+  // (row bh of [B H, N_k]) that bwd_gqa_reduce_kernel adds up.
+  int u, rank;
+  xcd_map(blockIdx.x, BH / GL, G / GL, u, rank);
+  const int kvbh = u * GL / G;
+  const int bseq = u * GL / H;  // batch index
   const int k0 = rank * kBKV;  // causal: low key tiles see the most queries and go first
   const int kw = k0 + wave * 32;
   const int key = kw + l32;
-  const int nq = VL ? min(max(lens_q[bh / H], 0), Nq) : Nq;  // valid lengths of this sequence
-  const int nk = VL ? min(max(lens_k[bh / H], 0), Nk) : Nk;
+  const int nq = VL ? min(max(lens_q[bseq], 0), Nq) : Nq;  // valid lengths of this sequence
+  const int nk = VL ? min(max(lens_k[bseq], 0), Nk) : Nk;
   const int shift = nk - nq;  // causal: key j visible to query i iff j <= i + shift
 
-  const bf16* Qh = Q + (size_t)bh * Nq * D;
-  const bf16* dOh = dO + (size_t)bh * Nq * DV;
-  const float* Lh = NLs + (size_t)bh * Nq;
-  const float* Dh = ND + (size_t)bh * Nq;
+  // the query head being streamed, and its rows (set per head below)
+  int bh = u * GL;
+  const bf16* Qh = Q;
+  const bf16* dOh = dO;
+  const float* Lh = NLs;
+  const float* Dh = ND;
 
   // resident B operands: K^T and V^T columns (lane = key, 8 dims per k-step)
   bf16x8 kf[D / 16], vf[DV / 16];
@@ -229,8 +244,8 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
     for (int ks = 0; ks < D / 16; ++ks) {
       u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
       if (key < nk) {
-        a = ld16(K + ((size_t)bh * Nk + key) * D + ks * 16 + hi * 8);
-        b = ld16(V + ((size_t)bh * Nk + key) * D + ks * 16 + hi * 8);
+        a = ld16(K + ((size_t)kvbh * Nk + key) * D + ks * 16 + hi * 8);
+        b = ld16(V + ((size_t)kvbh * Nk + key) * D + ks * 16 + hi * 8);
       }
       kf[ks] = as_bf16x8(a);
       vf[ks] = as_bf16x8(b);
@@ -239,13 +254,13 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       u32x4 a = {0u, 0u, 0u, 0u};
-      if (key < nk) a = ld16(K + ((size_t)bh * Nk + key) * D + ks * 16 + hi * 8);
+      if (key < nk) a = ld16(K + ((size_t)kvbh * Nk + key) * D + ks * 16 + hi * 8);
       kf[ks] = as_bf16x8(a);
     }
 #pragma unroll
     for (int ks = 0; ks < DV / 16; ++ks) {
       u32x4 b = {0u, 0u, 0u, 0u};
-      if (key < nk) b = ld16(V + ((size_t)bh * Nk + key) * DV + ks * 16 + hi * 8);
+      if (key < nk) b = ld16(V + ((size_t)kvbh * Nk + key) * DV + ks * 16 + hi * 8);
       vf[ks] = as_bf16x8(b);
     }
   }
@@ -300,8 +315,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   // (x = l32 & 7, group g = l32 >> 3, hi) loads 16 bytes, the 8 keys of its group, of query rows
   // 8 hi + x and 16 + 8 hi + x of the block; an 8 x 8 transpose of 16-bit values inside each
   // group of 8 lanes then hands lane x its key's values of those 8 + 8 rows, as bf16 pairs.
-  const auto brs = bias_rsrc(
-      bias.ptr + (long long)(bh / H) * bias.sb + (long long)(bh % H) * bias.sh, Nq, Nk, bias.sq);
+  auto brs = bias_rsrc(bias.ptr, Nq, Nk, bias.sq);  // set per query head below
   auto load_bias = [&](int t, int qb, u32x4 (&raw)[2]) {
     const int kg = kw + 8 * (l32 >> 3);  // first key of the lane's group
 #pragma unroll
@@ -546,34 +560,98 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   using BT = std::integral_constant<bool, true>;
   using BF = std::integral_constant<bool, false>;
 
-  if (t0 < t1) copy(t0, buf0);
-  // buffer of tile t: (t - t0) & 1
-  int t = t0;
-  for (; t + 1 < tm; t += 2) {
-    step(I0(), BT(), t);
-    step(I1(), BT(), t + 1);
+  for (int g = 0; g < GL; ++g) {
+    bh = u * GL + g;
+    Qh = Q + (size_t)bh * Nq * D;
+    dOh = dO + (size_t)bh * Nq * DV;
+    Lh = NLs + (size_t)bh * Nq;
+    Dh = ND + (size_t)bh * Nq;
+    if constexpr (BIAS)
+      brs = bias_rsrc(bias.ptr + (long long)(bh / H) * bias.sb + (long long)(bh % H) * bias.sh,
+                      Nq, Nk, bias.sq);
+    if (g > 0) __syncthreads();  // every wave is done with the previous head's last tile
+    if (t0 < t1) copy(t0, buf0);
+    // buffer of tile t: (t - t0) & 1
+    int t = t0;
+    for (; t + 1 < tm; t += 2) {
+      step(I0(), BT(), t);
+      step(I1(), BT(), t + 1);
+    }
+    if (t < tm) {
+      step(I0(), BT(), t);
+      ++t;
+      if (t < t1) step(I1(), BF(), t++);
+    }
+    for (; t + 1 < t1; t += 2) {
+      step(I0(), BF(), t);
+      step(I1(), BF(), t + 1);
+    }
+    if (t < t1) step(I0(), BF(), t);
   }
-  if (t < tm) {
-    step(I0(), BT(), t);
-    ++t;
-    if (t < t1) step(I1(), BF(), t++);
-  }
-  for (; t + 1 < t1; t += 2) {
-    step(I0(), BF(), t);
-    step(I1(), BF(), t + 1);
-  }
-  if (t < t1) step(I0(), BF(), t);
 
   // (in a one-gradient mode the other gradient's products are dead code and compile away)
-  if (key < nk) {
-    if (MODE != kDvOnly) store_row<D>(dK + ((size_t)bh * Nk + key) * D, dk, scale, hi);
+  // one query head's partial rows: the plain variant only (the launcher passes pK = nullptr to
+  // every other one)
+  constexpr bool kPartialOk = MODE == kDkDv && !VL && !DROP && !BIAS && D == DV;
+  if (kPartialOk && pK != nullptr) {
+    if (key < Nk) {
+      const bool live = key < nk;
+      store_row_f32<D>(pK + ((size_t)bh * Nk + key) * D, dk, scale, live, hi);
+      store_row_f32<DV>(pV + ((size_t)bh * Nk + key) * DV, dv, 1.f, live, hi);
+    }
+  } else if (key < nk) {
+    if (MODE != kDvOnly) store_row<D>(dK + ((size_t)kvbh * Nk + key) * D, dk, scale, hi);
     if (MODE != kDkOnly)
-      store_row<DV>(dV + ((size_t)bh * Nk + key) * DV, dv, DROP ? drop.inv_keep : 1.f, hi);
+      store_row<DV>(dV + ((size_t)kvbh * Nk + key) * DV, dv, DROP ? drop.inv_keep : 1.f, hi);
   } else if (VL && key < Nk) {  // padding keys
-    store_zero_row<D>(dK + ((size_t)bh * Nk + key) * D, hi);
-    store_zero_row<DV>(dV + ((size_t)bh * Nk + key) * DV, hi);
+    store_zero_row<D>(dK + ((size_t)kvbh * Nk + key) * D, hi);
+    store_zero_row<DV>(dV + ((size_t)kvbh * Nk + key) * DV, hi);
   }
 #endif
+}
+
+// ---------------------------------------------------------------------------------------------
+// 2b. Grouped query heads with partial rows: dK, dV of K/V head kvbh = the sums of the fp32
+// partial rows of its G query heads kvbh G .. kvbh G + G - 1, in that order, rounded to bf16.
+// HBM-bound: each thread reads 8 elements of G rows of pK and pV and writes 16 bytes of each.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_gqa_reduce_kernel(const float* __restrict__ pK,
+                                                             const float* __restrict__ pV,
+                                                             bf16* __restrict__ dK,
+                                                             bf16* __restrict__ dV, int G, int Nk,
+                                                             long long rows) {
+  constexpr int LPR = D / 8;  // threads per row
+  for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < rows * LPR;
+       idx += (long long)gridDim.x * 256) {
+    const long long row = idx / LPR;
+    const int c8 = (int)(idx % LPR) * 8;
+    const long long kvbh = row / Nk, j = row % Nk;
+    float sk[8], sv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sk[e] = sv[e] = 0.f;
+    for (int g = 0; g < G; ++g) {
+      const size_t off = ((size_t)(kvbh * G + g) * Nk + j) * D + c8;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(pK + off);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(pK + off + 4);
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(pV + off);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(pV + off + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sk[e] += a0[e];
+        sk[4 + e] += a1[e];
+        sv[e] += b0[e];
+        sv[4 + e] += b1[e];
+      }
+    }
+    u32x4 wk, wv;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wk[w] = pack_bf16x2(sk[2 * w], sk[2 * w + 1]);
+      wv[w] = pack_bf16x2(sv[2 * w], sv[2 * w + 1]);
+    }
+    st16(dK + row * D + c8, wk);
+    st16(dV + row * D + c8, wv);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -593,7 +671,8 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLs, const float* __restrict__ ND,
     bf16* __restrict__ dQ, const int* __restrict__ lens_q, const int* __restrict__ lens_k,
-    int BH, int H, int Nq, int Nk, float c, float scale, DropoutParams drop, BiasParams bias) {
+    int BH, int H, int G, int Nq, int Nk, float c, float scale, DropoutParams drop,
+    BiasParams bias) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using SM = DqLds<D, DV>;
   // one array per buffer: the LDS copies into one buffer then provably do not alias the reads of
@@ -606,9 +685,9 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
-  int bh, rank;
-  xcd_map(blockIdx.x, BH, bh, rank);
   const int nqt = (Nq + kBR - 1) / kBR;
+  int bh, rank;
+  xcd_map(blockIdx.x, BH, G, bh, rank);
   const int qt = CAUSAL ? nqt - 1 - rank : rank;
   const int q0 = qt * kBR;
   const int qw = q0 + wave * 32;
@@ -617,8 +696,8 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   const int nk = VL ? min(max(lens_k[bh / H], 0), Nk) : Nk;
   const int shift = nk - nq;
 
-  const bf16* Kh = K + (size_t)bh * Nk * D;
-  const bf16* Vh = V + (size_t)bh * Nk * DV;
+  const bf16* Kh = K + (size_t)(bh / G) * Nk * D;  // K/V head of this query head
+  const bf16* Vh = V + (size_t)(bh / G) * Nk * DV;
 
   // resident B operands: Q^T and dO^T columns (lane = query)
   bf16x8 qf[D / 16], dof[DV / 16];
@@ -845,21 +924,38 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  const int G = a.Hkv ? a.H / a.Hkv : 1;  // query heads per K/V head
+  // grouped query heads with too few K/V workgroups to fill the chip: one workgroup per query
+  // head and fp32 partial rows in the workspace, summed by a second kernel
+  constexpr bool split = (DROP || BIAS) && D == 128;
+  const bool partial =
+      !split && !VL && !DROP && !BIAS && D == DV && bwd_gqa_uses_partials(a.B, a.H, a.H / G, a.Nk);
+  const int GL = partial ? 1 : G;
+  float* pK = partial ? a.delta + bwd_part_offset(a.B, a.H, a.Nq) : nullptr;
+  float* pV = partial ? pK + (size_t)BH * a.Nk * D : nullptr;
   if (phases & 2u) {
-    const long long grid = (long long)BH * ((a.Nk + kBKV - 1) / kBKV);
+    const long long grid = (long long)(BH / GL) * ((a.Nk + kBKV - 1) / kBKV);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    constexpr bool split = (DROP || BIAS) && D == 128;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, split ? kDvOnly : kDkDv, BIAS, DV>),
                        dim3((unsigned)grid), dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, nls,
-                       a.delta, a.dk, a.dv, a.lens_q, a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale,
+                       a.delta, a.dk, a.dv, a.lens_q, a.lens_k, BH, a.H, G, GL, pK, pV, a.Nq, a.Nk, c, a.scale,
                        a.drop, a.bias);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (split) {
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, kDkOnly, BIAS, DV>),
                          dim3((unsigned)grid), dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, nls,
-                         a.delta, a.dk, a.dv, a.lens_q, a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale,
+                         a.delta, a.dk, a.dv, a.lens_q, a.lens_k, BH, a.H, G, GL, pK, pV, a.Nq, a.Nk, c, a.scale,
                          a.drop, a.bias);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (partial) {
+      const long long rows = (long long)(BH / G) * a.Nk;
+      const long long threads = rows * (D / 8);
+      const int rgrid = (int)std::min<long long>((threads + 255) / 256, 8192);
+      hipLaunchKernelGGL((bwd_gqa_reduce_kernel<D>), dim3(rgrid), dim3(256), 0, a.stream, pK, pV,
+                         a.dk, a.dv, G, a.Nk, rows);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -869,7 +965,7 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VL, DROP, BIAS, DV>), dim3((unsigned)grid),
                        dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, nls, a.delta, a.dq, a.lens_q,
-                       a.lens_k, BH, a.H, a.Nq, a.Nk, c, a.scale, a.drop, a.bias);
+                       a.lens_k, BH, a.H, G, a.Nq, a.Nk, c, a.scale, a.drop, a.bias);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -877,6 +973,16 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
 }
 
 }  // namespace
+
+bool bwd_gqa_uses_partials(int B, int H, int Hkv, int Nk) {
+  // fewer than 8 workgroups per CU (256 CUs) with one workgroup per K/V head and key tile:
+  // one per query head instead, and the group sums formed by a second pass
+  if (Hkv <= 0 || Hkv >= H) return false;
+  const long long wgs = (long long)B * Hkv * ((Nk + kBKV - 1) / kBKV);
+  return wgs < 2048;
+}
+
+size_t bwd_part_offset(int B, int H, int Nq) { return 2 * bwd_lse2_offset(B, H, Nq); }
 
 size_t bwd_lse2_offset(int B, int H, int Nq) {
   // nD first, then nLs, each padded to a multiple of 16 bytes (counted in floats)

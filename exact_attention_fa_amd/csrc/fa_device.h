@@ -179,6 +179,26 @@ __device__ __forceinline__ bf16x8 lds_read_transposed(const unsigned char* tile,
   return concat_s16x4(lo, hi);
 }
 
+// ---- workgroup -> (head, tile rank) -------------------------------------------------------
+// For a grid of BH * nt workgroups over BH query heads that come in groups of G consecutive heads
+// sharing one K/V head (G = 1: every head has its own). Workgroups are dealt to the 8 XCDs round
+// robin (XCD = blockIdx & 7), each XCD with its own L2. With the number of K/V heads BH / G a
+// multiple of 8, XCD x serves the query heads of K/V heads x, x + 8, ... only, so all tiles that
+// read one K/V head meet in one L2; inside an XCD the workgroups go rank by rank (rank 0 first:
+// the longest tiles of the causal kernels).
+__device__ __forceinline__ void xcd_map(int bid, int BH, int G, int& bh, int& rank) {
+  const int BHkv = BH / G;
+  if ((BHkv & 7) == 0) {
+    const int xcd = bid & 7, local = bid >> 3, per = (BHkv >> 3) * G;  // query heads per XCD
+    rank = local / per;
+    const int rem = local - rank * per;
+    bh = ((rem / G) * 8 + xcd) * G + rem % G;
+  } else {
+    bh = bid % BH;
+    rank = bid / BH;
+  }
+}
+
 // ---- HBM/L2 -> LDS copies without register staging ------------------------------------------
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes return zero.
 // Word 3 is the gfx9-family raw-buffer configuration (32-bit data format, no swizzle).

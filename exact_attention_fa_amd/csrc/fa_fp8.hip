@@ -264,15 +264,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
 
   const int nqt = (Nq + BR - 1) / BR;
   int bh, rank;
-  const int bid = blockIdx.x;
-  if ((BH & 7) == 0) {
-    const int xcd = bid & 7, local = bid >> 3, per = BH >> 3;
-    bh = (local % per) * 8 + xcd;
-    rank = local / per;
-  } else {
-    bh = bid % BH;
-    rank = bid / BH;
-  }
+  xcd_map(blockIdx.x, BH, 1, bh, rank);
   const int qt = CAUSAL ? nqt - 1 - rank : rank;
   const int q0 = qt * BR;
   const int qw = q0 + wave * 32;

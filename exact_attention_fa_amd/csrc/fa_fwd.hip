@@ -65,12 +65,14 @@ struct FwdLds {
 // Anlamak Bölüm 1", 0.2), read from HBM one tile ahead; -inf entries mask, and a row whose scores
 // are all -inf gets O = 0 and LSE = -inf.
 // DV: head dimension of V and O (the notation's d_v; the same as D unless asked otherwise).
+// G: query heads per K/V head (grouped-query attention; 1 unless asked otherwise): query head bh
+// reads K/V head bh / G, K and V holding BH / G heads.
 template <int D, int DV, int NW, bool CAUSAL, bool VL, bool DROP, bool BIAS>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64) void fwd_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int* __restrict__ lens_q,
-    const int* __restrict__ lens_k, int BH, int H, int Nq, int Nk, float c, DropoutParams drop,
-    BiasParams bias) {
+    const int* __restrict__ lens_k, int BH, int H, int G, int Nq, int Nk, float c,
+    DropoutParams drop, BiasParams bias) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using L = FwdLds<D, DV>;
   constexpr int BR = NW * 32;  // query rows per workgroup
@@ -86,20 +88,11 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // ---- workgroup -> (b*h, query tile): longest causal tiles first; with BH a multiple of 8,
-  // all query tiles of one head go to one XCD (workgroups are dealt to the 8 XCDs round robin),
-  // so that head's K/V stays in that XCD's L2.
+  // ---- workgroup -> (b*h, query tile): longest causal tiles first, all tiles that read one K/V
+  // head on one XCD (xcd_map).
   const int nqt = (Nq + BR - 1) / BR;
   int bh, rank;
-  const int bid = blockIdx.x;
-  if ((BH & 7) == 0) {
-    const int xcd = bid & 7, local = bid >> 3, per = BH >> 3;
-    bh = (local % per) * 8 + xcd;
-    rank = local / per;
-  } else {
-    bh = bid % BH;
-    rank = bid / BH;
-  }
+  xcd_map(blockIdx.x, BH, G, bh, rank);
   const int qt = CAUSAL ? nqt - 1 - rank : rank;
   const int q0 = qt * BR;
   const int qw = q0 + wave * 32;  // first query row of this wave
@@ -110,8 +103,8 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
   const int shift = nk - nq;      // causal: key j visible to query i iff j <= i + shift
 
   const bf16* Qh = Q + (size_t)bh * Nq * D;
-  const bf16* Kh = K + (size_t)bh * Nk * D;
-  const bf16* Vh = V + (size_t)bh * Nk * DV;
+  const bf16* Kh = K + (size_t)(bh / G) * Nk * D;  // K/V head of this query head
+  const bf16* Vh = V + (size_t)(bh / G) * Nk * DV;
 
   int kend = nk;
   if (CAUSAL) kend = min(nk, min(q0 + BR, nq) + shift);
@@ -372,7 +365,7 @@ hipError_t launch(const FwdArgs& a) {
   const float c = a.scale * kLog2e;
   hipLaunchKernelGGL((fwd_kernel<D, DV, NW, CAUSAL, VL, DROP, BIAS>), dim3((unsigned)grid),
                      dim3(NW * 64), 0, a.stream, a.q, a.k, a.v, a.o, a.lse, a.lens_q, a.lens_k,
-                     a.B * a.H, a.H, a.Nq, a.Nk, c, a.drop, a.bias);
+                     a.B * a.H, a.H, a.Hkv ? a.H / a.Hkv : 1, a.Nq, a.Nk, c, a.drop, a.bias);
   return hipGetLastError();
 }
 

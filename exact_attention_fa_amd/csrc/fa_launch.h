@@ -36,6 +36,7 @@ struct FwdArgs {
   DropoutParams drop{};
   BiasParams bias{};
   int d_v = 0;  // head dimension of V and O; 0: the same as d
+  int Hkv = 0;  // key/value heads (H a multiple of Hkv); 0: the same as H
 };
 
 struct BwdArgs {
@@ -58,6 +59,7 @@ struct BwdArgs {
   DropoutParams drop{};
   BiasParams bias{};
   int d_v = 0;  // head dimension of V, O, dO and dV; 0: the same as d
+  int Hkv = 0;  // key/value heads of K, V, dK and dV (H a multiple of Hkv); 0: the same as H
 };
 
 struct DecodeArgs {
@@ -121,6 +123,11 @@ hipError_t launch_fwd_fp8(const Fp8Args& a);
 hipError_t launch_fwd(const FwdArgs& a);
 // Offset (in floats) of L2 after D in the backward workspace.
 size_t bwd_lse2_offset(int B, int H, int Nq);
+// Grouped query heads: whether the dK/dV pass runs one workgroup per query head and sums fp32
+// partial rows in a second kernel (too few K/V workgroups otherwise), and where those rows start
+// in the workspace (floats; [B H, N_k, d] for dK, then the same for dV).
+bool bwd_gqa_uses_partials(int B, int H, int Hkv, int Nk);
+size_t bwd_part_offset(int B, int H, int Nq);
 // Backward phases; `phase_mask` bit 0 = D preprocess, bit 1 = dK/dV, bit 2 = dQ.
 hipError_t launch_bwd(const BwdArgs& a, unsigned phase_mask = 7u);
 hipError_t launch_decode(const DecodeArgs& a);

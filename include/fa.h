@@ -128,6 +128,29 @@ fa_status fa_bwd_dv(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const 
                     void* workspace, size_t workspace_bytes, int B, int H, int N_q, int N_k, int d,
                     int d_v, float scale, int causal, hipStream_t stream);
 
+/* ---- Grouped query heads in the forward and backward passes ------------------------------------
+ *
+ * Page "Bellek Duvarının Fiziği", section "Duvarın Ötesi: KV Cache, Uzun Bağlam ve Yaklaşık
+ * Attention" names query heads that share key/value heads (GQA/MQA) without defining them; the
+ * definition used here is the decode's (below): H query heads, H_kv key/value heads, H a multiple
+ * of H_kv (else FA_ERR_ARG), query head h attends with key/value head h / (H / H_kv). Layouts as
+ * for fa_fwd / fa_bwd except k, v, dk, dv [B,H_kv,N_k,d]; dk and dv of a key/value head are the
+ * sums of the gradients its H / H_kv query heads send to it, formed in a fixed order without
+ * atomics (a dK/dV workgroup of a key/value head visits its query heads in turn).
+ * H_kv = H is fa_fwd / fa_bwd. When the K/V heads times the 128-key tiles are too few to fill
+ * the GPU (fewer than 2048), the dK/dV pass runs one workgroup per query head instead and keeps
+ * fp32 partial rows in the workspace that a second kernel sums over each group, in head order;
+ * fa_bwd_gqa_workspace_bytes (0 for invalid sizes) covers both cases.
+ */
+size_t fa_bwd_gqa_workspace_bytes(int B, int H, int H_kv, int N_q, int N_k, int d);
+fa_status fa_fwd_gqa(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+                     int B, int H, int H_kv, int N_q, int N_k, int d, float scale, int causal,
+                     hipStream_t stream);
+fa_status fa_bwd_gqa(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                     const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+                     void* workspace, size_t workspace_bytes, int B, int H, int H_kv, int N_q,
+                     int N_k, int d, float scale, int causal, hipStream_t stream);
+
 /* ---- Additive bias on the scores --------------------------------------------------------------
  *
  * "FlashAttention'ı Anlamak Bölüm 1", notation 0.2: S = Q K^T / sqrt(d) + B with B an optional

@@ -30,6 +30,9 @@ Readings where the pages are silent (each also listed in the design notes):
   * the stored statistic is the natural-log log-sum-exp of the scaled, masked scores,
     L_i = ln sum_j exp(S_ij);
   * d_v = d;
+  * grouped query heads: H query heads, H_kv key/value heads, H a multiple of H_kv, query head
+    h attends with key/value head h // (H // H_kv); dK and dV of a key/value head are the sums
+    of the gradients its query heads send to it;
   * a batch of different-length sequences (padded tensors plus per-sequence lengths) is the
     single-sequence definition applied to each sequence's own rows and keys, causal alignment
     per sequence; a row that sees no key (padding, or causal with more queries than keys) has
@@ -155,6 +158,48 @@ def backward(q, k, v, do, scale: float, causal: bool):
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h] = backward_head(q[b, h], k[b, h], v[b, h], do[b, h],
                                                          scale, causal)
+    return dq, dk, dv
+
+
+def kv_head_of(h: int, H: int, H_kv: int) -> int:
+    """Key/value head of query head h with grouped query heads ([MW] "Duvarın Ötesi: KV Cache,
+    Uzun Bağlam ve Yaklaşık Attention" names GQA/MQA; the reading used throughout: H a multiple
+    of H_kv, consecutive groups of H // H_kv query heads share one key/value head)."""
+    if H_kv < 1 or H % H_kv != 0:
+        raise ValueError("the query head count must be a multiple of the key/value head count")
+    return h // (H // H_kv)
+
+
+def forward_gqa(q, k, v, scale: float, causal: bool):
+    """Forward with grouped query heads: q [B,H,n_q,d], k/v [B,H_kv,n_k,d] -> (o [B,H,n_q,d],
+    lse [B,H,n_q]); each query head is forward_head against its key/value head."""
+    B, H, n_q, _ = np.shape(q)
+    H_kv = np.shape(k)[1]
+    o = np.empty((B, H, n_q, np.shape(v)[3]), dtype=np.float64)
+    lse = np.empty((B, H, n_q), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, H_kv)
+            o[b, h], lse[b, h] = forward_head(q[b, h], k[b, g], v[b, g], scale, causal)
+    return o, lse
+
+
+def backward_gqa(q, k, v, do, scale: float, causal: bool):
+    """Gradients of forward_gqa's o. A key/value head enters the outputs of all query heads of its
+    group, so by the chain rule its dK and dV are the sums of the per-query-head gradients of
+    backward_head ([MW] "Geri Yayılım"); dQ is per query head. Returns (dq, dk, dv) shaped like
+    (q, k, v), fp64."""
+    B, H = np.shape(q)[:2]
+    H_kv = np.shape(k)[1]
+    dq = np.empty(np.shape(q), dtype=np.float64)
+    dk = np.zeros(np.shape(k), dtype=np.float64)
+    dv = np.zeros(np.shape(v), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, H_kv)
+            dq[b, h], gk, gv = backward_head(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal)
+            dk[b, g] += gk
+            dv[b, g] += gv
     return dq, dk, dv
 
 

@@ -762,6 +762,64 @@ def pin_bias_special_cases():
             assert abs(fd - gx[idx]) <= 1e-6 * (1 + abs(fd)), (idx, fd, gx[idx])
 
 
+def _gqa_case(rng, B, H, H_kv, n_q, n_k, d):
+    return (rng.standard_normal((B, H, n_q, d)), rng.standard_normal((B, H_kv, n_k, d)),
+            rng.standard_normal((B, H_kv, n_k, d)), rng.standard_normal((B, H, n_q, d)))
+
+
+def pin_gqa_closed_form():
+    """Grouped query heads: when every V row of key/value head g equals the constant g + 1, each
+    output row of a query head h is a convex combination of identical rows, so it equals
+    h // (H // H_kv) + 1 exactly, whatever the scores (pins the head-to-group mapping); the
+    log-sum-exp of query head h is that of its own row against its group's keys."""
+    rng = _rng(31)
+    for B, H, H_kv, n_q, n_k, d, causal in [(2, 4, 2, 5, 5, 4, True), (1, 6, 3, 3, 7, 8, False),
+                                            (1, 8, 1, 4, 4, 4, True)]:
+        q, k, _, _ = _gqa_case(rng, B, H, H_kv, n_q, n_k, d)
+        v = np.broadcast_to(np.arange(1, H_kv + 1, dtype=np.float64)[None, :, None, None],
+                            (B, H_kv, n_k, d)).copy()
+        o, lse = A.forward_gqa(q, k, v, 0.6, causal)
+        for h in range(H):
+            g = h // (H // H_kv)
+            assert np.max(np.abs(o[:, h] - (g + 1))) <= 1e-12, (h, g)
+            for b in range(B):
+                s = 0.6 * q[b, h] @ k[b, g].T
+                if causal:
+                    s = np.where(np.arange(n_k)[None, :] <= np.arange(n_q)[:, None] + n_k - n_q,
+                                 s, -np.inf)
+                ref = np.log(np.sum(np.exp(s - s.max(1, keepdims=True)), 1)) + s.max(1)
+                np.testing.assert_allclose(lse[b, h], ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_gqa_gradients():
+    """Grouped query heads, backward: central differences of f = sum(dO * O) through the shared
+    K and V (and Q) against backward_gqa; sum_j dK_j = 0 per key/value head and sum_j dV_j =
+    the sum of dO over all rows of the group's query heads."""
+    rng = _rng(32)
+    h = 1e-6
+    q, k, v, do = _gqa_case(rng, 1, 4, 2, 3, 4, 2)
+    for causal in (False, True):
+        dq, dk, dv = A.backward_gqa(q, k, v, do, 0.7, causal)
+        for x, gx in ((q, dq), (k, dk), (v, dv)):
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + h
+                fp = float(np.sum(A.forward_gqa(q, k, v, 0.7, causal)[0] * do))
+                x[idx] = old - h
+                fm = float(np.sum(A.forward_gqa(q, k, v, 0.7, causal)[0] * do))
+                x[idx] = old
+                fd = (fp - fm) / (2 * h)
+                assert abs(fd - gx[idx]) <= 1e-6 * (1 + abs(fd)), (causal, idx, fd, gx[idx])
+    q, k, v, do = _gqa_case(rng, 2, 6, 2, 9, 9, 8)
+    dq, dk, dv = A.backward_gqa(q, k, v, do, 0.5, True)
+    for b in range(2):
+        for g in range(2):
+            assert np.linalg.norm(dk[b, g].sum(axis=0)) <= 1e-11 * (np.linalg.norm(dk[b, g]) + 1)
+            np.testing.assert_allclose(dv[b, g].sum(axis=0),
+                                       do[b, 3 * g:3 * g + 3].sum(axis=(0, 1)), rtol=1e-12,
+                                       atol=1e-12)
+
+
 ALL_PINS = [pin_brute_force_rows, pin_rows_sum_to_one, pin_causal_future_invariance,
             pin_finite_differences, pin_closed_forms, pin_invariances, pin_gradient_sum_rules,
             pin_torch_sdpa, pin_hand_examples, pin_decode_split_combine,
@@ -772,4 +830,4 @@ ALL_PINS = [pin_brute_force_rows, pin_rows_sum_to_one, pin_causal_future_invaria
             pin_dropout_expectation_and_identities, pin_dropout_finite_differences,
             pin_e4m3_against_torch, pin_hadamard_rotation, pin_fp8_quantization,
             pin_fp8_forward_brute_force, pin_fp8_incoherent_claim, pin_bias_brute_force,
-            pin_bias_special_cases]
+            pin_bias_special_cases, pin_gqa_closed_form, pin_gqa_gradients]

@@ -189,6 +189,32 @@ def test_dv_validation(lib):
                          2, 8, 8, 128, 64, 0.125, 0, None) == 6
 
 
+def test_gqa_validation(lib):
+    def fwd(H=4, Hkv=2, q=FAKE, causal=0, nq=8):
+        return lib.fa_fwd_gqa(q, FAKE, FAKE, FAKE, FAKE, 1, H, Hkv, nq, 8, 64, 0.125, causal, None)
+    assert fwd(H=4, Hkv=3) == 8      # H not a multiple of H_kv
+    assert fwd(Hkv=0) == 8
+    assert fwd(H=0) == 2
+    assert fwd(q=None) == 1
+    assert fwd(q=FAKE + 4) == 4
+    assert fwd(causal=1, nq=9) == 5
+    ws = lib.fa_bwd_gqa_workspace_bytes(1, 4, 2, 8, 8, 64)
+    # one K/V tile per head: too few workgroups, so fp32 partial rows of dK and dV per query head
+    assert ws == lib.fa_bwd_workspace_bytes(1, 4, 8, 8, 64) + 2 * 4 * 8 * 64 * 4
+    assert lib.fa_bwd_gqa_workspace_bytes(1, 4, 3, 8, 8, 64) == 0
+    # 8 K/V heads x 256 key tiles = 2048 workgroups: no partial rows
+    assert (lib.fa_bwd_gqa_workspace_bytes(1, 32, 8, 64, 32768, 64)
+            == lib.fa_bwd_workspace_bytes(1, 32, 64, 32768, 64))
+
+    def bwd(H=4, Hkv=2, ws_bytes=ws, d=64):
+        return lib.fa_bwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              ws_bytes, 1, H, Hkv, 8, 8, d, 0.125, 0, None)
+    assert bwd(Hkv=3) == 8
+    assert bwd(Hkv=0) == 8
+    assert bwd(ws_bytes=ws - 16) == 6
+    assert bwd(d=96) == 3
+
+
 def test_bwd_phase_validation(lib):
     ws = lib.fa_bwd_workspace_bytes(1, 2, 64, 64, 128)
     assert ws == 2 * 2 * 64 * 4

@@ -324,7 +324,41 @@ def _fwd_bias_transposed(q, k, v, bias, scale, causal):
     return _orig_fwd_bias(q, k, v, b, scale, causal)
 
 
+_orig_fwd_gqa = A.forward_gqa
+_orig_bwd_gqa = A.backward_gqa
+
+
+def _fwd_gqa_head_modulo(q, k, v, scale, causal):
+    # query head h paired with key/value head h % H_kv instead of h // (H // H_kv)
+    B, H = np.shape(q)[:2]
+    H_kv = np.shape(k)[1]
+    o = np.empty(np.shape(q))
+    lse = np.empty(np.shape(q)[:3])
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h] = A.forward_head(q[b, h], k[b, h % H_kv], v[b, h % H_kv], scale,
+                                                causal)
+    return o, lse
+
+
+def _bwd_gqa_last_head_only(q, k, v, do, scale, causal):
+    # the group's key/value gradients overwritten by each query head instead of summed
+    B, H = np.shape(q)[:2]
+    H_kv = np.shape(k)[1]
+    dq = np.empty(np.shape(q))
+    dk = np.zeros(np.shape(k))
+    dv = np.zeros(np.shape(v))
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // H_kv)
+            dq[b, h], dk[b, g], dv[b, g] = A.backward_head(q[b, h], k[b, g], v[b, g], do[b, h],
+                                                           scale, causal)
+    return dq, dk, dv
+
+
 MUTANTS = {
+    "gqa_head_modulo_fwd": ("forward_gqa", _fwd_gqa_head_modulo),
+    "gqa_bwd_not_summed": ("backward_gqa", _bwd_gqa_last_head_only),
     "paged_block_and_row_swapped": ("gather_paged", _gather_block_and_row_swapped),
     "paged_ignores_block_table": ("gather_paged", _gather_physical_order),
     "gqa_head_modulo": ("decode_paged", _decode_paged_head_modulo),
