@@ -432,8 +432,10 @@ def main() -> int:
     Hkv = GQA["H_kv"]
     kg, vg = k[:, :Hkv].contiguous(), v[:, :Hkv].contiguous()
     dkg, dvg = torch.empty_like(kg), torch.empty_like(vg)
+    gws = torch.empty(fa.bwd_gqa_workspace_bytes(B, H, Hkv, N, N, d), dtype=torch.uint8,
+                      device=dev)
     run_gf = lambda: fa.fwd_gqa(q, kg, vg, causal=causal, out=(o, lse))  # noqa: E731
-    run_gb = lambda: fa.bwd_gqa(q, kg, vg, o, lse, do, causal=causal, workspace=ws,  # noqa: E731
+    run_gb = lambda: fa.bwd_gqa(q, kg, vg, o, lse, do, causal=causal, workspace=gws,  # noqa: E731
                                 out=(dq, dkg, dvg))
     for _ in range(max(args.warmup, 3)):
         run_gf()
@@ -453,7 +455,7 @@ def main() -> int:
     gnote = f"causal B{B} H{H} N{N} d{d} with {Hkv} K/V heads ({H // Hkv} query heads each)"
     kernels["fwd_gqa"] = mfma_entry(f_fwd, gf_ms, gnote)
     kernels["bwd_gqa"] = mfma_entry(f_bwd, gb_ms, gnote + "; preprocess + dK/dV + dQ")
-    del kg, vg, dkg, dvg
+    del kg, vg, dkg, dvg, gws
 
     # ---- FP8 forward with incoherent processing (rotation + quantization + attention on the
     # codes), the forward workload again, timed on its own
