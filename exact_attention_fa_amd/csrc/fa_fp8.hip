@@ -6,7 +6,8 @@
 //      signs times a Hadamard matrix): outlier coordinates are spread over all coordinates, and
 //      (Q M)(K M)^T = Q K^T because M is orthogonal.
 //   2. Q, K and V are quantized to FP8 with block-wise scales (Q per 32 rows, K per 64 rows, V one
-//      scale per head): scale = amax / 448, code = E4M3(x / scale) after clamping to +-448.
+//      scale per head): scale = amax / 448, code = E4M3(x / scale) after clamping to +-448,
+//      with x / scale evaluated as x times the fp32 reciprocal of the scale.
 //   3. Attention runs on the FP8 codes: S^T = K8 Q8^T on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3
 //      operands, unit block exponents) with the two block scales folded into the softmax
 //      multiply; the probabilities are quantized to E4M3 for O^T = V8^T P8^T on the same
@@ -64,6 +65,19 @@ __device__ __forceinline__ int cvt2_fp8(float a, float b, int w) {
 
 __device__ __forceinline__ float clamp_fp8(float x) { return fminf(fmaxf(x, -kFp8Max), kFp8Max); }
 
+// y = clamp(x * r) with r = 1 / s rounded to fp32; when r overflows (s below 2^-128, a block of
+// subnormal values) the quotient x / s itself. r and s are the same for all lanes of a block.
+__device__ __forceinline__ void scale_by_reciprocal(const float (&x)[8], float s, float r,
+                                                    float (&y)[8]) {
+  if (__builtin_isinf(r)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = clamp_fp8(x[e] / s);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = clamp_fp8(x[e] * r);
+  }
+}
+
 // max over the 256 threads of a workgroup (all threads must call it)
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
@@ -112,11 +126,13 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(
     const uint32_t word = (chunk >> 2) == 0 ? sw[0] : (chunk >> 2) == 1 ? sw[1]
                           : (chunk >> 2) == 2 ? sw[2] : sw[3];
     const uint32_t bits = (word >> (8 * (chunk & 3))) & 0xFFu;  // signs of dims 8 chunk + 0..7
+    uint32_t smask[8];  // sign bit to flip per value
+#pragma unroll
+    for (int e = 0; e < 8; ++e) smask[e] = ((bits >> e) & 1u) << 31;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if ((bits >> e) & 1u) x[p][e] = -x[p][e];
+      for (int e = 0; e < 8; ++e) x[p][e] = __uint_as_float(__float_as_uint(x[p][e]) ^ smask[e]);
       // butterfly stages of span 1, 2, 4 inside the lane
 #pragma unroll
       for (int h = 1; h < 8; h *= 2)
@@ -127,14 +143,14 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(
             x[p][e] = a + b;
             x[p][e + h] = a - b;
           }
-      // spans 8 .. D/2: lane distance 1 .. TPR/2 inside the row's lane group
+      // spans 8 .. D/2: lane distance 1 .. TPR/2 inside the row's lane group; the upper lane
+      // of a pair takes o - x, the lower x + o, both as one exactly rounded fma(x, +-1, o)
 #pragma unroll
-      for (int dist = 1; dist < TPR; dist *= 2)
+      for (int dist = 1; dist < TPR; dist *= 2) {
+        const float sg = (chunk & dist) ? -1.f : 1.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float o = __shfl_xor(x[p][e], dist);
-          x[p][e] = (chunk & dist) ? (o - x[p][e]) : (x[p][e] + o);
-        }
+        for (int e = 0; e < 8; ++e) x[p][e] = fmaf(x[p][e], sg, __shfl_xor(x[p][e], dist));
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[p][e] *= inv_sqrt_d;
     }
@@ -165,14 +181,14 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(
     }
   }
   unsigned char* dst = (kind == 0 ? q8 : k8) + (size_t)bh * N * D;
+  const float rs[2] = {1.f / s[0], 1.f / s[1]};
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = blk * 64 + p * RPP + rsub;
     if (row >= N) continue;
-    const float sc = s[kind == 0 ? (p * RPP) / 32 : 0];
+    const int b = kind == 0 ? (p * RPP) / 32 : 0;
     float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = clamp_fp8(x[p][e] / sc);
+    scale_by_reciprocal(x[p], s[b], rs[b], y);
     u32x2 w;
     w[0] = (uint32_t)cvt2_fp8<true>(y[2], y[3], cvt2_fp8<false>(y[0], y[1], 0));
     w[1] = (uint32_t)cvt2_fp8<true>(y[6], y[7], cvt2_fp8<false>(y[4], y[5], 0));
@@ -186,40 +202,68 @@ template <int D>
 __global__ __launch_bounds__(256) void fp8_prep_v_kernel(
     const bf16* __restrict__ V, const float* __restrict__ vpart, unsigned char* __restrict__ v8t,
     float* __restrict__ sv, int Nk, int nkb64) {
-  constexpr int TPR = D / 8, RPP = 256 / TPR, PASSES = 64 / RPP;
+  constexpr int TPR = D / 8, RPP = 256 / TPR, PASSES = 64 / RPP;  // PASSES: keys per thread
+  static_assert(PASSES == 2 || PASSES == 4, "one 16- or 32-bit LDS word per dimension");
   constexpr int TST = 80;  // tile row stride (bytes): 64 keys + 16, keeps 16-byte row reads aligned
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) unsigned char tile[D * TST];
   const int tid = threadIdx.x, chunk = tid % TPR, rsub = tid / TPR;
   const int bh = blockIdx.x / nkb64, blk = blockIdx.x % nkb64;
+  // this thread's keys are PASSES * rsub + p: its bytes of one dimension form one LDS word.
+  // The row loads are issued before the head-scale reduction so that the two latencies overlap.
+  const bf16* src = V + (size_t)bh * Nk * D;
+  u32x4 w[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int key = blk * 64 + PASSES * rsub + p;
+    w[p] = u32x4{0u, 0u, 0u, 0u};
+    if (key < Nk) w[p] = ld16(src + (size_t)key * D + chunk * 8);
+  }
   float am = 0.f;
   for (int i = tid; i < nkb64; i += 256) am = fmaxf(am, vpart[(size_t)bh * nkb64 + i]);
   am = block_max(am, red);
   const float s = am > 0.f ? am / kFp8Max : 1.f;
+  const float r = 1.f / s;
   if (blk == 0 && tid == 0) sv[bh] = s;
-  const bf16* src = V + (size_t)bh * Nk * D;
+  uint32_t c[PASSES][2];  // E4M3 codes of dimensions 8 chunk + 0..3 and + 4..7 of key p
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
-    const int row = p * RPP + rsub;  // key within the block
-    const int key = blk * 64 + row;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (key < Nk) w = ld16(src + (size_t)key * D + chunk * 8);
-    float y[8];
+    float x[8], y[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      y[2 * i] = clamp_fp8(bf16_lo(w[i]) / s);
-      y[2 * i + 1] = clamp_fp8(bf16_hi(w[i]) / s);
+      x[2 * i] = bf16_lo(w[p][i]);
+      x[2 * i + 1] = bf16_hi(w[p][i]);
     }
-    const uint32_t c0 = (uint32_t)cvt2_fp8<true>(y[2], y[3], cvt2_fp8<false>(y[0], y[1], 0));
-    const uint32_t c1 = (uint32_t)cvt2_fp8<true>(y[6], y[7], cvt2_fp8<false>(y[4], y[5], 0));
+    scale_by_reciprocal(x, s, r, y);
+    c[p][0] = (uint32_t)cvt2_fp8<true>(y[2], y[3], cvt2_fp8<false>(y[0], y[1], 0));
+    c[p][1] = (uint32_t)cvt2_fp8<true>(y[6], y[7], cvt2_fp8<false>(y[4], y[5], 0));
+  }
+  unsigned char* trow = tile + (chunk * 8) * TST + PASSES * rsub;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      tile[(chunk * 8 + e) * TST + row] = (unsigned char)(((e < 4 ? c0 : c1) >> (8 * (e & 3))) & 0xFFu);
+  for (int h = 0; h < 2; ++h) {
+    // byte transpose: lo = [k0.b0, k1.b0, k0.b1, k1.b1], hi = [k0.b2, k1.b2, k0.b3, k1.b3]
+    const uint32_t lo01 = __builtin_amdgcn_perm(c[1][h], c[0][h], 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(c[1][h], c[0][h], 0x07030602u);
+    if constexpr (PASSES == 4) {
+      const uint32_t lo23 = __builtin_amdgcn_perm(c[3][h], c[2][h], 0x05010400u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(c[3][h], c[2][h], 0x07030602u);
+      const uint32_t d[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+                             __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+                             __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
+                             __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) *reinterpret_cast<uint32_t*>(trow + (4 * h + e) * TST) = d[e];
+    } else {
+      const uint32_t d[2] = {lo01, hi01};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<uint16_t*>(trow + (4 * h + e) * TST) = (uint16_t)(d[e >> 1] >> (16 * (e & 1)));
+    }
   }
   __syncthreads();
   const size_t Nkp = (size_t)nkb64 * 64;
-  for (int c = tid; c < D * 4; c += 256) {
-    const int dim = c >> 2, part = c & 3;
+  for (int c4 = tid; c4 < D * 4; c4 += 256) {
+    const int dim = c4 >> 2, part = c4 & 3;
     const u32x4 val = *reinterpret_cast<const u32x4*>(tile + dim * TST + 16 * part);
     st16(v8t + ((size_t)bh * D + dim) * Nkp + (size_t)blk * 64 + 16 * part, val);
   }

@@ -29,8 +29,10 @@ Readings (each also in the design notes):
   * block scales: Q per 32 rows, K per 64 rows, V per head; s = amax / 448 (s = 1 if amax = 0);
     code = E4M3(clamp(x / s, -448, 448)). These decisions are taken in float32 exactly as the
     kernels take them: the rotation runs as the fast Walsh-Hadamard butterfly in float32 (spans
-    1, 2, 4, ..., d/2, each stage (a + b, a - b)), then x (1/sqrt(d) rounded to float32), then the
-    float32 division by s, so every FP8 code matches the kernels' bit for bit;
+    1, 2, 4, ..., d/2, each stage (a + b, a - b)), then x (1/sqrt(d) rounded to float32), then
+    x / s is evaluated as x * r with r = 1 / s rounded to float32 (the pages fix no evaluation
+    order; x / s itself only where r overflows, s < 2^-128), so every FP8 code matches the
+    kernels' bit for bit;
   * probabilities: P = exp(S - m) with m the row maximum of the scores of the dequantized
     Q and K; the P V product uses E4M3(256 P) / 256 (2^8 puts P's range [0, 1] into E4M3's
     normal range); O = sum_j P^_j V^_j / sum_j P_j (normaliser from the unquantized P);
@@ -127,7 +129,10 @@ def quantize_rows(x_f32, block_rows: int | None):
         amax = np.float32(np.max(np.abs(rows))) if rows.size else np.float32(0)
         s = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
         scales[blk] = s
-        y = np.clip(rows / s, -E4M3_MAX, E4M3_MAX)       # float32 division, as the kernels
+        with np.errstate(over="ignore"):
+            r = np.float32(np.float32(1.0) / s)
+        q = rows / s if np.isinf(r) else rows * r   # float32, as the kernels
+        y = np.clip(q, -E4M3_MAX, E4M3_MAX)
         codes[blk * br:(blk + 1) * br] = e4m3_encode(y.astype(np.float64))
     return codes, scales
 

@@ -638,6 +638,14 @@ def pin_fp8_quantization():
     assert np.array_equal(codes2[:32], codes[:32]) and np.array_equal(codes2[64:], codes[64:])
     zc, zs = F8.quantize_rows(np.zeros((10, 8), np.float32), None)
     assert np.all(zc == 0) and zs[0] == 1.0
+    # a block so small that 1 / s overflows fp32: the same half-step bound and top code
+    t = (rng.standard_normal((20, 16)) * 2.0 ** -124).astype(np.float32)
+    tc, ts = F8.quantize_rows(t, None)
+    with np.errstate(over="ignore"):
+        assert ts[0] < 2.0 ** -128 and np.isinf(np.float32(1) / ts[0])
+    y = t.astype(np.float64) / np.float64(ts[0])
+    assert np.all(np.abs(F8.e4m3_decode(tc) - y) <= np.maximum(np.abs(y) / 16, 2.0 ** -10) + 1e-9)
+    assert (tc.flat[np.argmax(np.abs(t))] & 0x7F) == 0x7E
 
 
 def pin_fp8_forward_brute_force():

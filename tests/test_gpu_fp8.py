@@ -86,6 +86,24 @@ def test_fp8_outliers_codes_and_bound(gpu):
         check(gpu, q16, k16, v16, True, inc, 77, f"outliers inc{inc}")
 
 
+def test_fp8_tiny_blocks_codes(gpu):
+    """Blocks whose largest |x| is below 448 * 2^-128 (scale s under 2^-128, so 1 / s overflows
+    fp32 and the quantization divides by s): one 32-row Q block, one 64-row K block and the
+    whole V of one head scaled by 2^-124; codes, scales and outputs checked as everywhere."""
+    q16, k16, v16 = inputs.qkv_bf16(74, 1, 2, 150, 150, 128)
+    f = inputs.bf16_to_f64
+    tiny = 2.0 ** -124
+    q16[0, 0, 32:64] = inputs.bf16_round(f(q16[0, 0, 32:64]) * tiny)
+    k16[0, 1, 64:128] = inputs.bf16_round(f(k16[0, 1, 64:128]) * tiny)
+    v16[0, 1] = inputs.bf16_round(f(v16[0, 1]) * tiny)
+    for inc in (False, True):
+        p0 = F8.prepare_head(f(q16[0, 0]), f(k16[0, 0]), f(v16[0, 0]), inc, 78)
+        p1 = F8.prepare_head(f(q16[0, 1]), f(k16[0, 1]), f(v16[0, 1]), inc, 78)
+        for sc in (p0["sq"][1], p1["sk"][1], p1["sv"][0]):
+            assert sc < 2.0 ** -128, "the case must take the division branch"
+        check(gpu, q16, k16, v16, False, inc, 78, f"tiny blocks inc{inc}")
+
+
 def test_fp8_b4_h16_n2048(gpu):
     q16, k16, v16 = inputs.qkv_bf16(2, 4, 16, 2048, 2048, 128)
     check(gpu, q16, k16, v16, True, True, 1, "B4 H16 N2048 causal",
