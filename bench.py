@@ -10,7 +10,8 @@ One step = one pass over every kernel of the path on synthetic bf16 inputs alrea
 events around those kernels; `ms_per_step` is the wall time of the whole step including the decode.
 The decode is reported in GB/s of K and V read. Every kernel's own rate and roofline fraction is
 listed, and `roofline` repeats the entry of the step's kernel that takes the most time. Further
-entries are timed apart from the step: the paged-cache decode with grouped query heads, a
+entries are timed apart from the step: the decode with grouped query heads over a paged and
+over a contiguous cache, a
 causal forward + backward over a batch of eight sequences of different lengths (TFLOP/s of the
 valid rows and keys only), the forward + backward workload with dropout on P, with an additive
 bias, with d_v = 64 and with 4 K/V heads (grouped query heads), and the FP8 forward with
@@ -55,8 +56,9 @@ KERNEL_SOURCES = {"fwd": ["fa_fwd.hip", "fa_device.h"], "bwd": ["fa_bwd.hip", "f
 KERNEL_FAMILY = {"fwd": "fwd", "fwd_varlen": "fwd", "fwd_dropout": "fwd", "fwd_bias": "fwd",
                  "fwd_dv64": "fwd", "fwd_gqa": "fwd",
                  "bwd_preprocess": "bwd", "bwd_dkdv": "bwd", "bwd_dq": "bwd",
-                 "decode": "decode", "decode_paged_gqa": "decode"}
+                 "decode": "decode", "decode_paged_gqa": "decode", "decode_gqa": "decode"}
 TRAFFIC_KEY = {"decode": "decode_split", "decode_paged_gqa": "decode_paged_mfma",
+               "decode_gqa": "decode_gqa_mfma",
                "fwd_dv64": "fwd_dv"}
 
 
@@ -308,6 +310,33 @@ def main() -> int:
                        f"from the step")
     kernels["decode_paged_gqa"]["splits"] = psplits
     del kcache, vcache
+
+    # ---- the same grouped-query decode over a contiguous cache [B, H_kv, N_k, d]
+    kg, vg = dkc[:, :Hkv].contiguous(), dvc[:, :Hkv].contiguous()
+    go, gl = torch.empty_like(dq1), torch.empty((DB, DH, 1), dtype=torch.float32, device=dev)
+    gsplits = fa.decode_gqa_num_splits(DB, DH, Hkv, DN, Dd)
+    gws = torch.empty(fa.decode_gqa_workspace_bytes(DB, DH, Hkv, DN, Dd, gsplits),
+                      dtype=torch.uint8, device=dev)
+    run_g = lambda: fa.decode_gqa(dq1, kg, vg, num_splits=gsplits, workspace=gws,  # noqa: E731
+                                  out=(go, gl))
+    for _ in range(max(args.warmup, 3)):
+        run_g()
+    torch.cuda.synchronize()
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a_, b_ in gev:
+        a_.record()
+        run_g()
+        b_.record()
+    torch.cuda.synchronize()
+    g_ms = sum(a_.elapsed_time(b_) for a_, b_ in gev) / len(gev)
+    g_bytes = 2 * DB * Hkv * DN * Dd * 2 + DB * DH * Dd * 2 * 2 + DB * DH * 4
+    log(f"contiguous GQA decode {g_ms:.3f} ms")
+    kernels["decode_gqa"] = hbm_entry(
+        g_bytes, g_ms, f"contiguous K/V cache [B{DB}, {Hkv} K/V heads, {DN} positions, d{Dd}] read "
+                       f"once for {DH} query heads; q, o, lse; timed apart from the step")
+    kernels["decode_gqa"]["splits"] = gsplits
+    del kg, vg
 
     # ---- variable-length batch: causal forward + backward (timed on its own, outside the step)
     VB, VH, VN, Vd = VARLEN["B"], VARLEN["H"], VARLEN["N"], VARLEN["d"]

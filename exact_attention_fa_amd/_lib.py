@@ -44,6 +44,9 @@ SIGNATURES = {
     "fa_bwd_dropout": (_I, [_P] * 10 + [_Z] + [_I] * 5 + [_F, _I, _F, _U64, _U32, _P]),
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_varlen": (_I, [_P] * 12 + [_Z, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_decode_gqa_num_splits": (_I, [_I, _I, _I, _I, _I]),
+    "fa_decode_gqa_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "fa_decode_gqa": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_paged_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "fa_decode_paged_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -210,6 +213,41 @@ def decode(q, k, v, scale: float | None = None, num_splits: int = 0, workspace=N
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           B, H, Nq, Nk, d, _scale(scale, d), 0, int(num_splits), _stream(q))
     _check("fa_decode", st)
+    return o, lse
+
+
+def decode_gqa_num_splits(B: int, H: int, H_kv: int, Nk: int, d: int) -> int:
+    return int(load().fa_decode_gqa_num_splits(B, H, H_kv, Nk, d))
+
+
+def decode_gqa_workspace_bytes(B: int, H: int, H_kv: int, Nk: int, d: int,
+                               num_splits: int = 0) -> int:
+    return int(load().fa_decode_gqa_workspace_bytes(B, H, H_kv, Nk, d, num_splits))
+
+
+def decode_gqa(q, k, v, scale: float | None = None, num_splits: int = 0, workspace=None,
+               out=None):
+    """One decode step with grouped query heads: q [B,H,1,d] against k/v [B,H_kv,Nk,d]
+    -> (o [B,H,1,d] bf16, lse [B,H,1] fp32)."""
+    import torch
+    B, H, Nq, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    _need(q, "q", (B, H, 1, d), torch.bfloat16)
+    _need(k, "k", (B, H_kv, Nk, d), torch.bfloat16)
+    _need(v, "v", (B, H_kv, Nk, d), torch.bfloat16)
+    nbytes = decode_gqa_workspace_bytes(B, H, H_kv, Nk, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    st = load().fa_decode_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), B, H, H_kv, Nk, d,
+                              _scale(scale, d), int(num_splits), _stream(q))
+    _check("fa_decode_gqa", st)
     return o, lse
 
 

@@ -172,6 +172,44 @@ fa_status fa_decode(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf1
   return from_hip(fa::launch_decode(a));
 }
 
+int fa_decode_gqa_num_splits(int B, int H, int H_kv, int N_k, int d) {
+  if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || N_k < 1) return 1;
+  return H_kv == H ? fa::decode_auto_splits(B, H, N_k, d)
+                   : fa::decode_paged_auto_splits(B, H, H_kv, N_k, d);
+}
+
+size_t fa_decode_gqa_workspace_bytes(int B, int H, int H_kv, int N_k, int d, int num_splits) {
+  if (B < 1 || H < 1 || H_kv < 1 || N_k < 1 || (d != 64 && d != 128) || num_splits < 0) return 0;
+  const int c = num_splits == 0 ? fa_decode_gqa_num_splits(B, H, H_kv, N_k, d) : num_splits;
+  const size_t rows = (size_t)B * H * c;
+  return round_up16(rows * d * sizeof(float)) + round_up16(rows * sizeof(float));
+}
+
+fa_status fa_decode_gqa(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
+                        float* lse, void* workspace, size_t workspace_bytes, int B, int H,
+                        int H_kv, int N_k, int d, float scale, int num_splits,
+                        hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status s = check_common(B, H, 1, N_k, d, scale, 0);
+  if (s != FA_OK) return s;
+  if (H_kv < 1 || H % H_kv != 0) return FA_ERR_ARG;
+  if (num_splits < 0 || num_splits > 1024 || num_splits > N_k) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const int c = num_splits == 0 ? fa_decode_gqa_num_splits(B, H, H_kv, N_k, d) : num_splits;
+  if (!workspace || workspace_bytes < fa_decode_gqa_workspace_bytes(B, H, H_kv, N_k, d, c))
+    return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  const size_t rows = (size_t)B * H * c;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             round_up16(rows * d * sizeof(float)));
+  fa::DecodeArgs a{bf(q), bf(k), bf(v), bf(o), lse, part_o, part_lse, B, H, N_k, d, c, scale,
+                   stream};
+  a.Hkv = H_kv;
+  return from_hip(fa::launch_decode(a));
+}
+
 int fa_decode_paged_num_splits(int B, int H, int H_kv, int max_blocks_per_seq, int block_size,
                                int d) {
   if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || max_blocks_per_seq < 1 || block_size < 1)

@@ -204,13 +204,15 @@ hipError_t launch(const DecodeArgs& a) {
 // that load each row by a lane shuffle. The online softmax is the forward's; each wave writes its
 // split's normalised output and log-sum-exp per query head, and the combine kernel merges the
 // splits. Heads past the group in the last block have zero queries and are never stored.
-template <int D>
+// PAGED = false: the same kernel over a contiguous cache K, V [B, H_kv, Nk, d] (no block table,
+// every sequence Nk positions long; table, lens, bs_log2, num_blocks and max_blocks unused).
+template <int D, bool PAGED>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(64) void
 decode_paged_mfma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ Kc,
                          const bf16* __restrict__ Vc, const int* __restrict__ table,
                          const int* __restrict__ lens, float* __restrict__ part_o,
                          float* __restrict__ part_lse, int H, int Hkv, int C, int chunk,
-                         int bs_log2, int num_blocks, int max_blocks, float c) {
+                         int bs_log2, int num_blocks, int max_blocks, float c, int Nk) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KS = D / 16;          // 16-dim steps of the first product = row pieces per lane
   constexpr int CPR = D / 8;          // 16-byte chunks per row
@@ -230,14 +232,15 @@ decode_paged_mfma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ Kc
   const int lane = threadIdx.x, l32 = lane & 31, hi = lane >> 5;
   const int nheads = min(32, G - 32 * hb);  // query heads of this block
   const int h0 = kvh * G + 32 * hb;          // first query head of the block
-  const int len = min(max(lens[b], 0), max_blocks << bs_log2);
+  const int len = PAGED ? min(max(lens[b], 0), max_blocks << bs_log2) : Nk;
   const int k0 = split * chunk;
   const int k1 = min(len, k0 + chunk);
   const int ntiles = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
   const int bmask = (1 << bs_log2) - 1;
   const size_t head_off = ((size_t)kvh << bs_log2) * D;  // this K/V head inside a block
   const size_t block_stride = ((size_t)Hkv << bs_log2) * D;
-  const int* trow = table + (size_t)b * max_blocks;
+  const int* trow = PAGED ? table + (size_t)b * max_blocks : nullptr;
+  const size_t seq_off = ((size_t)b * Hkv + kvh) * (size_t)Nk * D;  // contiguous: row 0
 
   // B operand of S^T = K Q^T: query head h0 + l32, dims 16 ks + 8 hi (zero past the block)
   bf16x8 qf[KS];
@@ -251,6 +254,7 @@ decode_paged_mfma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ Kc
   // loads: piece j of this lane is chunk (lane % CPR) of tile row RPI j + lane / CPR
   const int lrow = lane / CPR, lch = lane % CPR;
   auto block_of = [&](int t) -> unsigned {  // block id of tile row l32 of tile t (k1: none)
+    if constexpr (!PAGED) return 0u;
     const int key = k0 + 32 * t + l32;
     return key < k1 ? (unsigned)trow[key >> bs_log2] : 0xffffffffu;
   };
@@ -258,14 +262,21 @@ decode_paged_mfma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ Kc
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
       const int r = RPI * j + lrow;
-      const unsigned blk = (unsigned)__shfl((int)blk_row, r);
-      // past the split, or an id out of range: zero rows
-      const bool ok = blk < (unsigned)num_blocks;
-      const size_t off = blk * block_stride + head_off +
-                         (size_t)((k0 + 32 * t + r) & bmask) * D + lch * 8;
       const u32x4 z = {0u, 0u, 0u, 0u};
-      kr[j] = ok ? ld16_nt(Kc + off) : z;
-      vr[j] = ok ? ld16_nt(Vc + off) : z;
+      if constexpr (PAGED) {
+        const unsigned blk = (unsigned)__shfl((int)blk_row, r);
+        // past the split, or an id out of range: zero rows
+        const bool ok = blk < (unsigned)num_blocks;
+        const size_t off = blk * block_stride + head_off +
+                           (size_t)((k0 + 32 * t + r) & bmask) * D + lch * 8;
+        kr[j] = ok ? ld16_nt(Kc + off) : z;
+        vr[j] = ok ? ld16_nt(Vc + off) : z;
+      } else {
+        const int key = k0 + 32 * t + r;  // past the split: zero rows
+        const size_t off = seq_off + (size_t)key * D + lch * 8;
+        kr[j] = key < k1 ? ld16_nt(Kc + off) : z;
+        vr[j] = key < k1 ? ld16_nt(Vc + off) : z;
+      }
     }
   };
   // rows into the LDS tiles (the reads of the previous tile came earlier in this wave's program
@@ -386,9 +397,28 @@ hipError_t launch_paged(const DecodePagedArgs& a) {
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float c = a.scale * kLog2e;
   const int bs_log2 = __builtin_ctz((unsigned)a.block_size);
-  hipLaunchKernelGGL((decode_paged_mfma_kernel<D>), dim3((unsigned)grid), dim3(64), 0, a.stream,
-                     a.q, a.k_cache, a.v_cache, a.block_table, a.seq_lens, a.part_o, a.part_lse,
-                     a.H, a.Hkv, C, chunk, bs_log2, a.num_blocks, a.max_blocks, c);
+  hipLaunchKernelGGL((decode_paged_mfma_kernel<D, true>), dim3((unsigned)grid), dim3(64), 0,
+                     a.stream, a.q, a.k_cache, a.v_cache, a.block_table, a.seq_lens, a.part_o,
+                     a.part_lse, a.H, a.Hkv, C, chunk, bs_log2, a.num_blocks, a.max_blocks, c, 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.H), dim3(64), 0, a.stream,
+                     a.part_o, a.part_lse, a.o, a.lse, C);
+  return hipGetLastError();
+}
+
+// grouped query heads over a contiguous cache: K, V [B, Hkv, Nk, d]
+template <int D>
+hipError_t launch_gqa(const DecodeArgs& a) {
+  const int C = a.splits;
+  const int chunk = (a.Nk + C - 1) / C;
+  const int nhb = (a.H / a.Hkv + 31) / 32;
+  const long long grid = (long long)a.B * a.Hkv * nhb * C;
+  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const float c = a.scale * kLog2e;
+  hipLaunchKernelGGL((decode_paged_mfma_kernel<D, false>), dim3((unsigned)grid), dim3(64), 0,
+                     a.stream, a.q, a.k, a.v, nullptr, nullptr, a.part_o, a.part_lse, a.H, a.Hkv,
+                     C, chunk, 0, 0, 0, c, a.Nk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.H), dim3(64), 0, a.stream,
@@ -411,6 +441,7 @@ int decode_auto_splits(int B, int H, int Nk, int d) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a) {
+  if (a.Hkv > 0 && a.Hkv != a.H) return a.d == 128 ? launch_gqa<128>(a) : launch_gqa<64>(a);
   return a.d == 128 ? launch<128>(a) : launch<64>(a);
 }
 

@@ -73,6 +73,7 @@ struct DecodeArgs {
   int B, H, Nk, d, splits;
   float scale;
   hipStream_t stream;
+  int Hkv = 0;  // K/V heads [B, Hkv, Nk, d] (0 or H: one per query head)
 };
 
 struct DecodePagedArgs {

@@ -279,7 +279,7 @@ fa_status fa_decode(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf1
                     int B, int H, int N_q, int N_k, int d, float scale, int causal,
                     int num_splits, hipStream_t stream);
 
-/* ---- Decode over a paged KV cache with grouped-query heads -----------------------------------
+/* ---- Decode with grouped-query heads, over a paged or a contiguous KV cache --------------------
  *
  * Page "Bellek Duvarının Fiziği", section "Duvarın Ötesi: KV Cache, Uzun Bağlam ve Yaklaşık
  * Attention": at inference the KV cache is the second IO front, attacked by a paged cache
@@ -301,6 +301,25 @@ fa_status fa_decode(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf1
  * [0, max_blocks_per_seq * block_size], and a row with no position gets o = 0, lse = -inf.
  * block_size must be a power of two (1 .. 4096).
  */
+
+/* The split count fa_decode_gqa uses when called with num_splits = 0. */
+int fa_decode_gqa_num_splits(int B, int H, int H_kv, int N_k, int d);
+
+/* Bytes of device workspace fa_decode_gqa needs (0 = the automatic split count): per (b, h,
+ * split) one fp32 partial output row of d values and one fp32 log-sum-exp. */
+size_t fa_decode_gqa_workspace_bytes(int B, int H, int H_kv, int N_k, int d, int num_splits);
+
+/* Split-KV decode with grouped query heads over a contiguous cache (same grouping as above, no
+ * block table, every sequence N_k positions long):
+ *   q [B,H,1,d], k/v [B,H_kv,N_k,d] bf16 in; o [B,H,1,d] bf16 and lse [B,H,1] fp32 out;
+ *   query head h reads K/V head h / (H / H_kv). num_splits: 0 = automatic, else
+ *   1 .. min(N_k, 1024); split c covers positions [c * chunk, (c + 1) * chunk) with
+ *   chunk = ceil(N_k / num_splits). All pointers and the workspace 16-byte aligned.
+ * Errors as for fa_decode; FA_ERR_ARG also for H not a multiple of H_kv. */
+fa_status fa_decode_gqa(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
+                        float* lse, void* workspace, size_t workspace_bytes, int B, int H,
+                        int H_kv, int N_k, int d, float scale, int num_splits,
+                        hipStream_t stream);
 
 /* The split count fa_decode_paged uses when called with num_splits = 0. */
 int fa_decode_paged_num_splits(int B, int H, int H_kv, int max_blocks_per_seq, int block_size,

@@ -215,6 +215,29 @@ def test_gqa_validation(lib):
     assert bwd(d=96) == 3
 
 
+def test_decode_gqa_validation(lib):
+    assert lib.fa_decode_gqa_num_splits(8, 32, 8, 65536, 128) == lib.fa_decode_paged_num_splits(
+        8, 32, 8, 4096, 16, 128)
+    assert lib.fa_decode_gqa_num_splits(8, 32, 32, 65536, 128) == lib.fa_decode_num_splits(
+        8, 32, 65536, 128)
+    ws = lib.fa_decode_gqa_workspace_bytes(2, 8, 2, 100, 64, 4)
+    assert ws == 2 * 8 * 4 * 64 * 4 + 2 * 8 * 4 * 4
+    assert lib.fa_decode_gqa_workspace_bytes(2, 8, 2, 100, 96, 4) == 0
+
+    def dec(H=8, Hkv=2, q=FAKE, ws_bytes=ws, splits=4, nk=100, d=64):
+        return lib.fa_decode_gqa(q, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, 2, H, Hkv, nk, d,
+                                 0.125, splits, None)
+    assert dec(Hkv=3) == 8       # H not a multiple of H_kv
+    assert dec(Hkv=0) == 8
+    assert dec(H=0) == 2
+    assert dec(q=None) == 1
+    assert dec(q=FAKE + 4) == 4
+    assert dec(d=96) == 3
+    assert dec(splits=101) == 8  # more splits than positions
+    assert dec(splits=-1) == 8
+    assert dec(ws_bytes=ws - 16) == 6
+
+
 def test_bwd_phase_validation(lib):
     ws = lib.fa_bwd_workspace_bytes(1, 2, 64, 64, 128)
     assert ws == 2 * 2 * 64 * 4
