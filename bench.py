@@ -15,7 +15,9 @@ over a contiguous cache, a
 causal forward + backward over a batch of eight sequences of different lengths (TFLOP/s of the
 valid rows and keys only), the forward + backward workload with dropout on P, with an additive
 bias, with d_v = 64 and with 4 K/V heads (grouped query heads), and the FP8 forward with
-incoherent processing (against the dense fp8 peak). Last, a plain 8192^3 bf16 GEMM on random data (the vendor library) gives the rate the
+incoherent processing (against the dense fp8 peak), and the forward alone on the other shapes
+(B1 H1 N256 d64; B4 H16 N2048 d128 with and without the causal mask; causal B1 H32 N32768 d128
+and B1 H64 N32768 d64). Last, a plain 8192^3 bf16 GEMM on random data (the vendor library) gives the rate the
 matrix cores sustain on such data; every bf16 MFMA entry also carries its fraction of that rate.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -36,6 +38,12 @@ from exact_attention_fa_amd import inputs, metrics  # noqa: E402
 
 FB = dict(B=2, H=16, N=8192, d=128, causal=True, seed=3)         # forward + backward workload
 DEC = dict(B=8, H=32, Nk=65536, d=128, seed=5)                  # decode workload
+# forward on the other shapes: (entry, B, H, N, d, causal, launches per timed block)
+SHAPES = [("fwd_b1h1n256d64", 1, 1, 256, 64, False, 200),
+          ("fwd_b4h16n2048", 4, 16, 2048, 128, False, 50),
+          ("fwd_b4h16n2048_causal", 4, 16, 2048, 128, True, 50),
+          ("fwd_b1h32n32768", 1, 32, 32768, 128, True, 4),
+          ("fwd_b1h64n32768_d64", 1, 64, 32768, 64, True, 4)]
 PAGED = dict(H_kv=8, block_size=16, seed=9)  # paged GQA decode: the decode workload's first 8
                                              # K/V heads as a shuffled block cache, 4 q heads each
 VARLEN = dict(B=8, H=16, N=8192, d=128, n_min=1024, causal=True, seed=21)  # variable lengths,
@@ -54,7 +62,7 @@ def log(msg: str) -> None:
 KERNEL_SOURCES = {"fwd": ["fa_fwd.hip", "fa_device.h"], "bwd": ["fa_bwd.hip", "fa_device.h"],
                   "decode": ["fa_decode.hip", "fa_device.h"]}
 KERNEL_FAMILY = {"fwd": "fwd", "fwd_varlen": "fwd", "fwd_dropout": "fwd", "fwd_bias": "fwd",
-                 "fwd_dv64": "fwd", "fwd_gqa": "fwd",
+                 "fwd_dv64": "fwd", "fwd_gqa": "fwd", **{e[0]: "fwd" for e in SHAPES},
                  "bwd_preprocess": "bwd", "bwd_dkdv": "bwd", "bwd_dq": "bwd",
                  "decode": "decode", "decode_paged_gqa": "decode", "decode_gqa": "decode"}
 TRAFFIC_KEY = {"decode": "decode_split", "decode_paged_gqa": "decode_paged_mfma",
@@ -510,6 +518,32 @@ def main() -> int:
     e8["frac"] = e8["achieved"] / e8["peak"]
     kernels["fwd_fp8"] = e8
     del f8ws
+
+    # ---- the forward on the other shapes of the workload table (iid N(0, 1) bf16 inputs): R
+    # back-to-back launches between one event pair, so that launch overhead does not dominate the
+    # small ones
+    for sname, sB, sH, sN, sd, scausal, reps in SHAPES:
+        sq, sk, sv = (torch.randn((sB, sH, sN, sd), device=dev).to(torch.bfloat16) for _ in range(3))
+        so = torch.empty_like(sq)
+        sl = torch.empty((sB, sH, sN), dtype=torch.float32, device=dev)
+        run_s = lambda: fa.fwd(sq, sk, sv, causal=scausal, out=(so, sl))  # noqa: E731
+        for _ in range(max(args.warmup, 3)):
+            run_s()
+        torch.cuda.synchronize()
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(max(1, args.steps // 4))]
+        for a_, b_ in sev:
+            a_.record()
+            for _ in range(reps):
+                run_s()
+            b_.record()
+        torch.cuda.synchronize()
+        s_ms = sum(a_.elapsed_time(b_) for a_, b_ in sev) / len(sev) / reps
+        log(f"forward {sname} {s_ms:.4f} ms")
+        kernels[sname] = mfma_entry(metrics.attention_flops(sB, sH, sN, sN, sd, causal=scausal),
+                                    s_ms, f"{'causal' if scausal else 'non-causal'} B{sB} H{sH} "
+                                          f"N{sN} d{sd}, average of {reps} back-to-back launches")
+        del sq, sk, sv, so, sl
 
     for name, nbytes in traffic.items():  # the entries timed apart from the step
         if name in kernels and kernels[name]["traffic"] is None:
