@@ -23,22 +23,26 @@ The method is an approximation, so this oracle takes its steps in that order:
 Readings (each also in the design notes):
   * FP8 = OCP E4M3 (4 exponent bits, bias 7, 3 mantissa bits, largest finite 448, subnormals down
     to 2^-9, round to nearest even); values are clamped to +-448 before rounding;
+  * the orthogonal matrix: M = diag(sigma) H_d / sqrt(d) with H_d the Sylvester-Hadamard matrix
+    (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]); the rotated rows x M are formed here as an
+    fp64 matrix product (exact up to fp64 rounding, far below any E4M3 step);
   * signs: sigma_i = -1 iff bit i of the 128-bit output of Philox-4x32-10 (oracle.dropout.philox)
     with counter (0, 0, 0, 0) and key (seed mod 2^32, seed div 2^32) is set (bit i = bit i mod 32
     of word i div 32);
-  * block scales: Q per 32 rows, K per 64 rows, V per head; s = amax / 448 (s = 1 if amax = 0);
-    code = E4M3(clamp(x / s, -448, 448)). These decisions are taken in float32 exactly as the
-    kernels take them: the rotation runs as the fast Walsh-Hadamard butterfly in float32 (spans
-    1, 2, 4, ..., d/2, each stage (a + b, a - b)), then x (1/sqrt(d) rounded to float32), then
-    x / s is evaluated as x * r with r = 1 / s rounded to float32 (the pages fix no evaluation
-    order; x / s itself only where r overflows, s < 2^-128), so every FP8 code matches the
-    kernels' bit for bit;
+  * block scales: Q per 32 rows, K per 64 rows, V per head; s = amax / 448 computed in fp64 from
+    the block's largest |x| and stored as the nearest fp32 value (s = 1 if amax = 0); the code of
+    x is E4M3(clamp(x / s, -448, 448)) with x / s an fp64 quotient, rounded once. An
+    implementation that evaluates these steps in fp32 reaches the same codes except where the
+    quotient lies within its fp32 evaluation error of a midpoint between two E4M3 values; there
+    the code may be the neighbouring one (quantize_head returns the quotients so that a test can
+    tell such ties apart);
   * probabilities: P = exp(S - m) with m the row maximum of the scores of the dequantized
     Q and K; the P V product uses E4M3(256 P) / 256 (2^8 puts P's range [0, 1] into E4M3's
     normal range); O = sum_j P^_j V^_j / sum_j P_j (normaliser from the unquantized P);
-    L = m + ln sum_j P_j. The kernels quantize P relative to their running maximum, which can
-    sit up to 0.5 (log2 units) below the final maximum, so their P codes may sit on a shifted
-    grid: O is compared with a tolerance derived from the E4M3 step, not bit for bit.
+    L = m + ln sum_j P_j. A streaming implementation quantizes P relative to a running maximum,
+    which may sit below the final one (up to 2^0.5 in P), so its P codes may sit on a shifted
+    grid: O is compared with a tolerance derived from the E4M3 step (o_tolerance), not bit for
+    bit.
 """
 from __future__ import annotations
 
@@ -102,39 +106,54 @@ def hadamard_signs(seed: int, d: int) -> np.ndarray:
     return np.where(np.array(bits) == 1, -1.0, 1.0)
 
 
-def rotate_f32(x, signs) -> np.ndarray:
-    """Rows of x times diag(signs) H_d / sqrt(d), in float32, by the butterfly (reading above)."""
-    y = np.asarray(x, dtype=np.float32) * np.asarray(signs, dtype=np.float32)
-    d = y.shape[-1]
-    h = 1
-    while h < d:
-        y = y.reshape(*y.shape[:-1], d // (2 * h), 2, h)
-        a, b = y[..., 0, :], y[..., 1, :]
-        y = np.stack([a + b, a - b], axis=-2).reshape(*y.shape[:-3], d)
-        h *= 2
-    return y * np.float32(1.0 / math.sqrt(d))
+def sylvester_hadamard(d: int) -> np.ndarray:
+    """H_d by the Sylvester recursion H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]] (d a power of
+    two), as fp64 entries +-1."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
 
 
-def quantize_rows(x_f32, block_rows: int | None):
-    """E4M3 codes and float32 scales of [n, d] float32 rows, one scale per block of block_rows
-    rows (None: one scale for all rows). Returns (codes uint8 [n, d], scales float32 [nblocks])."""
-    x = np.asarray(x_f32, dtype=np.float32)
+def rotation_matrix(signs) -> np.ndarray:
+    """M = diag(signs) H_d / sqrt(d), fp64 (orthogonal)."""
+    sg = np.asarray(signs, dtype=np.float64)
+    d = sg.shape[0]
+    return (sg[:, None] * sylvester_hadamard(d)) / math.sqrt(d)
+
+
+def rotate(x, signs) -> np.ndarray:
+    """Rows of x times M = diag(signs) H_d / sqrt(d), as an fp64 matrix product."""
+    return np.asarray(x, dtype=np.float64) @ rotation_matrix(signs)
+
+
+def block_scale(rows) -> np.float32:
+    """s = amax / 448 of one block (fp64 quotient, stored as the nearest fp32); 1 if amax = 0."""
+    amax = float(np.max(np.abs(rows))) if np.size(rows) else 0.0
+    return np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+
+
+def quantize_rows(x, block_rows: int | None):
+    """E4M3 codes and fp32 scales of [n, d] rows, one scale per block of block_rows rows (None:
+    one scale for all rows). Returns (codes uint8 [n, d], scales float32 [nblocks], quotients
+    fp64 [n, d]): the code of x is E4M3(clamp(x / s, -448, 448)), x / s taken in fp64."""
+    x = np.asarray(x, dtype=np.float64)
     n = x.shape[0]
     br = n if block_rows is None else block_rows
     nb = max(1, -(-n // br)) if n else 0
     codes = np.zeros(x.shape, dtype=np.uint8)
     scales = np.ones(nb, dtype=np.float32)
+    quot = np.zeros(x.shape, dtype=np.float64)
     for blk in range(nb):
         rows = x[blk * br:(blk + 1) * br]
-        amax = np.float32(np.max(np.abs(rows))) if rows.size else np.float32(0)
-        s = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+        s = block_scale(rows)
         scales[blk] = s
-        with np.errstate(over="ignore"):
-            r = np.float32(np.float32(1.0) / s)
-        q = rows / s if np.isinf(r) else rows * r   # float32, as the kernels
-        y = np.clip(q, -E4M3_MAX, E4M3_MAX)
-        codes[blk * br:(blk + 1) * br] = e4m3_encode(y.astype(np.float64))
-    return codes, scales
+        y = rows / np.float64(s)
+        quot[blk * br:(blk + 1) * br] = y
+        codes[blk * br:(blk + 1) * br] = e4m3_encode(np.clip(y, -E4M3_MAX, E4M3_MAX))
+    return codes, scales, quot
 
 
 def dequantize_rows(codes, scales, block_rows: int | None) -> np.ndarray:
@@ -146,21 +165,48 @@ def dequantize_rows(codes, scales, block_rows: int | None) -> np.ndarray:
 
 
 def prepare_head(q, k, v, incoherent: bool, seed: int):
-    """Steps 1 and 2 for one head: returns a dict of codes and scales (q8, sq, k8, sk, v8, sv)."""
+    """Steps 1 and 2 for one head: a dict of codes and scales (q8, sq, k8, sk, v8, sv), the
+    quantized quotients x / s (qy, ky, vy) and the rows before quantization (qr, kr: rotated
+    when incoherent, vr), all fp64."""
     d = np.shape(q)[-1]
-    qf = np.asarray(q, dtype=np.float32)
-    kf = np.asarray(k, dtype=np.float32)
+    qr = np.asarray(q, dtype=np.float64)
+    kr = np.asarray(k, dtype=np.float64)
+    vr = np.asarray(v, dtype=np.float64)
     if incoherent:
         sg = hadamard_signs(seed, d)
-        qf, kf = rotate_f32(qf, sg), rotate_f32(kf, sg)
-    q8, sq = quantize_rows(qf, Q_BLOCK_ROWS)
-    k8, sk = quantize_rows(kf, K_BLOCK_ROWS)
-    v8, sv = quantize_rows(np.asarray(v, dtype=np.float32), None)
-    return dict(q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv)
+        qr, kr = rotate(qr, sg), rotate(kr, sg)
+    q8, sq, qy = quantize_rows(qr, Q_BLOCK_ROWS)
+    k8, sk, ky = quantize_rows(kr, K_BLOCK_ROWS)
+    v8, sv, vy = quantize_rows(vr, None)
+    return dict(q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, qy=qy, ky=ky, vy=vy, qr=qr, kr=kr,
+                vr=vr)
 
 
-def attention_from_codes(prep, scale: float, causal: bool):
-    """Step 3 for one head from prepare_head's codes: (o [n_q, d], lse [n_q]) in fp64."""
+def e4m3_tie_distance(y) -> np.ndarray:
+    """Distance of each |y| (<= 448) to the nearest midpoint between two adjacent non-negative
+    E4M3 values, i.e. how far y is from a point where its rounding would change."""
+    vals = np.sort(e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8)))  # 0 .. 448, 127 values
+    mids = (vals[1:] + vals[:-1]) / 2
+    a = np.minimum(np.abs(np.asarray(y, dtype=np.float64)), E4M3_MAX)
+    i = np.clip(np.searchsorted(mids, a), 1, len(mids) - 1)
+    return np.minimum(np.abs(a - mids[i - 1]), np.abs(a - mids[i]))
+
+
+def e4m3_code_index(codes) -> np.ndarray:
+    """Signed position of each code on the ordered E4M3 value line (0 for both zeros), so that
+    two codes of adjacent values differ by exactly one."""
+    c = np.asarray(codes, dtype=np.int64)
+    mag = c & 0x7F  # magnitudes are ordered like their bit patterns
+    return np.where(c & 0x80, -mag, mag)
+
+
+def attention_from_codes(prep, scale: float, causal: bool, p_shift=0.0):
+    """Step 3 for one head from prepare_head's codes: (o [n_q, d], lse [n_q]) in fp64.
+
+    p_shift (default 0; a scalar or one value per row, in log2 units) quantizes each row's
+    probabilities relative to a reference that sits p_shift below its maximum, as a streaming
+    implementation with a running maximum does: P^ = E4M3(256 2^p_shift P) / (256 2^p_shift).
+    The normaliser and L use the unquantized P either way."""
     qh = dequantize_rows(prep["q8"], prep["sq"], Q_BLOCK_ROWS)
     kh = dequantize_rows(prep["k8"], prep["sk"], K_BLOCK_ROWS)
     vh = dequantize_rows(prep["v8"], prep["sv"], None)
@@ -168,7 +214,8 @@ def attention_from_codes(prep, scale: float, causal: bool):
     m = np.max(s, axis=1, keepdims=True)
     p = np.exp(s - m)
     z = np.sum(p, axis=1, keepdims=True)
-    p_hat = e4m3_round(P_SCALE * p) / P_SCALE
+    g = P_SCALE * np.exp2(np.reshape(np.asarray(p_shift, dtype=np.float64), (-1, 1)))
+    p_hat = e4m3_round(g * p) / g
     o = (p_hat @ vh) / z
     return o, (m + np.log(z))[:, 0]
 
@@ -191,12 +238,13 @@ def forward_fp8(q, k, v, scale: float, causal: bool, incoherent: bool, seed: int
 
 
 def o_tolerance(prep, scale: float, causal: bool) -> np.ndarray:
-    """Per-row bound on |O_kernel - O_oracle| for O computed from the same codes with P quantized
-    on grids whose maxima differ by up to 2^0.5: each quantized probability is within half an
-    E4M3 step (relative 2^-4, or 2^-10 / 256 absolute below the normal range) of P on either side,
-    so the two outputs differ by at most
-    2 (2^-4 sum_j P_j |v_j| + (2^-10 / 256) 2^0.5 sum_j |v_j|) / sum_j P_j per element, plus the
-    bf16 rounding of the output (2^-8 |O|). Returns [n_q, d]."""
+    """Per-element bound [n_q, d] on |O' - O| between this oracle's O (attention_from_codes) and
+    an O' computed from the same codes whose probabilities were quantized on another grid (a
+    reference maximum up to 2^0.5 away in P, see p_shift) and then rounded to bf16. Each
+    quantized probability lies within half an E4M3 step of P: relative 2^-4 in the normal range,
+    at most 2^0.5 2^-10 / 256 absolute below it. Both outputs carry such an error per key, so
+    |O' - O| <= 2 (2^-4 sum_j P_j |v_j| + 2^0.5 (2^-10 / 256) sum_j |v_j|) / sum_j P_j,
+    plus the bf16 rounding of O' (2^-8 |O|, above half a bf16 step)."""
     qh = dequantize_rows(prep["q8"], prep["sq"], Q_BLOCK_ROWS)
     kh = dequantize_rows(prep["k8"], prep["sk"], K_BLOCK_ROWS)
     vh = np.abs(dequantize_rows(prep["v8"], prep["sv"], None))

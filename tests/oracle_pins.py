@@ -451,6 +451,20 @@ def pin_philox_against_numpy():
         assert got == want, (ctr, key)
 
 
+def pin_philox_known_answers():
+    """Philox-4x32-10 against the published known-answer vectors of the Random123 distribution
+    (the reference implementation of [PX]): this pins the 32-bit multipliers, which the numpy
+    check above (a 64-bit member) does not reach."""
+    cases = [((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+             ((0xFFFFFFFF,) * 4, (0xFFFFFFFF, 0xFFFFFFFF),
+              (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+             ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+              (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1))]
+    for ctr, key, want in cases:
+        got = tuple(int(x) for x in DR.philox([ctr], key)[0])
+        assert got == want, (ctr, key, [hex(x) for x in got])
+
+
 def pin_philox_constants():
     """Weyl increments are floor(2^W (golden ratio - 1)) and floor(2^W (sqrt(3) - 1)), computed
     here with exact integer square roots; multipliers are odd (invertible mod 2^W)."""
@@ -597,55 +611,109 @@ def pin_e4m3_against_torch():
 
 
 def pin_hadamard_rotation():
-    """The float32 butterfly equals x diag(sigma) H_d / sqrt(d) with scipy's Sylvester-Hadamard
-    matrix; the rotation is orthogonal, so Q K^T is unchanged; signs are +-1 from Philox bits."""
+    """H_d by the Sylvester recursion equals scipy's Hadamard matrix (an independent
+    implementation); the fp64 rotation equals x diag(sigma) H_d / sqrt(d) formed from it and the
+    fast Walsh-Hadamard butterfly (spans 1, 2, ..., d/2 of (a + b, a - b), written out here); it is
+    orthogonal, so Q K^T is unchanged; the signs are the Philox bits."""
     import scipy.linalg
     rng = _rng(21)
+    for d in (1, 2, 4, 8, 16, 32, 64, 128):
+        assert np.array_equal(F8.sylvester_hadamard(d), scipy.linalg.hadamard(d).astype(np.float64))
     for d in (64, 128):
         sg = F8.hadamard_signs(2**35 + 9, d)
         assert set(np.unique(sg)) <= {-1.0, 1.0} and 0 < np.sum(sg < 0) < d
-        x = rng.standard_normal((7, d)).astype(np.float32)
-        ref = (x.astype(np.float64) * sg) @ scipy.linalg.hadamard(d) / math.sqrt(d)
-        assert np.max(np.abs(F8.rotate_f32(x, sg) - ref)) < 1e-5
-        M = np.diag(sg) @ scipy.linalg.hadamard(d) / math.sqrt(d)
+        x = rng.standard_normal((7, d))
+        ref = (x * sg) @ scipy.linalg.hadamard(d) / math.sqrt(d)
+        assert np.max(np.abs(F8.rotate(x, sg) - ref)) < 1e-12
+        y = x * sg
+        h = 1
+        while h < d:
+            y = y.reshape(7, d // (2 * h), 2, h)
+            y = np.stack([y[:, :, 0] + y[:, :, 1], y[:, :, 0] - y[:, :, 1]], axis=2).reshape(7, d)
+            h *= 2
+        assert np.max(np.abs(F8.rotate(x, sg) - y / math.sqrt(d))) < 1e-12
+        M = F8.rotation_matrix(sg)
         assert np.allclose(M @ M.T, np.eye(d), atol=1e-12)
         q, k = rng.standard_normal((5, d)), rng.standard_normal((6, d))
-        assert np.allclose((q @ M) @ (k @ M).T, q @ k.T, atol=1e-10)
+        assert np.allclose(F8.rotate(q, sg) @ F8.rotate(k, sg).T, q @ k.T, atol=1e-10)
     w = DR.philox([[0, 0, 0, 0]], (9, 0))[0]
     sg = F8.hadamard_signs(9, 128)
     assert all((sg[i] < 0) == bool((int(w[i // 32]) >> (i % 32)) & 1) for i in range(128))
 
 
 def pin_fp8_quantization():
-    """Codes reconstruct each value within half an E4M3 step; the largest |x| of each block maps
-    to the code of 448; editing one block changes only that block's scale and codes."""
+    """Scales are the fp32 value nearest amax / 448 of each block; codes reconstruct each value
+    within half an E4M3 step and are the nearest E4M3 values of x / s (checked against PyTorch's
+    float8_e4m3fn conversion of the fp64 quotient, away from ties); the largest |x| of each block
+    maps to the code of 448; editing one block changes only that block's scale and codes."""
+    import torch
     rng = _rng(22)
-    x = (rng.standard_normal((100, 64)) * 3).astype(np.float32)
-    codes, sc = F8.quantize_rows(x, 32)
-    assert sc.shape == (4,)
+    x = rng.standard_normal((100, 64)) * 3
+    codes, sc, quot = F8.quantize_rows(x, 32)
+    assert sc.shape == (4,) and sc.dtype == np.float32
     for b in range(4):
         blk = x[32 * b:32 * (b + 1)]
-        assert sc[b] == np.float32(np.max(np.abs(blk)) / np.float32(448.0))
+        assert sc[b] == np.float32(np.max(np.abs(blk)) / 448.0)
         c = codes[32 * b:32 * (b + 1)]
         i = np.unravel_index(np.argmax(np.abs(blk)), blk.shape)
         assert (c[i] & 0x7F) == 0x7E
-        y = blk.astype(np.float64) / sc[b]
+        y = blk / np.float64(sc[b])
+        assert np.array_equal(quot[32 * b:32 * (b + 1)], y)
         assert np.all(np.abs(F8.e4m3_decode(c) - y) <= np.maximum(np.abs(y) / 16, 2.0 ** -10) + 1e-12)
+        # torch converts from fp32: compare where the fp32 rounding of y cannot cross a tie
+        safe = F8.e4m3_tie_distance(y) > 1e-6 * np.maximum(np.abs(y), 1e-3)
+        t = torch.from_numpy(np.clip(y, -448, 448).astype(np.float32)).to(torch.float8_e4m3fn)
+        assert np.array_equal(c[safe], t.view(torch.uint8).numpy()[safe])
     x2 = x.copy()
     x2[40] *= 5
-    codes2, sc2 = F8.quantize_rows(x2, 32)
+    codes2, sc2, _ = F8.quantize_rows(x2, 32)
     assert sc2[0] == sc[0] and sc2[2] == sc[2] and sc2[3] == sc[3] and sc2[1] != sc[1]
     assert np.array_equal(codes2[:32], codes[:32]) and np.array_equal(codes2[64:], codes[64:])
-    zc, zs = F8.quantize_rows(np.zeros((10, 8), np.float32), None)
+    zc, zs, _ = F8.quantize_rows(np.zeros((10, 8)), None)
     assert np.all(zc == 0) and zs[0] == 1.0
-    # a block so small that 1 / s overflows fp32: the same half-step bound and top code
-    t = (rng.standard_normal((20, 16)) * 2.0 ** -124).astype(np.float32)
-    tc, ts = F8.quantize_rows(t, None)
-    with np.errstate(over="ignore"):
-        assert ts[0] < 2.0 ** -128 and np.isinf(np.float32(1) / ts[0])
-    y = t.astype(np.float64) / np.float64(ts[0])
+    # a block so small that its scale is an fp32 subnormal: the same half-step bound and top code
+    t = rng.standard_normal((20, 16)) * 2.0 ** -124
+    tc, ts, _ = F8.quantize_rows(t, None)
+    assert ts[0] < 2.0 ** -126 and ts[0] == np.float32(np.max(np.abs(t)) / 448.0)
+    y = t / np.float64(ts[0])
     assert np.all(np.abs(F8.e4m3_decode(tc) - y) <= np.maximum(np.abs(y) / 16, 2.0 ** -10) + 1e-9)
     assert (tc.flat[np.argmax(np.abs(t))] & 0x7F) == 0x7E
+    # the tie distance and the code line: midpoints are at distance 0, codes of neighbours
+    # differ by one position
+    vals = F8.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    mids = (vals[1:] + vals[:-1]) / 2
+    assert np.all(F8.e4m3_tie_distance(mids) == 0) and np.all(F8.e4m3_tie_distance(vals) > 0)
+    assert F8.e4m3_tie_distance(np.array([1.0]))[0] == 1 / 32      # 1 lies 2^-5 from 1 +- 2^-5
+    enc = F8.e4m3_encode(np.concatenate([-vals[::-1], vals]))
+    idx = F8.e4m3_code_index(enc)
+    assert np.all(np.diff(idx) <= 1) and idx[0] == -126 and idx[-1] == 126
+
+
+def pin_fp8_o_tolerance():
+    """o_tolerance holds what it claims: outputs whose probabilities were quantized relative to a
+    reference up to 2^0.5 below the row maximum (any shift in [0, 0.5], the same or different per
+    row; scale 0.5 puts many probabilities in E4M3's subnormal range), rounded to bf16, stay
+    inside it; a V scale off by 1.25 and a missing 1 / sum(P) fall outside it somewhere."""
+    from exact_attention_fa_amd import inputs
+    rng = _rng(25)
+    for n_q, n_k, d, causal, sc in [(64, 64, 64, True, 0.125), (40, 200, 128, False, 0.125),
+                                    (30, 100, 64, False, 0.5), (70, 70, 128, True, 0.09)]:
+        q, k, v = (rng.standard_normal((n, d)) for n in (n_q, n_k, n_k))
+        pr = F8.prepare_head(q, k, v, True, 5)
+        o, _ = F8.attention_from_codes(pr, sc, causal)
+        tol = F8.o_tolerance(pr, sc, causal)
+        shifts = [0.0, 0.1, 0.25, 0.4, 0.5, rng.uniform(0, 0.5, n_q)]
+        for sh in shifts:
+            o2, _ = F8.attention_from_codes(pr, sc, causal, p_shift=sh)
+            o2 = inputs.bf16_to_f64(inputs.bf16_round(o2.astype(np.float32)))
+            assert np.all(np.abs(o2 - o) <= tol), (n_q, n_k, sh)
+        assert np.any(np.abs(1.25 * o - o) > tol)
+        qh = F8.dequantize_rows(pr["q8"], pr["sq"], F8.Q_BLOCK_ROWS)
+        kh = F8.dequantize_rows(pr["k8"], pr["sk"], F8.K_BLOCK_ROWS)
+        vh = F8.dequantize_rows(pr["v8"], pr["sv"], None)
+        s = A.scores(qh, kh, sc, causal)
+        ph = F8.e4m3_round(256 * np.exp(s - np.max(s, axis=1, keepdims=True))) / 256
+        assert np.any(np.abs(ph @ vh - o) > tol)  # no 1 / sum(P)
 
 
 def pin_fp8_forward_brute_force():
@@ -833,9 +901,9 @@ ALL_PINS = [pin_brute_force_rows, pin_rows_sum_to_one, pin_causal_future_invaria
             pin_torch_sdpa, pin_hand_examples, pin_decode_split_combine,
             pin_paged_gqa_brute_force, pin_paged_invariances, pin_varlen_brute_force,
             pin_varlen_padding_and_truncation, pin_varlen_finite_differences,
-            pin_philox_against_numpy, pin_philox_constants, pin_dropout_mask_statistics,
+            pin_philox_against_numpy, pin_philox_known_answers, pin_philox_constants, pin_dropout_mask_statistics,
             pin_dropout_mask_layout, pin_dropout_brute_force,
             pin_dropout_expectation_and_identities, pin_dropout_finite_differences,
-            pin_e4m3_against_torch, pin_hadamard_rotation, pin_fp8_quantization,
+            pin_e4m3_against_torch, pin_hadamard_rotation, pin_fp8_quantization, pin_fp8_o_tolerance,
             pin_fp8_forward_brute_force, pin_fp8_incoherent_claim, pin_bias_brute_force,
             pin_bias_special_cases, pin_gqa_closed_form, pin_gqa_gradients]

@@ -264,7 +264,7 @@ def _bwd_drop_unmasked_dp(q, k, v, do, scale, causal, p, seed, offset):
 
 
 _orig_e4m3_round = F8.e4m3_round
-_orig_rotate = F8.rotate_f32
+_orig_rotate = F8.rotate
 _orig_att_codes = F8.attention_from_codes
 
 
@@ -279,7 +279,32 @@ def _e4m3_ties_away(x):
 
 
 def _rotate_unnormalised(x, signs):
-    return _orig_rotate(x, signs) * np.float32(np.sqrt(np.shape(x)[-1]))
+    return _orig_rotate(x, signs) * np.sqrt(np.shape(x)[-1])
+
+
+def _hadamard_other_recursion(d):
+    # [[H, H], [-H, H]]: also orthogonal, but not the Sylvester matrix
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [-h, h]])
+    return h
+
+
+def _block_scale_from_fp32_amax_halved(rows):
+    amax = float(np.max(np.abs(rows))) if np.size(rows) else 0.0
+    return np.float32(amax / 224.0) if amax > 0 else np.float32(1.0)
+
+
+_orig_tol = F8.o_tolerance
+
+
+def _o_tolerance_no_normaliser(prep, scale, causal):
+    # the bound without its division by sum(P): far too loose
+    qh = F8.dequantize_rows(prep["q8"], prep["sq"], F8.Q_BLOCK_ROWS)
+    kh = F8.dequantize_rows(prep["k8"], prep["sk"], F8.K_BLOCK_ROWS)
+    s = A.scores(qh, kh, scale, causal)
+    z = np.sum(np.exp(s - np.max(s, axis=1, keepdims=True)), axis=1, keepdims=True)
+    return _orig_tol(prep, scale, causal) * z
 
 
 def _rotate_no_signs(x, signs):
@@ -377,8 +402,11 @@ MUTANTS = {
     "fp8_ties_away_from_zero": ("e4m3_round", _e4m3_ties_away, F8),
     "bias_scaled_with_scores": ("forward_bias", _fwd_bias_scaled),
     "bias_transposed": ("forward_bias", _fwd_bias_transposed),
-    "fp8_rotation_unnormalised": ("rotate_f32", _rotate_unnormalised, F8),
-    "fp8_rotation_without_signs": ("rotate_f32", _rotate_no_signs, F8),
+    "fp8_rotation_unnormalised": ("rotate", _rotate_unnormalised, F8),
+    "fp8_rotation_without_signs": ("rotate", _rotate_no_signs, F8),
+    "fp8_hadamard_other_recursion": ("sylvester_hadamard", _hadamard_other_recursion, F8),
+    "fp8_scale_amax_over_224": ("block_scale", _block_scale_from_fp32_amax_halved, F8),
+    "fp8_tolerance_without_normaliser": ("o_tolerance", _o_tolerance_no_normaliser, F8),
     "fp8_q_blocks_of_64": ("Q_BLOCK_ROWS", 64, F8),
     "fp8_p_unshifted": ("attention_from_codes", _att_codes_unshifted_p, F8),
     "fp8_normaliser_from_quantized_p": ("attention_from_codes", _att_codes_quantized_normaliser, F8),
