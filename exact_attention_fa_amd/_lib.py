@@ -102,6 +102,29 @@ def _need(t, name: str, shape, dtype) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _workspace(ws, nbytes: int, device):
+    """A caller's workspace: a contiguous tensor on the GPU of at least nbytes bytes (the library
+    checks the size again); None allocates one."""
+    import torch
+    if ws is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return ws
+
+
+def _outs(out, specs):
+    """Validate caller-supplied outputs: out is a tuple matched against specs, a list of
+    (name, shape, dtype)."""
+    if len(out) != len(specs):
+        raise ValueError(f"out must hold {len(specs)} tensors")
+    for t, (name, shape, dtype) in zip(out, specs):
+        _need(t, name, shape, dtype)
+    return out
+
+
 def _scale(scale, d: int) -> float:
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
@@ -142,12 +165,13 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
         _need(t, n, shp, torch.bfloat16)
     _need(lse, "lse", (B, H, Nq), torch.float32)
     nbytes = bwd_workspace_bytes(B, H, Nq, Nk, d)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
-        dq, dk, dv = out
+        dq, dk, dv = _outs(out, [("dq", tuple(q.shape), torch.bfloat16),
+                                 ("dk", tuple(k.shape), torch.bfloat16),
+                                 ("dv", tuple(v.shape), torch.bfloat16)])
     st = load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -169,6 +193,9 @@ def bwd_phase(phase: str, q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: 
         _need(t, n, shp, torch.bfloat16)
     _need(lse, "lse", (B, H, Nq), torch.float32)
     lib = load()
+    if workspace is None:
+        raise ValueError("bwd_phase needs the workspace shared by the three phases")
+    workspace = _workspace(workspace, 0, q.device)
     ws, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     sc, ca, st = _scale(scale, d), int(bool(causal)), _stream(q)
     if phase == "preprocess":
@@ -202,13 +229,13 @@ def decode(q, k, v, scale: float | None = None, num_splits: int = 0, workspace=N
     _need(k, "k", (B, H, Nk, d), torch.bfloat16)
     _need(v, "v", (B, H, Nk, d), torch.bfloat16)
     nbytes = decode_workspace_bytes(B, H, Nk, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
     if out is None:
         o = torch.empty_like(q)
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     else:
-        o, lse = out
+        o, lse = _outs(out, [("o", (B, H, Nq, d), torch.bfloat16),
+                             ("lse", (B, H, Nq), torch.float32)])
     st = load().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           B, H, Nq, Nk, d, _scale(scale, d), 0, int(num_splits), _stream(q))
@@ -236,13 +263,13 @@ def decode_gqa(q, k, v, scale: float | None = None, num_splits: int = 0, workspa
     _need(k, "k", (B, H_kv, Nk, d), torch.bfloat16)
     _need(v, "v", (B, H_kv, Nk, d), torch.bfloat16)
     nbytes = decode_gqa_workspace_bytes(B, H, H_kv, Nk, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
     if out is None:
         o = torch.empty_like(q)
         lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
     else:
-        o, lse = out
+        o, lse = _outs(out, [("o", (B, H, 1, d), torch.bfloat16),
+                             ("lse", (B, H, 1), torch.float32)])
     st = load().fa_decode_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                               lse.data_ptr(), workspace.data_ptr(),
                               workspace.numel() * workspace.element_size(), B, H, H_kv, Nk, d,
@@ -278,8 +305,7 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale: float | None
     _need(block_table, "block_table", (B, max_blocks), torch.int32)
     _need(seq_lens, "seq_lens", (B,), torch.int32)
     nbytes = decode_paged_workspace_bytes(B, H, H_kv, max_blocks, block_size, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
     if out is None:
         o = torch.empty_like(q)
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
@@ -342,12 +368,13 @@ def bwd_varlen(q, k, v, o, lse, dout, seq_lens_q, seq_lens_k, causal: bool = Fal
     _lens(seq_lens_q, "seq_lens_q", B)
     _lens(seq_lens_k, "seq_lens_k", B)
     nbytes = bwd_workspace_bytes(B, H, Nq, Nk, d)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
-        dq, dk, dv = out
+        dq, dk, dv = _outs(out, [("dq", tuple(q.shape), torch.bfloat16),
+                                 ("dk", tuple(k.shape), torch.bfloat16),
+                                 ("dv", tuple(v.shape), torch.bfloat16)])
     st = load().fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                               lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                               dv.data_ptr(), seq_lens_q.data_ptr(), seq_lens_k.data_ptr(),
@@ -393,12 +420,13 @@ def bwd_dropout(q, k, v, o, lse, dout, p_drop: float, seed: int, offset: int = 0
         _need(t, n, shp, torch.bfloat16)
     _need(lse, "lse", (B, H, Nq), torch.float32)
     nbytes = bwd_workspace_bytes(B, H, Nq, Nk, d)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
-        dq, dk, dv = out
+        dq, dk, dv = _outs(out, [("dq", tuple(q.shape), torch.bfloat16),
+                                 ("dk", tuple(k.shape), torch.bfloat16),
+                                 ("dv", tuple(v.shape), torch.bfloat16)])
     st = load().fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                dv.data_ptr(), workspace.data_ptr(),
@@ -424,8 +452,7 @@ def fwd_fp8(q, k, v, causal: bool = False, incoherent: bool = True, seed: int = 
     _need(k, "k", (B, H, Nk, d), torch.bfloat16)
     _need(v, "v", (B, H, Nk, d), torch.bfloat16)
     nbytes = fwd_fp8_workspace_bytes(B, H, Nq, Nk, d)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
     if out is None:
         o = torch.empty_like(q)
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
@@ -500,7 +527,8 @@ def fwd_bias(q, k, v, bias, causal: bool = False, scale: float | None = None, ou
         o = torch.empty_like(q)
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     else:
-        o, lse = out
+        o, lse = _outs(out, [("o", (B, H, Nq, d), torch.bfloat16),
+                             ("lse", (B, H, Nq), torch.float32)])
     st = load().fa_fwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             bias.data_ptr(), sb, sh, sq, B, H, Nq, Nk, d, _scale(scale, d),
                             int(bool(causal)), _stream(q))
@@ -520,12 +548,13 @@ def bwd_bias(q, k, v, o, lse, dout, bias, causal: bool = False, scale: float | N
     _need(lse, "lse", (B, H, Nq), torch.float32)
     bias, (sb, sh, sq) = _bias_strides(bias, B, H, Nq, Nk)
     nbytes = bwd_workspace_bytes(B, H, Nq, Nk, d)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
-        dq, dk, dv = out
+        dq, dk, dv = _outs(out, [("dq", tuple(q.shape), torch.bfloat16),
+                                 ("dk", tuple(k.shape), torch.bfloat16),
+                                 ("dv", tuple(v.shape), torch.bfloat16)])
     st = load().fa_bwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                             lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                             dv.data_ptr(), bias.data_ptr(), sb, sh, sq, workspace.data_ptr(),
@@ -547,7 +576,8 @@ def fwd_dv(q, k, v, causal: bool = False, scale: float | None = None, out=None):
         o = torch.empty((B, H, Nq, dv_), dtype=torch.bfloat16, device=q.device)
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     else:
-        o, lse = out
+        o, lse = _outs(out, [("o", (B, H, Nq, dv_), torch.bfloat16),
+                             ("lse", (B, H, Nq), torch.float32)])
     st = load().fa_fwd_dv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                           B, H, Nq, Nk, d, dv_, _scale(scale, d), int(bool(causal)), _stream(q))
     _check("fa_fwd_dv", st)
@@ -566,12 +596,13 @@ def bwd_dv(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = No
         _need(t, n, shp, torch.bfloat16)
     _need(lse, "lse", (B, H, Nq), torch.float32)
     nbytes = bwd_workspace_bytes(B, H, Nq, Nk, d)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
-        dq, dk, dv = out
+        dq, dk, dv = _outs(out, [("dq", tuple(q.shape), torch.bfloat16),
+                                 ("dk", tuple(k.shape), torch.bfloat16),
+                                 ("dv", tuple(v.shape), torch.bfloat16)])
     st = load().fa_bwd_dv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                           dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -620,12 +651,13 @@ def bwd_gqa(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = N
         _need(t, n, shp, torch.bfloat16)
     _need(lse, "lse", (B, H, Nq), torch.float32)
     nbytes = bwd_gqa_workspace_bytes(B, H, Hkv, Nq, Nk, d)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
-        dq, dk, dv = out
+        dq, dk, dv = _outs(out, [("dq", tuple(q.shape), torch.bfloat16),
+                                 ("dk", tuple(k.shape), torch.bfloat16),
+                                 ("dv", tuple(v.shape), torch.bfloat16)])
     st = load().fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),

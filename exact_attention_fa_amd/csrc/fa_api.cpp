@@ -10,11 +10,16 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// One head's rows of width w (bf16) span fewer than 2^31 bytes: the kernels address inside a
+// head with 32-bit byte offsets.
+bool head_extent_ok(int n, int w) { return (long long)n * w * 2 < (1LL << 31); }
+
 fa_status check_common(int B, int H, int Nq, int Nk, int d, float scale, int causal) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
   const long long bh = (long long)B * H;
   if (bh * Nq >= (1LL << 31) || bh * Nk >= (1LL << 31)) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!head_extent_ok(Nq, d) || !head_extent_ok(Nk, d)) return FA_ERR_SHAPE;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
   if (causal && Nq > Nk) return FA_ERR_CAUSAL;
   return FA_OK;
@@ -417,6 +422,7 @@ fa_status fa_fwd_dv(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf1
   fa_status s = check_common(B, H, N_q, N_k, d, scale, causal);
   if (s != FA_OK) return s;
   if (d_v != 64 && d_v != 128) return FA_ERR_HEADDIM;
+  if (!head_extent_ok(N_q, d_v) || !head_extent_ok(N_k, d_v)) return FA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
   fa::FwdArgs a{bf(q), bf(k), bf(v), bf(o), lse, B, H, N_q, N_k, d, scale, causal != 0, stream};
@@ -429,6 +435,8 @@ fa_status fa_bwd_dv(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const 
                     void* workspace, size_t workspace_bytes, int B, int H, int N_q, int N_k, int d,
                     int d_v, float scale, int causal, hipStream_t stream) {
   if (d_v != 64 && d_v != 128) return FA_ERR_HEADDIM;
+  if (N_q >= 1 && N_k >= 1 && (!head_extent_ok(N_q, d_v) || !head_extent_ok(N_k, d_v)))
+    return FA_ERR_SHAPE;
   return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N_q,
                      N_k, d, scale, causal, stream, 15u, 7u, nullptr, nullptr, nullptr, nullptr,
                      d_v);

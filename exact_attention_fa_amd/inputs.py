@@ -136,3 +136,34 @@ def outlier_bf16(seed: int, tensor: str, B: int, H: int, n: int, d: int, frac: f
             x[hit] += mag * g.standard_normal(int(hit.sum()))
             out[b, h] = bf16_round(x.astype(np.float32))
     return out
+
+
+def rising_keys(q_u16: np.ndarray, k_u16: np.ndarray, per_key: float, q_value: float = 3.0):
+    """Copies of Q [.., n_q, d] and K [.., n_k, d] (bf16 bit patterns) with column 0 overwritten:
+    Q[.., 0] = q_value and K[.., j, 0] = per_key * j (rounded to bf16), so that every query's
+    score grows with the key index and a running row maximum rises on every block of keys."""
+    q = np.array(q_u16, copy=True)
+    k = np.array(k_u16, copy=True)
+    q[..., 0] = bf16_round(np.full(q.shape[:-1], q_value, dtype=np.float32))
+    n_k = k.shape[-2]
+    ramp = (np.arange(n_k, dtype=np.float64) * per_key).astype(np.float32)
+    k[..., 0] = bf16_round(np.broadcast_to(ramp, k.shape[:-1]))
+    return q, k
+
+
+def rising_keys_paged(q_u16: np.ndarray, k_cache: np.ndarray, block_table, seq_lens,
+                      per_key: float, q_value: float = 3.0):
+    """rising_keys for a paged cache (paged_kv_bf16's layout): q [B, H, d] gets column 0 =
+    q_value, and position j of sequence b (block block_table[b, j // bs], row j % bs) gets
+    K column 0 = per_key * j in every K/V head."""
+    q = np.array(q_u16, copy=True)
+    kc = np.array(k_cache, copy=True)
+    q[..., 0] = bf16_round(np.full(q.shape[:-1], q_value, dtype=np.float32))
+    bs = kc.shape[2]
+    for b, n in enumerate(np.asarray(seq_lens)):
+        j = np.arange(int(n))
+        vals = bf16_round((j * per_key).astype(np.float32))
+        blocks, rows = np.asarray(block_table)[b][j // bs], j % bs
+        for h in range(kc.shape[1]):
+            kc[blocks, h, rows, 0] = vals
+    return q, kc

@@ -68,6 +68,33 @@ def test_fwd_validation(lib):
     assert _fwd(lib, o=FAKE + 2) == 4
 
 
+def test_per_head_extent_validation(lib):
+    """One head whose rows span 2^31 bytes or more (N_k = 2^24 at d = 128, or 2^23 at d = 128 is
+    the first size that does) is rejected before any launch: the kernels address inside a head
+    with 32-bit byte offsets. Every call here gets fake pointers, so reaching a launch would
+    fail differently."""
+    big = 1 << 23                                  # 2^23 rows x 128 x 2 bytes = 2^31
+    assert _fwd(lib, Nk=1 << 24, d=128) == 2
+    assert _fwd(lib, Nk=big, d=128) == 2
+    assert _fwd(lib, Nq=big, Nk=big, d=128) == 2
+    assert _fwd(lib, Nk=1 << 24, d=64) == 2        # 2^24 x 64 x 2 = 2^31
+    ws = lib.fa_bwd_workspace_bytes(1, 1, 8, big, 128)
+    assert lib.fa_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 1, 1, 8,
+                      big, 128, 0.125, 0, None) == 2
+    assert lib.fa_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 8, 1 << 24, 128, 0.125, 0,
+                          None) == 2
+    assert lib.fa_fwd_dropout(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 1 << 24, 128, 0.125, 0,
+                              0.1, 1, 0, None) == 2
+    # d_v wider than d: V's rows decide
+    assert lib.fa_fwd_dv(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 8, big, 64, 128, 0.125, 0,
+                         None) == 2
+    assert lib.fa_bwd_dv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 1, 1,
+                         8, big, 64, 128, 0.125, 0, None) == 2
+    wsd = lib.fa_decode_workspace_bytes(1, 1, 1 << 24, 128, 4)
+    assert lib.fa_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wsd, 1, 1, 1, 1 << 24, 128, 0.125,
+                         0, 4, None) == 2
+
+
 def test_bwd_validation(lib):
     ws = lib.fa_bwd_workspace_bytes(2, 3, 100, 50, 64)
     assert ws >= 2 * 3 * 100 * 4 and ws % 16 == 0

@@ -25,10 +25,13 @@ def _decode(fa, q16, k16, v16, splits=0, scale=None):
 @pytest.mark.parametrize("nk", [1, 7, 64, 1000, 4097, 20000])
 @pytest.mark.parametrize("splits", [0, 1, 2, 7, 16, 64])
 def test_decode_parity(gpu, d, nk, splits):
-    if splits > nk:
-        pytest.skip("more splits than keys is rejected by design")
     B, H = 2, 3
     q16, k16, v16 = inputs.qkv_bf16(50 + nk, B, H, 1, nk, d)
+    if splits > nk:  # more splits than keys: rejected before any launch
+        with pytest.raises(gpu.FaError) as e:
+            _decode(gpu, q16, k16, v16, splits)
+        assert e.value.status == 8  # FA_ERR_ARG
+        return
     o, lse = _decode(gpu, q16, k16, v16, splits)
     f = inputs.bf16_to_f64
     o_ref, l_ref = oracle.decode(f(q16), f(k16), f(v16), default_scale(d))

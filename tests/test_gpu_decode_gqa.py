@@ -47,9 +47,12 @@ CASES = [  # (B, H, H_kv, N_k, d)
 @pytest.mark.parametrize("splits", [0, 1, 7, 64])
 def test_decode_gqa_parity(gpu, case, splits):
     B, H, H_kv, Nk, d = case
-    if splits > Nk:
-        pytest.skip("more splits than positions is rejected by design")
     q16, k16, v16 = _case(90 + H + Nk, B, H, H_kv, Nk, d)
+    if splits > Nk:  # more splits than positions: rejected before any launch
+        with pytest.raises(gpu.FaError) as e:
+            _run(gpu, q16, k16, v16, splits)
+        assert e.value.status == 8  # FA_ERR_ARG
+        return
     o, lse = _run(gpu, q16, k16, v16, splits)
     o_ref, l_ref = _oracle(q16, k16, v16)
     assert_fwd_close(o, lse, o_ref, l_ref, f"decode_gqa {case} splits {splits}")

@@ -56,8 +56,11 @@ CASES = [  # (B, H, H_kv, d, block_size, seq_lens)
 def test_decode_paged_parity(gpu, case, splits):
     B, H, H_kv, d, bs, lens = case
     q16, kc, vc, table, sl = _case(70 + H + bs, B, H, H_kv, d, bs, lens)
-    if splits > table.shape[1] * bs:
-        pytest.skip("more splits than positions is rejected by design")
+    if splits > table.shape[1] * bs:  # more splits than positions: rejected before any launch
+        with pytest.raises(gpu.FaError) as e:
+            _run(gpu, q16, kc, vc, table, sl, splits)
+        assert e.value.status == 8  # FA_ERR_ARG
+        return
     o, lse = _run(gpu, q16, kc, vc, table, sl, splits)
     o_ref, l_ref = _oracle(q16, kc, vc, table, sl, default_scale(d))
     assert_fwd_close(o, lse, o_ref, l_ref, f"paged {case} C{splits}")

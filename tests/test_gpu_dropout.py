@@ -3,9 +3,10 @@
 on the same seeded inputs. With V the identity (N_k = d) the forward's output is P Z / (1 - p)
 itself, so the GPU's keep mask is compared bit for bit with the oracle's.
 
-Tolerances: the O bar (max abs 1e-2) is applied to (1 - p) O, the output before the inverted-
-dropout scale, because that scale multiplies every rounding error of O by 1 / (1 - p); the LSE
-and gradient bars (relative) are unchanged."""
+Tolerances: for p <= 0.5 the O bar (max abs 1e-2) is applied to O itself. At p = 0.9 it is
+applied to (1 - p) O, the output before the inverted-dropout scale: that scale multiplies O, and
+with it the bf16 step of every output element, by ten, so O's own rounding alone can exceed the
+bar. The LSE and gradient bars (relative) are unchanged."""
 from __future__ import annotations
 
 import numpy as np
@@ -18,6 +19,11 @@ from tests.helpers import GRAD_REL_FRO, assert_fwd_close, default_scale, from_de
 pytestmark = pytest.mark.gpu
 
 SEEDS = [(7, 0), (2**40 + 12345, 3), (0xFFFFFFFFFFFFFFFF, 2**32 - 1)]
+
+
+def o_factor(p: float) -> float:
+    """The factor O is compared under: 1 (O itself) for p <= 0.5, 1 - p above."""
+    return 1.0 if p <= 0.5 else 1.0 - p
 
 
 def _identity_v(B, H, n, d):
@@ -52,7 +58,8 @@ def test_dropout_mask_bitwise(gpu, si, p, causal, d):
             got = o[b, h] != 0.0
             assert np.array_equal(got, z & vis), (b, h, int(np.sum(got != (z & vis))))
     o_ref, l_ref = oracle.forward_dropout(f(q16), f(k16), f(v16), scale, causal, p, seed, offset)
-    assert_fwd_close(o * (1 - p), lse.cpu().numpy().astype(np.float64), o_ref * (1 - p), l_ref,
+    fo = o_factor(p)
+    assert_fwd_close(o * fo, lse.cpu().numpy().astype(np.float64), o_ref * fo, l_ref,
                      f"p{p} seed{si}")
 
 
@@ -72,7 +79,7 @@ def check_all(got, ins, scale, causal, p, seed, offset, what):
     f = inputs.bf16_to_f64
     q, k, v, do = (f(x) for x in ins)
     o_ref, l_ref = oracle.forward_dropout(q, k, v, scale, causal, p, seed, offset)
-    assert_fwd_close(got[0] * (1 - p), got[1], o_ref * (1 - p), l_ref, what)
+    assert_fwd_close(got[0] * o_factor(p), got[1], o_ref * o_factor(p), l_ref, what)
     ref = oracle.backward_dropout(q, k, v, do, scale, causal, p, seed, offset)
     for name, g, r in zip(("dQ", "dK", "dV"), got[2:], ref):
         assert np.all(np.isfinite(g)), f"{what}: non-finite {name}"
@@ -147,8 +154,8 @@ def test_dropout_full_size_head(gpu):
     sl = [f(x[b:b + 1, h:h + 1]) for x in (q16, k16, v16, do16)]
     ids = np.array([[b * H + h]])
     o_ref, l_ref = oracle.forward_dropout(*sl[:3], scale, True, p, seed, offset, head_ids=ids)
-    assert_fwd_close(from_dev(o[b:b + 1, h:h + 1]) * (1 - p),
-                     lse[b:b + 1, h:h + 1].cpu().numpy().astype(np.float64), o_ref * (1 - p),
+    assert_fwd_close(from_dev(o[b:b + 1, h:h + 1]) * o_factor(p),
+                     lse[b:b + 1, h:h + 1].cpu().numpy().astype(np.float64), o_ref * o_factor(p),
                      l_ref, "full-size head")
     ref = oracle.backward_dropout(*sl, scale, True, p, seed, offset, head_ids=ids)
     for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
