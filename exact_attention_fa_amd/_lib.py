@@ -31,6 +31,7 @@ SIGNATURES = {
     "fa_decode_num_splits": (_I, [_I, _I, _I, _I]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_decode_noalloc": (_I, [_P] * 5 + [_I] * 5 + [_F, _I, _I, _P]),
     "fa_fwd_dv": (_I, [_P] * 5 + [_I] * 6 + [_F, _I, _P]),
     "fa_bwd_dv": (_I, [_P] * 10 + [_Z] + [_I] * 6 + [_F, _I, _P]),
     "fa_fwd_gqa": (_I, [_P] * 5 + [_I] * 6 + [_F, _I, _P]),
@@ -240,6 +241,32 @@ def decode(q, k, v, scale: float | None = None, num_splits: int = 0, workspace=N
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           B, H, Nq, Nk, d, _scale(scale, d), 0, int(num_splits), _stream(q))
     _check("fa_decode", st)
+    return o, lse
+
+
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20  # FA_DECODE_NOALLOC_SCRATCH_BYTES of fa.h
+
+
+def decode_noalloc(q, k, v, scale: float | None = None, num_splits: int = 0, out=None):
+    """decode() with the split partials in the library's own device array instead of a
+    workspace: the library allocates nothing (pass out=(o, lse) to allocate nothing here either).
+    Calls that may overlap in time on one GPU race on that array."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _need(q, "q", (B, H, Nq, d), torch.bfloat16)
+    _need(k, "k", (B, H, Nk, d), torch.bfloat16)
+    _need(v, "v", (B, H, Nk, d), torch.bfloat16)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = _outs(out, [("o", (B, H, Nq, d), torch.bfloat16),
+                             ("lse", (B, H, Nq), torch.float32)])
+    st = load().fa_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), B, H, Nq, Nk, d, _scale(scale, d), 0,
+                                  int(num_splits), _stream(q))
+    _check("fa_decode_noalloc", st)
     return o, lse
 
 

@@ -34,6 +34,36 @@ size_t round_up16(size_t n) { return (n + 15) & ~size_t(15); }
 
 }  // namespace
 
+namespace fa {
+
+fa_status decode_validate(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                          const float* lse, int B, int H, int N_q, int N_k, int d, float scale,
+                          int causal, int num_splits, int* splits) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status s = check_common(B, H, N_q, N_k, d, scale, causal);
+  if (s != FA_OK) return s;
+  if (N_q != 1) return FA_ERR_ARG;
+  if (num_splits < 0 || num_splits > 1024 || num_splits > N_k) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  *splits = num_splits == 0 ? decode_auto_splits(B, H, N_k, d) : num_splits;
+  return FA_OK;
+}
+
+fa_status decode_run(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+                     void* workspace, int B, int H, int N_k, int d, float scale, int splits,
+                     hipStream_t stream) {
+  const size_t rows = (size_t)B * H * splits;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             round_up16(rows * d * sizeof(float)));
+  DecodeArgs a{bf(q), bf(k), bf(v), bf(o), lse, part_o, part_lse, B, H, N_k, d, splits, scale,
+               stream};
+  return from_hip(launch_decode(a));
+}
+
+}  // namespace fa
+
 extern "C" {
 
 const char* fa_status_string(fa_status s) {
@@ -157,24 +187,14 @@ size_t fa_decode_workspace_bytes(int B, int H, int N_k, int d, int num_splits) {
 fa_status fa_decode(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
                     void* workspace, size_t workspace_bytes, int B, int H, int N_q, int N_k,
                     int d, float scale, int causal, int num_splits, hipStream_t stream) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  fa_status s = check_common(B, H, N_q, N_k, d, scale, causal);
+  int c = 0;
+  const fa_status s =
+      fa::decode_validate(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, num_splits, &c);
   if (s != FA_OK) return s;
-  if (N_q != 1) return FA_ERR_ARG;
-  if (num_splits < 0 || num_splits > 1024 || num_splits > N_k) return FA_ERR_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-    return FA_ERR_ALIGN;
-  const int c = num_splits == 0 ? fa_decode_num_splits(B, H, N_k, d) : num_splits;
   if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, H, N_k, d, c))
     return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
-  const size_t rows = (size_t)B * H * c;
-  float* part_o = static_cast<float*>(workspace);
-  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             round_up16(rows * d * sizeof(float)));
-  fa::DecodeArgs a{bf(q), bf(k), bf(v), bf(o), lse, part_o, part_lse, B, H, N_k, d, c, scale,
-                   stream};
-  return from_hip(fa::launch_decode(a));
+  return fa::decode_run(q, k, v, o, lse, workspace, B, H, N_k, d, scale, c, stream);
 }
 
 int fa_decode_gqa_num_splits(int B, int H, int H_kv, int N_k, int d) {

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "fa.h"
+
 namespace fa {
 
 // Dropout on the attention probabilities (Philox-4x32-10 keyed by the 64-bit seed; the call
@@ -133,6 +135,17 @@ size_t bwd_part_offset(int B, int H, int Nq);
 hipError_t launch_bwd(const BwdArgs& a, unsigned phase_mask = 7u);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_decode_paged(const DecodePagedArgs& a);
+
+// fa_decode's argument checks (everything but the workspace); *splits receives the split count
+// the call uses (num_splits, or the automatic count for 0).
+fa_status decode_validate(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                          const float* lse, int B, int H, int N_q, int N_k, int d, float scale,
+                          int causal, int num_splits, int* splits);
+// Launches the split and combine kernels of a validated decode with its partials in `workspace`
+// (at least fa_decode_workspace_bytes(B, H, N_k, d, splits) bytes, 16-byte aligned).
+fa_status decode_run(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+                     void* workspace, int B, int H, int N_k, int d, float scale, int splits,
+                     hipStream_t stream);
 
 // Split count used by the decode when the caller passes 0.
 int decode_auto_splits(int B, int H, int Nk, int d);

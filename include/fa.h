@@ -279,6 +279,25 @@ fa_status fa_decode(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf1
                     int B, int H, int N_q, int N_k, int d, float scale, int causal,
                     int num_splits, hipStream_t stream);
 
+/* ---- Decode without allocation ----------------------------------------------------------------
+ *
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. fa_decode_noalloc is fa_decode (same arguments except
+ * the workspace, same kernels, same results bit for bit at the same split count) with the
+ * per-split partials in a device array that the library holds, one per GPU, until the process
+ * ends: FA_DECODE_NOALLOC_SCRATCH_BYTES (16 MiB). A call whose fa_decode_workspace_bytes(B, H,
+ * N_k, d, splits) exceeds it returns FA_ERR_WORKSPACE before anything is enqueued (pass a smaller
+ * num_splits, or use fa_decode). The call allocates nothing; its first call on a device looks up
+ * that device's array (FA_ERR_HIP if that fails), on the device that runs `stream`.
+ * Calls on one GPU share its array, which keeps the last call's partials: calls ordered on one
+ * stream are fine, calls that may overlap in time on one GPU (other streams, other threads)
+ * race and give undefined results.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+fa_status fa_decode_noalloc(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
+                            float* lse, int B, int H, int N_q, int N_k, int d, float scale,
+                            int causal, int num_splits, hipStream_t stream);
+
 /* ---- Decode with grouped-query heads, over a paged or a contiguous KV cache --------------------
  *
  * Page "Bellek Duvarının Fiziği", section "Duvarın Ötesi: KV Cache, Uzun Bağlam ve Yaklaşık

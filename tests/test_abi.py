@@ -302,6 +302,23 @@ def test_decode_validation(lib):
     assert call(d=32) == 3
 
 
+def test_decode_noalloc_validation(lib):
+    """fa_decode_noalloc validates like fa_decode and refuses, before any device call, a split
+    count whose partials exceed its fixed 16 MiB array."""
+    def call(q=FAKE, B=2, H=4, Nq=1, Nk=1000, d=128, splits=0):
+        return lib.fa_decode_noalloc(q, FAKE, FAKE, FAKE, FAKE, B, H, Nq, Nk, d, 0.125, 0,
+                                     splits, None)
+    assert call(q=None) == 1
+    assert call(Nq=2) == 8
+    assert call(splits=1001) == 8
+    assert call(d=96) == 3
+    assert call(q=FAKE + 2) == 4
+    # B8 H32 d128 at 1024 splits: 8 * 32 * 1024 * 129 * 4 bytes > 16 MiB
+    assert lib.fa_decode_workspace_bytes(8, 32, 65536, 128, 1024) > (16 << 20)
+    assert call(B=8, H=32, Nk=65536, splits=1024) == 6
+    assert lib.fa_decode_workspace_bytes(8, 32, 65536, 128, 16) <= (16 << 20)
+
+
 def test_decode_paged_validation(lib):
     # B8 H32 H_kv8, 512 blocks of 16 positions per sequence, d128
     c = lib.fa_decode_paged_num_splits(8, 32, 8, 512, 16, 128)
