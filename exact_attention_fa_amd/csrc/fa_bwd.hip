@@ -63,10 +63,10 @@ struct PaddedTile {
     }
   }
   // rows [row0, row0 + 64) of a [nrows][D] tensor starting at base (rows past nrows read as
-  // zero; the range covers at most the 64 rows of the tile)
+  // zero; one head spans fewer than 2^31 bytes, which the host checks)
   __device__ __forceinline__ void copy(const bf16* base, int row0, int nrows, unsigned char* dst,
                                       int wave) const {
-    const auto r = make_rsrc(base + (size_t)row0 * D, min(max(0, nrows - row0), 64) * D * 2);
+    const auto r = make_rsrc(base + (size_t)row0 * D, max(0, nrows - row0) * D * 2);
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i)
       if (wave + i * kNW < kCopies) buffer_to_lds(r, dst + (wave + i * kNW) * 1024, off[i]);
@@ -77,7 +77,7 @@ struct PaddedTile {
 __device__ __forceinline__ void copy_row_vec(const float* base, int row0, int nrows,
                                              unsigned char* dst, int lane) {
   if (lane < 16) {
-    const auto r = make_rsrc(base + row0, min(max(0, nrows - row0), 64) * 4);
+    const auto r = make_rsrc(base + row0, max(0, nrows - row0) * 4);
     buffer_to_lds(r, dst, lane * 16);
   }
 }

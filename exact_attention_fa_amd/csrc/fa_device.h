@@ -202,9 +202,13 @@ __device__ __forceinline__ void xcd_map(int bid, int BH, int G, int& bh, int& ra
 // ---- HBM/L2 -> LDS copies without register staging ------------------------------------------
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes return zero.
 // Word 3 is the gfx9-family raw-buffer configuration (32-bit data format, no swizzle).
+// `bytes` must be the same in every lane: it is read from the first active lane, so that the
+// resource stays in scalar registers (a range the compiler would compute on the vector ALU, e.g.
+// a clamp, would otherwise turn every load through it into a loop over distinct values).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 #else
   (void)base;
   (void)bytes;

@@ -338,7 +338,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     voff[i] = row * (int)Nkp + (ch < kBC8 / 16 ? ch : 0) * 16;
   }
   auto copy_k = [&](int t, unsigned char* dst) {
-    const int rows = min(max(0, Nk - t * kBC8), kBC8);  // rows past N_k read as zero
+    const int rows = max(0, Nk - t * kBC8);  // rows past N_k read as zero
     const auto r = make_rsrc(Kh + (size_t)t * kBC8 * D, rows * D);
 #pragma unroll
     for (int i = 0; i < KIW; ++i)

@@ -128,9 +128,9 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     voff[i] = row * DV * 2 + (ch < DV / 8 ? ch : 0) * 16;
   }
   auto tile_rsrc = [&](const bf16* base, int t, int w) {  // w: row width (elements)
-    // reads at or past the key length return zero; the range never exceeds one tile, so it
-    // stays far inside 32 bits whatever the length of the head
-    const int rows = min(max(0, nk - t * kBC), kBC);
+    // reads at or past the key length return zero (one head spans fewer than 2^31 bytes, which
+    // the host checks, so the range fits its 32 bits)
+    const int rows = max(0, nk - t * kBC);
     return make_rsrc(base + (size_t)t * kBC * w, rows * w * 2);
   };
   auto copy_k = [&](int t, unsigned char* dst) {
