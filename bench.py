@@ -53,6 +53,9 @@ FP8 = dict(incoherent=True, seed=0xF8)          # FP8 forward over the forward w
 BIAS = dict(seed=0xB1A5)  # additive bias [1, H, N, N] (shared by the batch), 2 N(0, 1) in bf16
 GQA = dict(H_kv=4)  # grouped query heads: the forward+backward workload with 4 K/V heads
 GEMM = dict(n=8192, seed=0x6E, reps=10)  # plain bf16 GEMM on random data: the sustained MFMA rate
+# matrix-core calibration loop: 2 workgroups of 4 waves per CU, 8 independent 32x32x16 bf16
+# accumulators per wave on random operands; iters per launch (about 30 ms)
+CALIB = dict(blocks=512, iters=100000, seed=0xCA1)
 
 
 def log(msg: str) -> None:
@@ -99,9 +102,15 @@ def measured_traffic() -> dict:
 def cpu_baseline(heads: int) -> dict:
     """The fp64 oracle (as it stands) on `heads` heads of the forward + backward workload."""
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=1)
+        if info:
+            blas = ", ".join(f"{i.get('internal_api', '?')} {i.get('version', '')} "
+                             f"({i.get('num_threads', '?')} threads)".replace("  ", " ")
+                             for i in info)
     except Exception:  # threadpoolctl missing: report the visible cores
         threads = os.cpu_count() or 1
     N, d = FB["N"], FB["d"]
@@ -120,6 +129,7 @@ def cpu_baseline(heads: int) -> dict:
     flops = (metrics.attention_flops(1, heads, N, N, d, causal=True)
              + metrics.attention_flops(1, heads, N, N, d, causal=True, backward=True))
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "blas": blas, "host_cpus": os.cpu_count(),
             "sample": f"fp64 numpy oracle, forward + backward of {heads} head(s) (b=0) of the "
                       f"causal B2 H16 N8192 d128 workload, {t:.1f} s; the oracle computes the full "
                       f"unmasked score matrix, the rate uses the same causal-halved formula"}
@@ -577,6 +587,47 @@ def main() -> int:
             e["frac_of_gemm"] = e["achieved"] / g_tf
     roof["frac_of_gemm"] = kernels[dominant].get("frac_of_gemm")
     del ga, gb, gc
+
+    # ---- the matrix cores' own ceiling on random bf16 operands, and the shader clock meanwhile
+    # (libfa_calib.so: a loop of independent 32x32x16 bf16 MFMAs, no memory traffic, timed by
+    # events; the clock from each wave's s_memtime against s_memrealtime at 100 MHz)
+    import ctypes
+    calib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_fa_amd", "libfa_calib.so"))
+    calib.fa_calib_mfma_bf16.restype = ctypes.c_int
+    calib.fa_calib_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    cb, ci = CALIB["blocks"], CALIB["iters"]
+    gen_c = torch.Generator(device=dev).manual_seed(CALIB["seed"])
+    c_ops = torch.randn((cb * 256 * 16 * 8,), generator=gen_c, device=dev).to(torch.bfloat16)
+    c_clk = torch.zeros((cb * 4, 4), dtype=torch.int64, device=dev)
+    c_sink = torch.empty((cb * 256,), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    run_c = lambda: calib.fa_calib_mfma_bf16(c_ops.data_ptr(), cb, ci, c_clk.data_ptr(),  # noqa: E731
+                                             c_sink.data_ptr(), stream)
+    if run_c() != 0:
+        raise RuntimeError("calibration loop failed to launch")
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    run_c()
+    c1.record()
+    torch.cuda.synchronize()
+    c_ms = c0.elapsed_time(c1)
+    c_tf = cb * 4 * ci * 8 * 2.0 * 32 * 32 * 16 / (c_ms * 1e-3) / 1e12
+    clk = c_clk.cpu().double()
+    mhz = float(((clk[:, 1] - clk[:, 0]) / (clk[:, 3] - clk[:, 2]) * 100.0).median())
+    log(f"MFMA loop on random bf16: {c_ms:.2f} ms, {c_tf:.0f} TFLOP/s at {mhz:.0f} MHz")
+    out["mfma_ceiling_bf16"] = {
+        "what": f"{cb} workgroups x 4 waves, each {ci} x 8 independent v_mfma_f32_32x32x16_bf16 "
+                "on random bf16 operands (no memory traffic)",
+        "tflops": c_tf, "frac_peak": c_tf / peak_tf, "clock_mhz": mhz,
+        "peak_at_clock": peak_tf * mhz / 2400.0}
+    for e in kernels.values():
+        if e["unit"] == "TFLOP/s" and e["peak"] == peak_tf:
+            e["frac_of_mfma_ceiling"] = e["achieved"] / c_tf
+    roof["frac_of_mfma_ceiling"] = kernels[dominant].get("frac_of_mfma_ceiling")
+    out["fwd_frac_of_mfma_ceiling"] = kernels["fwd"]["frac_of_mfma_ceiling"]
+    del c_ops, c_clk, c_sink
 
     if args.cpu_heads > 0:
         log(f"oracle CPU baseline on {args.cpu_heads} head(s) ...")
