@@ -13,7 +13,7 @@ listed, and `roofline` repeats the entry of the step's kernel that takes the mos
 entries are timed apart from the step: the decode with grouped query heads over a paged and
 over a contiguous cache, a
 causal forward + backward over a batch of eight sequences of different lengths (TFLOP/s of the
-valid rows and keys only), the forward + backward workload with dropout on P, with an additive
+valid rows and keys only), the same batch with 4 K/V heads and dropout as well, the forward + backward workload with dropout on P, with an additive
 bias, with d_v = 64 and with 4 K/V heads (grouped query heads), and the FP8 forward with
 incoherent processing (against the dense fp8 peak), and the forward alone on the other shapes
 (B1 H1 N256 d64; B4 H16 N2048 d128 with and without the causal mask; causal B1 H32 N32768 d128
@@ -49,6 +49,8 @@ PAGED = dict(H_kv=8, block_size=16, seed=9)  # paged GQA decode: the decode work
 VARLEN = dict(B=8, H=16, N=8192, d=128, n_min=1024, causal=True, seed=21)  # variable lengths,
                                              # uniform on [n_min, N], padded to N
 DROPOUT = dict(p=0.1, seed=0x5EED, offset=0)  # dropout on P over the forward+backward workload
+EXT = dict(H_kv=4, p=0.1, seed=0xE47, offset=0)  # the variable-length batch with grouped K/V
+                                                # heads and dropout together
 FP8 = dict(incoherent=True, seed=0xF8)          # FP8 forward over the forward workload
 BIAS = dict(seed=0xB1A5)  # additive bias [1, H, N, N] (shared by the batch), 2 N(0, 1) in bf16
 GQA = dict(H_kv=4)  # grouped query heads: the forward+backward workload with 4 K/V heads
@@ -391,7 +393,39 @@ def main() -> int:
     kernels["fwd_varlen"] = mfma_entry(vf_flops, vf_ms, vnote)
     kernels["bwd_varlen"] = mfma_entry(2.5 * vf_flops, vb_ms,
                                        vnote + "; preprocess + dK/dV + dQ, 2.5x the forward")
-    del vq, vk, vv, vdo, vo, vgrads, vws
+
+    # ---- the same batch with grouped K/V heads and dropout too (fa_fwd_ext / fa_bwd_ext): the
+    # first EXT["H_kv"] K/V heads shared by all query heads, dropout on P
+    eh = EXT["H_kv"]
+    ek, ev = vk[:, :eh].contiguous(), vv[:, :eh].contiguous()
+    egrads = (torch.empty_like(vq), torch.empty_like(ek), torch.empty_like(ev))
+    ews = torch.empty(fa.bwd_ext_workspace_bytes(VB, VH, eh, VN, VN, Vd), dtype=torch.uint8,
+                      device=dev)
+    ep, es, eo = EXT["p"], EXT["seed"], EXT["offset"]
+    run_ef = lambda: fa.fwd_ext(vq, ek, ev, vlens, vlens, ep, es, eo, causal=vc,  # noqa: E731
+                                out=(vo, vlse))
+    run_eb = lambda: fa.bwd_ext(vq, ek, ev, vo, vlse, vdo, vlens, vlens, ep, es, eo,  # noqa: E731
+                                causal=vc, workspace=ews, out=egrads)
+    for _ in range(max(args.warmup, 3)):
+        run_ef()
+        run_eb()
+    torch.cuda.synchronize()
+    eev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in eev:
+        e[0].record()
+        run_ef()
+        e[1].record()
+        run_eb()
+        e[2].record()
+    torch.cuda.synchronize()
+    ef_ms = sum(e[0].elapsed_time(e[1]) for e in eev) / len(eev)
+    eb_ms = sum(e[1].elapsed_time(e[2]) for e in eev) / len(eev)
+    log(f"varlen + GQA + dropout fwd {ef_ms:.3f} ms, bwd {eb_ms:.3f} ms")
+    enote = (vnote + f", {eh} K/V heads ({VH // eh} query heads each), dropout p = {ep}")
+    kernels["fwd_varlen_gqa_dropout"] = mfma_entry(vf_flops, ef_ms, enote)
+    kernels["bwd_varlen_gqa_dropout"] = mfma_entry(
+        2.5 * vf_flops, eb_ms, enote + "; preprocess + dK/dV + dQ, 2.5x the forward")
+    del vq, vk, vv, vdo, vo, vgrads, vws, ek, ev, egrads, ews
 
     # ---- dropout on P: the forward + backward workload again (timed on its own, outside the step)
     dp_, dseed, doff = DROPOUT["p"], DROPOUT["seed"], DROPOUT["offset"]

@@ -44,6 +44,9 @@ SIGNATURES = {
     "fa_fwd_dropout": (_I, [_P] * 5 + [_I] * 5 + [_F, _I, _F, _U64, _U32, _P]),
     "fa_bwd_dropout": (_I, [_P] * 10 + [_Z] + [_I] * 5 + [_F, _I, _F, _U64, _U32, _P]),
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_ext": (_I, [_P] * 7 + [_I] * 6 + [_F, _I, _F, _U64, _U32, _P]),
+    "fa_bwd_ext_workspace_bytes": (_Z, [_I] * 6),
+    "fa_bwd_ext": (_I, [_P] * 12 + [_Z] + [_I] * 6 + [_F, _I, _F, _U64, _U32, _P]),
     "fa_bwd_varlen": (_I, [_P] * 12 + [_Z, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_gqa_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "fa_decode_gqa_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
@@ -690,4 +693,76 @@ def bwd_gqa(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = N
                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                            B, H, Hkv, Nq, Nk, d, _scale(scale, d), int(bool(causal)), _stream(q))
     _check("fa_bwd_gqa", st)
+    return dq, dk, dv
+
+
+def fwd_ext(q, k, v, seq_lens_q=None, seq_lens_k=None, p_drop: float = 0.0, seed: int = 0,
+            offset: int = 0, causal: bool = False, scale: float | None = None, out=None):
+    """Forward with any subset of per-sequence lengths (int32 [B] on the GPU, both or neither),
+    grouped K/V heads (k/v [B,H_kv,Nk,d]) and dropout on P (p_drop > 0) -> (o, lse)."""
+    import torch
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _need(q, "q", (B, H, Nq, d), torch.bfloat16)
+    _need(k, "k", (B, Hkv, Nk, d), torch.bfloat16)
+    _need(v, "v", (B, Hkv, Nk, d), torch.bfloat16)
+    if (seq_lens_q is None) != (seq_lens_k is None):
+        raise ValueError("give both seq_lens_q and seq_lens_k, or neither")
+    if seq_lens_q is not None:
+        _lens(seq_lens_q, "seq_lens_q", B)
+        _lens(seq_lens_k, "seq_lens_k", B)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = _outs(out, [("o", (B, H, Nq, d), torch.bfloat16),
+                             ("lse", (B, H, Nq), torch.float32)])
+    lq = seq_lens_q.data_ptr() if seq_lens_q is not None else None
+    lk = seq_lens_k.data_ptr() if seq_lens_k is not None else None
+    st = load().fa_fwd_ext(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           lq, lk, B, H, Hkv, Nq, Nk, d, _scale(scale, d), int(bool(causal)),
+                           float(p_drop), int(seed) & (2**64 - 1), int(offset) & (2**32 - 1),
+                           _stream(q))
+    _check("fa_fwd_ext", st)
+    return o, lse
+
+
+def bwd_ext_workspace_bytes(B: int, H: int, H_kv: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load().fa_bwd_ext_workspace_bytes(B, H, H_kv, Nq, Nk, d))
+
+
+def bwd_ext(q, k, v, o, lse, dout, seq_lens_q=None, seq_lens_k=None, p_drop: float = 0.0,
+            seed: int = 0, offset: int = 0, causal: bool = False, scale: float | None = None,
+            workspace=None, out=None):
+    """Gradients (dq, dk, dv) of fwd_ext with the same options; dk, dv [B,H_kv,Nk,d] sum over
+    each group's query heads; padding rows and keys get zero gradients."""
+    import torch
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    for t, n, shp in ((q, "q", (B, H, Nq, d)), (k, "k", (B, Hkv, Nk, d)),
+                      (v, "v", (B, Hkv, Nk, d)), (o, "o", (B, H, Nq, d)),
+                      (dout, "dout", (B, H, Nq, d))):
+        _need(t, n, shp, torch.bfloat16)
+    _need(lse, "lse", (B, H, Nq), torch.float32)
+    if (seq_lens_q is None) != (seq_lens_k is None):
+        raise ValueError("give both seq_lens_q and seq_lens_k, or neither")
+    if seq_lens_q is not None:
+        _lens(seq_lens_q, "seq_lens_q", B)
+        _lens(seq_lens_k, "seq_lens_k", B)
+    workspace = _workspace(workspace, bwd_ext_workspace_bytes(B, H, Hkv, Nq, Nk, d), q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = _outs(out, [("dq", tuple(q.shape), torch.bfloat16),
+                                 ("dk", tuple(k.shape), torch.bfloat16),
+                                 ("dv", tuple(v.shape), torch.bfloat16)])
+    lq = seq_lens_q.data_ptr() if seq_lens_q is not None else None
+    lk = seq_lens_k.data_ptr() if seq_lens_k is not None else None
+    st = load().fa_bwd_ext(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), lq, lk,
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           B, H, Hkv, Nq, Nk, d, _scale(scale, d), int(bool(causal)),
+                           float(p_drop), int(seed) & (2**64 - 1), int(offset) & (2**32 - 1),
+                           _stream(q))
+    _check("fa_bwd_ext", st)
     return dq, dk, dv

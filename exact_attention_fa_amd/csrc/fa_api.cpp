@@ -522,4 +522,51 @@ fa_status fa_bwd_gqa(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const
                      0, H_kv);
 }
 
+fa_status fa_fwd_ext(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+                     const int32_t* seq_lens_q, const int32_t* seq_lens_k, int B, int H, int H_kv,
+                     int N_q, int N_k, int d, float scale, int causal, float p_drop,
+                     uint64_t seed, uint32_t offset, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  const bool varlen = seq_lens_q != nullptr || seq_lens_k != nullptr;
+  if (varlen && (!seq_lens_q || !seq_lens_k)) return FA_ERR_ARG;
+  fa_status s = check_common(B, H, N_q, N_k, d, scale, varlen ? 0 : causal);
+  if (s != FA_OK) return s;
+  if (H_kv < 1 || H % H_kv != 0) return FA_ERR_ARG;
+  fa::DropoutParams dp;
+  s = dropout_params(p_drop, seed, offset, &dp);
+  if (s != FA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  if (varlen && (!lens_ok(seq_lens_q) || !lens_ok(seq_lens_k))) return FA_ERR_ALIGN;
+  fa::FwdArgs a{bf(q), bf(k), bf(v), bf(o), lse, B, H, N_q, N_k, d, scale, causal != 0, stream,
+                seq_lens_q, seq_lens_k};
+  a.drop = dp;
+  a.Hkv = H_kv;
+  return from_hip(fa::launch_fwd(a));
+}
+
+size_t fa_bwd_ext_workspace_bytes(int B, int H, int H_kv, int N_q, int N_k, int d) {
+  return fa_bwd_gqa_workspace_bytes(B, H, H_kv, N_q, N_k, d);
+}
+
+fa_status fa_bwd_ext(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                     const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+                     const int32_t* seq_lens_q, const int32_t* seq_lens_k, void* workspace,
+                     size_t workspace_bytes, int B, int H, int H_kv, int N_q, int N_k, int d,
+                     float scale, int causal, float p_drop, uint64_t seed, uint32_t offset,
+                     hipStream_t stream) {
+  const bool varlen = seq_lens_q != nullptr || seq_lens_k != nullptr;
+  if (varlen && (!seq_lens_q || !seq_lens_k)) return FA_ERR_ARG;
+  if (varlen && (!lens_ok(seq_lens_q) || !lens_ok(seq_lens_k))) return FA_ERR_ALIGN;
+  if (H_kv < 1 || (H >= 1 && H % H_kv != 0)) return FA_ERR_ARG;
+  fa::DropoutParams dp;
+  const fa_status s = dropout_params(p_drop, seed, offset, &dp);
+  if (s != FA_OK) return s;
+  const size_t need = fa_bwd_ext_workspace_bytes(B, H, H_kv, N_q, N_k, d);
+  if (need != 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N_q,
+                     N_k, d, scale, causal, stream, 15u, 7u, varlen ? seq_lens_q : nullptr,
+                     varlen ? seq_lens_k : nullptr, &dp, nullptr, 0, H_kv);
+}
+
 }  // extern "C"

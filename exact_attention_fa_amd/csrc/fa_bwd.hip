@@ -998,11 +998,13 @@ hipError_t launch_d(const BwdArgs& a, unsigned phases) {
 
 template <int D>
 hipError_t launch_variant(const BwdArgs& a, unsigned phases) {
-  // per-sequence lengths, dropout and bias are separate variants (not combined)
+  // per-sequence lengths and dropout combine (with any grouping of the K/V heads); a bias runs
+  // on its own
   if (a.bias.ptr != nullptr) return launch_d<D, false, false, true>(a, phases);
-  if (a.drop.thresh < 65536u) return launch_d<D, false, true, false>(a, phases);
-  return a.lens_q != nullptr ? launch_d<D, true, false, false>(a, phases)
-                             : launch_d<D, false, false, false>(a, phases);
+  const bool vl = a.lens_q != nullptr, drop = a.drop.thresh < 65536u;
+  if (drop)
+    return vl ? launch_d<D, true, true, false>(a, phases) : launch_d<D, false, true, false>(a, phases);
+  return vl ? launch_d<D, true, false, false>(a, phases) : launch_d<D, false, false, false>(a, phases);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, unsigned phases) {

@@ -389,11 +389,12 @@ hipError_t launch_d(const FwdArgs& a) {
 
 template <int D>
 hipError_t launch_variant(const FwdArgs& a) {
-  // per-sequence lengths, dropout and bias are separate variants (not combined)
+  // per-sequence lengths and dropout combine (with any grouping of the K/V heads); a bias runs
+  // on its own
   if (a.bias.ptr != nullptr) return launch_d<D, false, false, true>(a);
-  if (a.drop.thresh < 65536u) return launch_d<D, false, true, false>(a);
-  return a.lens_q != nullptr ? launch_d<D, true, false, false>(a)
-                             : launch_d<D, false, false, false>(a);
+  const bool vl = a.lens_q != nullptr, drop = a.drop.thresh < 65536u;
+  if (drop) return vl ? launch_d<D, true, true, false>(a) : launch_d<D, false, true, false>(a);
+  return vl ? launch_d<D, true, false, false>(a) : launch_d<D, false, false, false>(a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {

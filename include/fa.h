@@ -256,6 +256,36 @@ fa_status fa_bwd_varlen(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, co
                         void* workspace, size_t workspace_bytes, int B, int H, int N_q, int N_k,
                         int d, float scale, int causal, hipStream_t stream);
 
+/* ---- Variable lengths, grouped K/V heads and dropout, together -------------------------------
+ *
+ * One call with any subset of three options, each meaning what its own entry point above
+ * documents (the training step of a batch of packed sequences needs all three at once, [MW]
+ * "Maskeleme ve Dropout" and "Duvarın Ötesi: KV Cache, Uzun Bağlam ve Yaklaşık Attention"):
+ *   seq_lens_q, seq_lens_k  per-sequence lengths in the padded layout, as fa_fwd_varlen (device
+ *                           int32 [B], 4-byte aligned); both NULL: every sequence is N_q x N_k
+ *                           (one NULL and not the other: FA_ERR_ARG);
+ *   H_kv                    key/value heads, as fa_fwd_gqa: k, v, dk, dv [B, H_kv, N_k, d], H a
+ *                           multiple of H_kv (else FA_ERR_ARG); H_kv = H: one per query head;
+ *   p_drop, seed, offset    dropout on P, as fa_fwd_dropout; p_drop = 0: none. The keep mask of
+ *                           (i, j) is drawn for query head b H + h and the row and key indices of
+ *                           the padded layout, which are the sequence's own indices.
+ * Without lengths causal needs N_q <= N_k (FA_ERR_CAUSAL); with them any N_q, N_k. The backward
+ * needs the forward's (seq_lens, H_kv, p_drop, seed, offset) and a workspace of at least
+ * fa_bwd_ext_workspace_bytes(B, H, H_kv, N_q, N_k, d) bytes (0 for invalid sizes). A bias and
+ * d_v != d are not among the options. Other arguments and errors as for fa_fwd / fa_bwd.
+ */
+fa_status fa_fwd_ext(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+                     const int32_t* seq_lens_q, const int32_t* seq_lens_k, int B, int H, int H_kv,
+                     int N_q, int N_k, int d, float scale, int causal, float p_drop,
+                     uint64_t seed, uint32_t offset, hipStream_t stream);
+size_t fa_bwd_ext_workspace_bytes(int B, int H, int H_kv, int N_q, int N_k, int d);
+fa_status fa_bwd_ext(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                     const float* lse, const fa_bf16* dout, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+                     const int32_t* seq_lens_q, const int32_t* seq_lens_k, void* workspace,
+                     size_t workspace_bytes, int B, int H, int H_kv, int N_q, int N_k, int d,
+                     float scale, int causal, float p_drop, uint64_t seed, uint32_t offset,
+                     hipStream_t stream);
+
 /* The split count fa_decode uses when called with num_splits = 0. */
 int fa_decode_num_splits(int B, int H, int N_k, int d);
 

@@ -16,6 +16,7 @@ import os
 import numpy as np
 
 import oracle.attention as A
+import oracle.combined as OC
 import oracle.dropout as DR
 import oracle.fp8 as F8
 
@@ -896,6 +897,126 @@ def pin_gqa_gradients():
                                        atol=1e-12)
 
 
+def _combined_case(rng, B=2, H=4, H_kv=2, n_q=9, n_k=13, d=8):
+    q = rng.standard_normal((B, H, n_q, d))
+    k = rng.standard_normal((B, H_kv, n_k, d))
+    v = rng.standard_normal((B, H_kv, n_k, d))
+    do = rng.standard_normal((B, H, n_q, d))
+    return q, k, v, do
+
+
+def pin_combined_brute_force():
+    """Variable lengths + grouped K/V heads + dropout by direct loops with math.exp: row i of
+    sequence b, query head h sees keys j < l_k (and j <= i + l_k - l_q when causal) of K/V head
+    h // (H / H_kv); o_i = sum_j exp(s_j - m) z_j v_j / ((1 - p) sum_j exp(s_j - m)) with z the
+    keep mask of query head b H + h; rows past l_q or with no key are o = 0, lse = -inf."""
+    rng = _rng(40)
+    q, k, v, _ = _combined_case(rng)
+    B, H, n_q, d = q.shape
+    H_kv, n_k = k.shape[1], k.shape[2]
+    lens_q, lens_k = [9, 6], [13, 4]
+    sc, pd, seed, off = 0.4, 0.3, 2**36 + 5, 7
+    for causal in (False, True):
+        o, lse = OC.forward_combined(q, k, v, lens_q, lens_k, sc, causal, pd, seed, off)
+        for b in range(B):
+            lq, lk = lens_q[b], lens_k[b]
+            for h in range(H):
+                g = h // (H // H_kv)
+                z = DR.dropout_keep(seed, off, b * H + h, lq, lk, pd)
+                for i in range(n_q):
+                    js = [j for j in range(lk) if i < lq and (not causal or j <= i + lk - lq)]
+                    if not js:
+                        assert np.all(o[b, h, i] == 0) and lse[b, h, i] == -np.inf
+                        continue
+                    s_ = [sc * sum(q[b, h, i, t] * k[b, g, j, t] for t in range(d)) for j in js]
+                    mx = max(s_)
+                    e = [math.exp(x - mx) for x in s_]
+                    zs = sum(e)
+                    for t in range(d):
+                        ref = sum(e[a] * z[i, j] * v[b, g, j, t] for a, j in enumerate(js))
+                        ref /= (1 - pd) * zs
+                        assert abs(o[b, h, i, t] - ref) <= 1e-12 * (1 + abs(ref))
+                    assert abs(lse[b, h, i] - (mx + math.log(zs))) <= 1e-12 * (1 + abs(mx))
+
+
+def pin_combined_reductions():
+    """With one feature or none the combined oracle is the pinned function for it: full lengths,
+    H_kv = H and p = 0 give forward / backward; lengths alone forward_varlen / backward_varlen;
+    grouping alone forward_gqa / backward_gqa; dropout alone forward_dropout / backward_dropout;
+    grouped K/V heads give what K/V repeated for every query head give, with the K/V gradients
+    of each group summed."""
+    rng = _rng(41)
+    sc, pd, seed, off = 0.35, 0.25, 77, 3
+    lq, lk = [7, 11], [11, 5]
+    for causal in (False, True):
+        q, k, v, do = _combined_case(rng, H=3, H_kv=3, n_q=11, n_k=11)
+        fw = OC.forward_combined(q, k, v, None, None, sc, causal, 0.0, 0, 0)
+        ref = A.forward(q, k, v, sc, causal)
+        assert all(np.allclose(x, y, rtol=1e-13, atol=1e-13) for x, y in zip(fw, ref))
+        bw = OC.backward_combined(q, k, v, do, None, None, sc, causal, 0.0, 0, 0)
+        ref = A.backward(q, k, v, do, sc, causal)
+        assert all(np.allclose(x, y, rtol=1e-12, atol=1e-12) for x, y in zip(bw, ref))
+        fw = OC.forward_combined(q, k, v, lq, lk, sc, causal, 0.0, 0, 0)
+        ref = A.forward_varlen(q, k, v, lq, lk, sc, causal)
+        assert np.allclose(fw[0], ref[0], rtol=1e-13, atol=1e-13)
+        assert np.array_equal(np.isinf(fw[1]), np.isinf(ref[1]))
+        assert np.allclose(fw[1][np.isfinite(fw[1])], ref[1][np.isfinite(ref[1])], rtol=1e-13)
+        bw = OC.backward_combined(q, k, v, do, lq, lk, sc, causal, 0.0, 0, 0)
+        ref = A.backward_varlen(q, k, v, do, lq, lk, sc, causal)
+        assert all(np.allclose(x, y, rtol=1e-12, atol=1e-12) for x, y in zip(bw, ref))
+        fw = OC.forward_combined(q, k, v, None, None, sc, causal, pd, seed, off)
+        ref = DR.forward_dropout(q, k, v, sc, causal, pd, seed, off)
+        assert all(np.allclose(x, y, rtol=1e-13, atol=1e-13) for x, y in zip(fw, ref))
+        bw = OC.backward_combined(q, k, v, do, None, None, sc, causal, pd, seed, off)
+        ref = DR.backward_dropout(q, k, v, do, sc, causal, pd, seed, off)
+        assert all(np.allclose(x, y, rtol=1e-12, atol=1e-12) for x, y in zip(bw, ref))
+        q, k, v, do = _combined_case(rng, H=6, H_kv=2, n_q=9, n_k=13)
+        fw = OC.forward_combined(q, k, v, None, None, sc, causal, 0.0, 0, 0)
+        ref = A.forward_gqa(q, k, v, sc, causal)
+        assert all(np.allclose(x, y, rtol=1e-13, atol=1e-13) for x, y in zip(fw, ref))
+        bw = OC.backward_combined(q, k, v, do, None, None, sc, causal, 0.0, 0, 0)
+        ref = A.backward_gqa(q, k, v, do, sc, causal)
+        assert all(np.allclose(x, y, rtol=1e-12, atol=1e-12) for x, y in zip(bw, ref))
+        # all three: grouped K/V against K/V repeated per query head
+        lq2, lk2 = [9, 4], [13, 8]
+        kr, vr = np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1)
+        fw = OC.forward_combined(q, k, v, lq2, lk2, sc, causal, pd, seed, off)
+        fr = OC.forward_combined(q, kr, vr, lq2, lk2, sc, causal, pd, seed, off)
+        assert np.array_equal(fw[0], fr[0]) and np.array_equal(fw[1], fr[1])
+        bw = OC.backward_combined(q, k, v, do, lq2, lk2, sc, causal, pd, seed, off)
+        br = OC.backward_combined(q, kr, vr, do, lq2, lk2, sc, causal, pd, seed, off)
+        assert np.allclose(bw[0], br[0], rtol=1e-13, atol=1e-13)
+        for x, y in zip(bw[1:], br[1:]):
+            assert np.allclose(x, y.reshape(2, 2, 3, 13, 8).sum(axis=2), rtol=1e-12, atol=1e-12)
+
+
+def pin_combined_finite_differences():
+    """Central differences of f = sum(dO * O) through Q, the shared K and V, with variable
+    lengths and dropout (mask fixed) against backward_combined, padding entries included (their
+    gradient is zero)."""
+    rng = _rng(42)
+    q, k, v, do = _combined_case(rng, B=2, H=4, H_kv=2, n_q=6, n_k=7, d=4)
+    lq, lk = [6, 3], [7, 5]
+    sc, pd, seed, off = 0.5, 0.3, 12345, 1
+    for causal in (False, True):
+        grads = OC.backward_combined(q, k, v, do, lq, lk, sc, causal, pd, seed, off)
+
+        def f(q_, k_, v_):
+            o, _ = OC.forward_combined(q_, k_, v_, lq, lk, sc, causal, pd, seed, off)
+            return float(np.sum(do * o))
+        h = 1e-6
+        for which, x, gx in ((0, q, grads[0]), (1, k, grads[1]), (2, v, grads[2])):
+            for idx in [tuple(rng.integers(0, n) for n in x.shape) for _ in range(12)]:
+                old = x[idx]
+                x[idx] = old + h
+                fp = f(q, k, v)
+                x[idx] = old - h
+                fm = f(q, k, v)
+                x[idx] = old
+                fd = (fp - fm) / (2 * h)
+                assert abs(fd - gx[idx]) <= 1e-6 * (1 + abs(fd)), (causal, which, idx, fd, gx[idx])
+
+
 ALL_PINS = [pin_brute_force_rows, pin_rows_sum_to_one, pin_causal_future_invariance,
             pin_finite_differences, pin_closed_forms, pin_invariances, pin_gradient_sum_rules,
             pin_torch_sdpa, pin_hand_examples, pin_decode_split_combine,
@@ -906,4 +1027,5 @@ ALL_PINS = [pin_brute_force_rows, pin_rows_sum_to_one, pin_causal_future_invaria
             pin_dropout_expectation_and_identities, pin_dropout_finite_differences,
             pin_e4m3_against_torch, pin_hadamard_rotation, pin_fp8_quantization, pin_fp8_o_tolerance,
             pin_fp8_forward_brute_force, pin_fp8_incoherent_claim, pin_bias_brute_force,
-            pin_bias_special_cases, pin_gqa_closed_form, pin_gqa_gradients]
+            pin_bias_special_cases, pin_gqa_closed_form, pin_gqa_gradients,
+            pin_combined_brute_force, pin_combined_reductions, pin_combined_finite_differences]

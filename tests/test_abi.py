@@ -302,6 +302,31 @@ def test_decode_validation(lib):
     assert call(d=32) == 3
 
 
+def test_ext_validation(lib):
+    """fa_fwd_ext / fa_bwd_ext: lengths both or neither, H a multiple of H_kv, p_drop in [0, 1),
+    causal N_q > N_k only with lengths, the workspace of fa_bwd_ext_workspace_bytes."""
+    def fwd(lq=FAKE, lk=FAKE, Hkv=2, Nq=8, Nk=8, causal=1, p=0.1, q=FAKE):
+        return lib.fa_fwd_ext(q, FAKE, FAKE, FAKE, FAKE, lq, lk, 2, 4, Hkv, Nq, Nk, 64, 0.125,
+                              causal, p, 1, 0, None)
+    assert fwd(q=None) == 1
+    assert fwd(lk=None) == 8 and fwd(lq=None) == 8
+    assert fwd(Hkv=3) == 8 and fwd(Hkv=0) == 8
+    assert fwd(p=1.0) == 8 and fwd(p=-0.1) == 8
+    assert fwd(lq=None, lk=None, Nq=9, Nk=8) == 5
+    assert fwd(lq=FAKE + 2) == 4
+    ws = lib.fa_bwd_ext_workspace_bytes(2, 4, 2, 8, 8, 64)
+    assert ws >= lib.fa_bwd_workspace_bytes(2, 4, 8, 8, 64) and ws % 16 == 0
+    assert lib.fa_bwd_ext_workspace_bytes(2, 4, 3, 8, 8, 64) == 0
+
+    def bwd(ws_bytes=ws, lk=FAKE, Hkv=2, p=0.1):
+        return lib.fa_bwd_ext(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, lk,
+                              FAKE, ws_bytes, 2, 4, Hkv, 8, 8, 64, 0.125, 1, p, 1, 0, None)
+    assert bwd(ws_bytes=ws - 16) == 6
+    assert bwd(lk=None) == 8
+    assert bwd(Hkv=3) == 8
+    assert bwd(p=2.0) == 8
+
+
 def test_decode_noalloc_validation(lib):
     """fa_decode_noalloc validates like fa_decode and refuses, before any device call, a split
     count whose partials exceed its fixed 16 MiB array."""

@@ -381,6 +381,45 @@ def _bwd_gqa_last_head_only(q, k, v, do, scale, causal):
     return dq, dk, dv
 
 
+import oracle.combined as OC  # noqa: E402
+
+_orig_fwd_comb = OC.forward_combined
+_orig_bwd_comb = OC.backward_combined
+
+
+def _fwd_comb_mask_of_kv_head(q, k, v, seq_lens_q, seq_lens_k, scale, causal, p, seed, offset):
+    # the keep mask drawn for the key/value head instead of the query head
+    B, H = np.shape(q)[:2]
+    H_kv = np.shape(k)[1]
+    saved = DR.dropout_keep
+    DR.dropout_keep = lambda sd, off, bh, n_q, n_k, p_: saved(
+        sd, off, (bh // H) * H_kv + (bh % H) // (H // H_kv), n_q, n_k, p_)
+    try:
+        return _orig_fwd_comb(q, k, v, seq_lens_q, seq_lens_k, scale, causal, p, seed, offset)
+    finally:
+        DR.dropout_keep = saved
+
+
+def _bwd_comb_last_head_only(q, k, v, do, seq_lens_q, seq_lens_k, scale, causal, p, seed, offset):
+    # the key/value gradients overwritten by each query head instead of summed over the group
+    H, H_kv = np.shape(q)[1], np.shape(k)[1]
+    G = H // H_kv
+    dq, dk, dv = _orig_bwd_comb(q, k, v, do, seq_lens_q, seq_lens_k, scale, causal, p, seed,
+                                offset)
+    keep = [h for h in range(H) if h % G == G - 1]
+    _, dk1, dv1 = _orig_bwd_comb(q[:, keep], k, v, do[:, keep], seq_lens_q, seq_lens_k, scale,
+                                 causal, p, seed, offset)
+    return dq, dk1, dv1
+
+
+def _fwd_comb_first_lengths(q, k, v, seq_lens_q, seq_lens_k, scale, causal, p, seed, offset):
+    # every sequence given the lengths of the first one
+    B = np.shape(q)[0]
+    lq = None if seq_lens_q is None else [seq_lens_q[0]] * B
+    lk = None if seq_lens_k is None else [seq_lens_k[0]] * B
+    return _orig_fwd_comb(q, k, v, lq, lk, scale, causal, p, seed, offset)
+
+
 MUTANTS = {
     "gqa_head_modulo_fwd": ("forward_gqa", _fwd_gqa_head_modulo),
     "gqa_bwd_not_summed": ("backward_gqa", _bwd_gqa_last_head_only),
@@ -421,6 +460,9 @@ MUTANTS = {
     "bwd_dk_no_scale": ("backward_head", _bwd_factory("dk_no_scale")),
     "bwd_dv_no_transpose": ("backward_head", _bwd_factory("dv_no_transpose")),
     "bwd_dq_uses_v": ("backward_head", _bwd_factory("dq_uses_v")),
+    "combined_mask_of_kv_head": ("forward_combined", _fwd_comb_mask_of_kv_head, OC),
+    "combined_dkdv_not_summed": ("backward_combined", _bwd_comb_last_head_only, OC),
+    "combined_first_lengths": ("forward_combined", _fwd_comb_first_lengths, OC),
 }
 
 
