@@ -36,6 +36,22 @@ size_t round_up16(size_t n) { return (n + 15) & ~size_t(15); }
 
 namespace fa {
 
+int xcd_head_group(size_t bytes_per_head, long long heads) {
+  // Measured on causal workloads (rows per head streamed by each workgroup, heads per XCD):
+  //   B8 H16 d128, eight sequences of 1363..8174 positions (4 MiB, 16): forward 1.075 / 0.986 /
+  //     0.972 / 1.201 ms and backward 3.33 / 2.95 / 2.89 / 3.48 ms with all of an XCD's heads /
+  //     1 / 2 / 4 at a time;
+  //   B1 H64 N32768 d64 (8 MiB, 8): forward 11.02 ms with all, 10.13 ms with 2;
+  //   B2 H16 N8192 d128 (4 MiB, 4): 0.525 ms with all, 0.532 ms with 2;
+  //   B4 H16 N2048 d128 (1 MiB, 8): 0.090 ms with all, 0.107 ms with 2.
+  // Grouping pays once an XCD's heads stream more than its share of the 256 MiB last-level
+  // cache (32 MiB); then two heads at a time, or as many as fit in about 2 MiB.
+  const long long per_xcd = (heads + 7) / 8;
+  if ((double)per_xcd * (double)bytes_per_head <= (double)(32u << 20)) return 1 << 20;
+  const size_t n = bytes_per_head ? ((size_t)2 << 20) / bytes_per_head : 2;
+  return (int)(n < 2 ? 2 : (n > (1u << 20) ? (1u << 20) : n));
+}
+
 fa_status decode_validate(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
                           const float* lse, int B, int H, int N_q, int N_k, int d, float scale,
                           int causal, int num_splits, int* splits) {

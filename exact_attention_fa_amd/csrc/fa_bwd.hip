@@ -200,7 +200,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
     bf16* __restrict__ dK, bf16* __restrict__ dV, const int* __restrict__ lens_q,
     const int* __restrict__ lens_k, int BH, int H, int G, int GL, float* __restrict__ pK,
     float* __restrict__ pV, int Nq, int Nk, float c, float scale, DropoutParams drop,
-    BiasParams bias) {
+    BiasParams bias, int hg) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using SM = DkdvLds<D, DV>;
   constexpr int ST = SM::ST, STO = SM::STO;
@@ -221,7 +221,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   // GL = 1 (pK != nullptr) each query head's contribution goes to fp32 partial rows pK, pV
   // (row bh of [B H, N_k]) that bwd_gqa_reduce_kernel adds up.
   int u, rank;
-  xcd_map(blockIdx.x, BH / GL, G / GL, u, rank);
+  xcd_map(blockIdx.x, BH / GL, G / GL, (Nk + kBKV - 1) / kBKV, hg, u, rank);
   const int kvbh = u * GL / G;
   const int bseq = u * GL / H;  // batch index
   const int k0 = rank * kBKV;  // causal: low key tiles see the most queries and go first
@@ -673,7 +673,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
     const bf16* __restrict__ dO, const float* __restrict__ NLs, const float* __restrict__ ND,
     bf16* __restrict__ dQ, const int* __restrict__ lens_q, const int* __restrict__ lens_k,
     int BH, int H, int G, int Nq, int Nk, float c, float scale, DropoutParams drop,
-    BiasParams bias) {
+    BiasParams bias, int hg) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using SM = DqLds<D, DV>;
   // one array per buffer: the LDS copies into one buffer then provably do not alias the reads of
@@ -688,7 +688,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
 
   const int nqt = (Nq + kBR - 1) / kBR;
   int bh, rank;
-  xcd_map(blockIdx.x, BH, G, bh, rank);
+  xcd_map(blockIdx.x, BH, G, (Nq + kBR - 1) / kBR, hg, bh, rank);
   const int qt = CAUSAL ? nqt - 1 - rank : rank;
   const int q0 = qt * kBR;
   const int qw = q0 + wave * 32;
@@ -932,6 +932,8 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
   const bool partial =
       !split && !VL && !DROP && !BIAS && D == DV && bwd_gqa_uses_partials(a.B, a.H, a.H / G, a.Nk);
   const int GL = partial ? 1 : G;
+  // dK/dV workgroups stream the Q and dO rows of the query heads of their unit (GL of them)
+  const int hg_kv = xcd_head_group((size_t)GL * a.Nq * (D + DV) * 2, (long long)BH / GL);
   float* pK = partial ? a.delta + bwd_part_offset(a.B, a.H, a.Nq) : nullptr;
   float* pV = partial ? pK + (size_t)BH * a.Nk * D : nullptr;
   if (phases & 2u) {
@@ -940,14 +942,14 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, split ? kDvOnly : kDkDv, BIAS, DV>),
                        dim3((unsigned)grid), dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, nls,
                        a.delta, a.dk, a.dv, a.lens_q, a.lens_k, BH, a.H, G, GL, pK, pV, a.Nq, a.Nk, c, a.scale,
-                       a.drop, a.bias);
+                       a.drop, a.bias, hg_kv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (split) {
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VL, DROP, kDkOnly, BIAS, DV>),
                          dim3((unsigned)grid), dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, nls,
                          a.delta, a.dk, a.dv, a.lens_q, a.lens_k, BH, a.H, G, GL, pK, pV, a.Nq, a.Nk, c, a.scale,
-                         a.drop, a.bias);
+                         a.drop, a.bias, hg_kv);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -966,7 +968,8 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VL, DROP, BIAS, DV>), dim3((unsigned)grid),
                        dim3(kNT), 0, a.stream, a.q, a.k, a.v, a.dout, nls, a.delta, a.dq, a.lens_q,
-                       a.lens_k, BH, a.H, G, a.Nq, a.Nk, c, a.scale, a.drop, a.bias);
+                       a.lens_k, BH, a.H, G, a.Nq, a.Nk, c, a.scale, a.drop, a.bias,
+                       xcd_head_group((size_t)a.Nk * (D + DV) * 2, (long long)BH / G));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

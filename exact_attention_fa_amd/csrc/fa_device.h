@@ -180,19 +180,27 @@ __device__ __forceinline__ bf16x8 lds_read_transposed(const unsigned char* tile,
 }
 
 // ---- workgroup -> (head, tile rank) -------------------------------------------------------
-// For a grid of BH * nt workgroups over BH query heads that come in groups of G consecutive heads
-// sharing one K/V head (G = 1: every head has its own). Workgroups are dealt to the 8 XCDs round
-// robin (XCD = blockIdx & 7), each XCD with its own L2. With the number of K/V heads BH / G a
-// multiple of 8, XCD x serves the query heads of K/V heads x, x + 8, ... only, so all tiles that
-// read one K/V head meet in one L2; inside an XCD the workgroups go rank by rank (rank 0 first:
-// the longest tiles of the causal kernels).
-__device__ __forceinline__ void xcd_map(int bid, int BH, int G, int& bh, int& rank) {
+// For a grid of BH * nt workgroups over BH query heads of nt tiles each, the query heads coming
+// in groups of G consecutive heads that share one K/V head (G = 1: every head has its own).
+// Workgroups are dealt to the 8 XCDs round robin (XCD = blockIdx & 7), each XCD with its own L2.
+// With the number of K/V heads BH / G a multiple of 8, XCD x serves the query heads of K/V heads
+// x, x + 8, ... only, so all tiles that read one K/V head meet in one L2. Inside an XCD its K/V
+// heads are taken hg at a time (hg >= 1), and the workgroups of such a head group go rank by rank
+// (rank 0 first: the longest tiles of the causal kernels), so that the workgroups running at
+// once stream the K/V (or Q/dO) tiles of few heads and find them in the L2.
+__device__ __forceinline__ void xcd_map(int bid, int BH, int G, int nt, int hg, int& bh,
+                                        int& rank) {
   const int BHkv = BH / G;
   if ((BHkv & 7) == 0) {
-    const int xcd = bid & 7, local = bid >> 3, per = (BHkv >> 3) * G;  // query heads per XCD
-    rank = local / per;
-    const int rem = local - rank * per;
-    bh = ((rem / G) * 8 + xcd) * G + rem % G;
+    const int xcd = bid & 7, local = bid >> 3, nkv = BHkv >> 3;  // K/V heads on this XCD
+    const int hgc = min(max(hg, 1), nkv);
+    const int grp = local / (hgc * G * nt);
+    const int in = local - grp * (hgc * G * nt);
+    const int kv0 = grp * hgc;
+    const int per = min(hgc, nkv - kv0) * G;  // query heads in this group (the last may be short)
+    rank = in / per;
+    const int rem = in - rank * per;
+    bh = ((kv0 + rem / G) * 8 + xcd) * G + rem % G;
   } else {
     bh = bid % BH;
     rank = bid / BH;

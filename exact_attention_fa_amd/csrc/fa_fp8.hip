@@ -308,7 +308,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
 
   const int nqt = (Nq + BR - 1) / BR;
   int bh, rank;
-  xcd_map(blockIdx.x, BH, 1, bh, rank);
+  xcd_map(blockIdx.x, BH, 1, (Nq + BR - 1) / BR, 1 << 30, bh, rank);
   const int qt = CAUSAL ? nqt - 1 - rank : rank;
   const int q0 = qt * BR;
   const int qw = q0 + wave * 32;

@@ -72,7 +72,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int* __restrict__ lens_q,
     const int* __restrict__ lens_k, int BH, int H, int G, int Nq, int Nk, float c,
-    DropoutParams drop, BiasParams bias) {
+    DropoutParams drop, BiasParams bias, int hg) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using L = FwdLds<D, DV>;
   constexpr int BR = NW * 32;  // query rows per workgroup
@@ -89,10 +89,10 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
   const int l32 = lane & 31, hi = lane >> 5;
 
   // ---- workgroup -> (b*h, query tile): longest causal tiles first, all tiles that read one K/V
-  // head on one XCD (xcd_map).
+  // head on one XCD, K/V heads taken hg at a time (xcd_map).
   const int nqt = (Nq + BR - 1) / BR;
   int bh, rank;
-  xcd_map(blockIdx.x, BH, G, bh, rank);
+  xcd_map(blockIdx.x, BH, G, nqt, hg, bh, rank);
   const int qt = CAUSAL ? nqt - 1 - rank : rank;
   const int q0 = qt * BR;
   const int qw = q0 + wave * 32;  // first query row of this wave
@@ -367,7 +367,9 @@ hipError_t launch(const FwdArgs& a) {
   const float c = a.scale * kLog2e;
   hipLaunchKernelGGL((fwd_kernel<D, DV, NW, CAUSAL, VL, DROP, BIAS>), dim3((unsigned)grid),
                      dim3(NW * 64), 0, a.stream, a.q, a.k, a.v, a.o, a.lse, a.lens_q, a.lens_k,
-                     a.B * a.H, a.H, a.Hkv ? a.H / a.Hkv : 1, a.Nq, a.Nk, c, a.drop, a.bias);
+                     a.B * a.H, a.H, a.Hkv ? a.H / a.Hkv : 1, a.Nq, a.Nk, c, a.drop, a.bias,
+                     xcd_head_group((size_t)a.Nk * (D + DV) * 2,
+                                    (long long)a.B * (a.Hkv ? a.Hkv : a.H)));
   return hipGetLastError();
 }
 

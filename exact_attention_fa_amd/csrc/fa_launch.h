@@ -147,6 +147,11 @@ fa_status decode_run(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf
                      void* workspace, int B, int H, int N_k, int d, float scale, int splits,
                      hipStream_t stream);
 
+// K/V heads an XCD works on at a time (xcd_map), for `heads` heads whose workgroups each stream
+// bytes_per_head from their head: all of them while an XCD's heads stream at most its share of
+// the last-level cache, else 2 (more when that many heads' rows fit in about 2 MiB).
+int xcd_head_group(size_t bytes_per_head, long long heads);
+
 // Split count used by the decode when the caller passes 0.
 int decode_auto_splits(int B, int H, int Nk, int d);
 // Split count used by the paged decode when the caller passes 0.
