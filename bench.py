@@ -64,41 +64,292 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = {"fwd": ["fa_fwd.hip", "fa_device.h"], "bwd": ["fa_bwd.hip", "fa_device.h"],
-                  "decode": ["fa_decode.hip", "fa_device.h"]}
-KERNEL_FAMILY = {"fwd": "fwd", "fwd_varlen": "fwd", "fwd_dropout": "fwd", "fwd_bias": "fwd",
-                 "fwd_dv64": "fwd", "fwd_gqa": "fwd", **{e[0]: "fwd" for e in SHAPES},
-                 "bwd_preprocess": "bwd", "bwd_dkdv": "bwd", "bwd_dq": "bwd",
-                 "decode": "decode", "decode_paged_gqa": "decode", "decode_gqa": "decode"}
-TRAFFIC_KEY = {"decode": "decode_split", "decode_paged_gqa": "decode_paged_mfma",
-               "decode_gqa": "decode_gqa_mfma",
-               "fwd_dv64": "fwd_dv"}
+# ---- profiles: which kernels each bench entry launches, in the order the bench runs them ------
+# A kernel instance is named as "name<template arguments>"; rocprofv3 reports some names mangled
+# and some demangled, and _matches accepts either form. Entry kinds: "step" entries run
+# warmup + steps times, "other" entries max(warmup, 3) + steps times, "shape" entries
+# max(warmup, 3) + max(1, steps // 4) * reps times. A kernel shared by several entries has its
+# calls split over them in this order.
+def _k(name, *args):
+    return f"{name}<{', '.join(str(a).lower() for a in args)}>"
+
+
+def _mangled(key: str) -> str:
+    name, args = key[:-1].split("<")
+    enc = "".join(f"Lb{int(a == 'true')}E" if a in ("true", "false") else f"Li{a}E"
+                  for a in args.split(", "))
+    return f"{len(name)}{name}I{enc}E"
+
+
+def _matches(kernel_name: str, key: str) -> bool:
+    return _mangled(key) in kernel_name or f"::{key}(" in kernel_name
+
+
+def _fwd(d, dv, nw, c, vl, dr, bi):
+    return _k("fwd_kernel", d, dv, nw, bool(c), bool(vl), bool(dr), bool(bi))
+
+
+def _dkdv(d, c, vl, dr, mode, bi, dv):
+    return _k("bwd_dkdv_kernel", d, bool(c), bool(vl), bool(dr), mode, bool(bi), dv)
+
+
+def _dq(d, c, vl, dr, bi, dv):
+    return _k("bwd_dq_kernel", d, bool(c), bool(vl), bool(dr), bool(bi), dv)
+
+
+_DELTA, _DELTA64 = _k("bwd_delta_kernel", 128), _k("bwd_delta_kernel", 64)
+_COMBINE = _k("decode_combine_kernel", 128)
+PROFILE_ENTRIES = [  # (entry, kind, reps, [kernel patterns])
+    ("fwd", "step", 1, [_fwd(128, 128, 8, 1, 0, 0, 0)]),
+    ("bwd_preprocess", "step", 1, [_DELTA]),
+    ("bwd_dkdv", "step", 1, [_dkdv(128, 1, 0, 0, 0, 0, 128)]),
+    ("bwd_dq", "step", 1, [_dq(128, 1, 0, 0, 0, 128)]),
+    ("decode", "step", 1, [_k("decode_split_kernel", 128), _COMBINE]),
+    ("decode_paged_gqa", "other", 1, [_k("decode_paged_mfma_kernel", 128, True), _COMBINE]),
+    ("decode_gqa", "other", 1, [_k("decode_paged_mfma_kernel", 128, False), _COMBINE]),
+    ("fwd_varlen", "other", 1, [_fwd(128, 128, 8, 1, 1, 0, 0)]),
+    ("bwd_varlen", "other", 1, [_DELTA, _dkdv(128, 1, 1, 0, 0, 0, 128), _dq(128, 1, 1, 0, 0, 128)]),
+    ("fwd_varlen_gqa_dropout", "other", 1, [_fwd(128, 128, 8, 1, 1, 1, 0)]),
+    ("bwd_varlen_gqa_dropout", "other", 1,
+     [_DELTA, _dkdv(128, 1, 1, 1, 1, 0, 128), _dkdv(128, 1, 1, 1, 2, 0, 128),
+      _dq(128, 1, 1, 1, 0, 128)]),
+    ("fwd_dropout", "other", 1, [_fwd(128, 128, 8, 1, 0, 1, 0)]),
+    ("bwd_dropout", "other", 1,
+     [_DELTA, _dkdv(128, 1, 0, 1, 1, 0, 128), _dkdv(128, 1, 0, 1, 2, 0, 128),
+      _dq(128, 1, 0, 1, 0, 128)]),
+    ("fwd_bias", "other", 1, [_fwd(128, 128, 8, 1, 0, 0, 1)]),
+    ("bwd_bias", "other", 1,
+     [_DELTA, _dkdv(128, 1, 0, 0, 1, 1, 128), _dkdv(128, 1, 0, 0, 2, 1, 128),
+      _dq(128, 1, 0, 0, 1, 128)]),
+    ("fwd_dv64", "other", 1, [_fwd(128, 64, 8, 1, 0, 0, 0)]),
+    ("bwd_dv64", "other", 1, [_DELTA64, _dkdv(128, 1, 0, 0, 0, 0, 64), _dq(128, 1, 0, 0, 0, 64)]),
+    ("fwd_gqa", "other", 1, [_fwd(128, 128, 8, 1, 0, 0, 0)]),
+    ("bwd_gqa", "other", 1, [_DELTA, _dkdv(128, 1, 0, 0, 0, 0, 128),
+                             _k("bwd_gqa_reduce_kernel", 128), _dq(128, 1, 0, 0, 0, 128)]),
+    ("fwd_fp8", "other", 1, [_k("fp8_prep_kernel", 128), _k("fp8_prep_v_kernel", 128),
+                             _k("fwd_fp8_kernel", 128, 8, True)]),
+    ("fwd_b1h1n256d64", "shape", 200, [_fwd(64, 64, 4, 0, 0, 0, 0)]),
+    ("fwd_b4h16n2048", "shape", 50, [_fwd(128, 128, 8, 0, 0, 0, 0)]),
+    ("fwd_b4h16n2048_causal", "shape", 50, [_fwd(128, 128, 8, 1, 0, 0, 0)]),
+    ("fwd_b1h32n32768", "shape", 4, [_fwd(128, 128, 8, 1, 0, 0, 0)]),
+    ("fwd_b1h64n32768_d64", "shape", 4, [_fwd(64, 64, 8, 1, 0, 0, 0)]),
+]
+# sources each entry's kernels are built from (a change to any of them retires its counters)
+_COMMON_SOURCES = ["fa_device.h", "fa_launch.h", "fa_api.cpp"]
+KERNEL_SOURCES = {"fwd": ["fa_fwd.hip"], "bwd": ["fa_bwd.hip"], "decode": ["fa_decode.hip"],
+                  "fp8": ["fa_fp8.hip"]}
+
+
+def _family(entry: str) -> str:
+    return "fp8" if entry == "fwd_fp8" else entry.split("_")[0]
+
+
+def _source_hash(family: str) -> str:
+    import hashlib
+    m = hashlib.sha256()
+    for src in KERNEL_SOURCES[family] + _COMMON_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_fa_amd", "csrc", src), "rb") as f:
+            m.update(f.read())
+    return m.hexdigest()[:16]
 
 
 def measured_traffic() -> dict:
-    """HBM bytes per launch per kernel from the committed rocprofv3 counter runs
-    (profiles/traffic.json), kept only for kernels whose sources are unchanged since."""
-    import hashlib
+    """HBM bytes per launch of each bench entry from the committed rocprofv3 counter runs
+    (profiles/traffic.json), kept only for entries whose kernel sources are unchanged since."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return {}
     with open(path) as f:
-        rec = json.load(f)["kernels"]
-    out = {}
-    for name, fam in KERNEL_FAMILY.items():
-        key = TRAFFIC_KEY.get(name, name)
-        if key not in rec:
-            continue
-        m = hashlib.sha256()
-        for src in KERNEL_SOURCES[fam]:
-            with open(os.path.join(ROOT, "exact_attention_fa_amd", "csrc", src), "rb") as f:
-                m.update(f.read())
-        if m.hexdigest()[:16] == rec[key]["source_hash"]:
-            b = rec[key]["bytes_per_launch"]
-            if name in TRAFFIC_KEY and "decode_combine" in rec:
-                b += rec["decode_combine"]["bytes_per_launch"]
-            out[name] = b
+        rec = json.load(f).get("entries", {})
+    return {name: e["bytes_per_launch"] for name, e in rec.items()
+            if e["source_hash"] == _source_hash(_family(name))}
+
+
+def _entry_calls(kind: str, reps: int, steps: int, warmup: int) -> tuple[int, int]:
+    """(calls, timed calls) of one bench entry's kernels."""
+    if kind == "step":
+        return warmup + steps, steps
+    if kind == "other":
+        return max(warmup, 3) + steps, steps
+    timed = max(1, steps // 4) * reps
+    return max(warmup, 3) + timed, timed
+
+
+def _read_csv(path: str) -> list:
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(run: str, sub: str, suffix: str) -> str:
+    for dirpath, _, files in os.walk(os.path.join(run, sub)):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(dirpath, fn)
+    raise FileNotFoundError(f"no *{suffix} under {os.path.join(run, sub)}")
+
+
+def _split_calls(names: list, steps: int, warmup: int) -> dict:
+    """Dispatch indices of every (entry, pattern) in the bench's order: each pattern's calls
+    (in dispatch order) are handed out to the entries that use it, in PROFILE_ENTRIES order."""
+    by_pat, out = {}, {}
+    for entry, kind, reps, pats in PROFILE_ENTRIES:
+        for pat in pats:
+            if pat not in by_pat:
+                by_pat[pat] = [i for i, n in enumerate(names) if _matches(n, pat)]
+    taken = {p: 0 for p in by_pat}
+    for entry, kind, reps, pats in PROFILE_ENTRIES:
+        calls, timed = _entry_calls(kind, reps, steps, warmup)
+        for pat in pats:
+            idx = by_pat[pat][taken[pat]:taken[pat] + calls]
+            taken[pat] += calls
+            out[(entry, pat)] = (idx, timed)
+    short = {p: (taken[p], len(by_pat[p])) for p in by_pat if taken[p] != len(by_pat[p])}
+    if short:
+        raise ValueError(f"calls expected vs found per kernel do not match the bench: {short}")
     return out
+
+
+def summarize_profiles(run: str, steps: int, warmup: int, pmc_steps: int, pmc_warmup: int,
+                       out_dir: str = "") -> None:
+    """Write profiles/ summaries from a directory of rocprofv3 results (see the command list in
+    the summaries): kernel durations per bench entry, HBM bytes per launch scaled by what the
+    same counters read for a plain 1 GiB copy, and profiles/traffic.json for the bench.
+    out_dir: where to write them (default: profiles/ of this repository)."""
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    import statistics
+    trace = _read_csv(_find(run, "stats", "kernel_trace.csv"))
+    trace.sort(key=lambda r: int(r["Dispatch_Id"]))
+    names = [r["Kernel_Name"] for r in trace]
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace]
+    split = _split_calls(names, steps, warmup)
+    cmd_t = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/stats -o bench -- "
+             f"python3 bench.py --steps {steps} --warmup {warmup} --cpu-heads 0")
+    lines = ["# Kernel durations per bench entry: causal attention fwd+bwd B2 H16 N8192 d128, "
+             "decode B8 H32 KV65536 d128, and the bench's other entries", "",
+             "Command (repository root, one MI355X):", "", "    " + cmd_t, "",
+             "Each entry's kernels over its timed launches (the bench's warm-up launches left out), "
+             "from `bench_kernel_trace.csv`; a kernel shared by several entries has its calls "
+             "handed to them in the order the bench runs them. Summarised by "
+             f"`python3 bench.py --summarize-profiles <out> --steps {steps} --warmup {warmup}`.",
+             "", "| entry | kernel | timed calls | average (us) | min (us) | max (us) |",
+             "|---|---|---|---|---|---|"]
+    entry_us = {}
+    for entry, kind, reps, pats in PROFILE_ENTRIES:
+        tot = 0.0
+        for pat in pats:
+            idx, timed = split[(entry, pat)]
+            t = [dur[i] for i in idx[-timed:]] if idx else []
+            if not t:
+                continue
+            tot += statistics.mean(t)
+            lines.append(f"| {entry} | `{pat}` | {len(t)} | {statistics.mean(t):.1f} | "
+                         f"{min(t):.1f} | {max(t):.1f} |")
+        entry_us[entry] = tot
+    lines += ["", "Per launch of each entry (sum over its kernels):", "", "| entry | average (us) |",
+              "|---|---|"] + [f"| {e} | {u:.1f} |" for e, u in entry_us.items()]
+    with open(os.path.join(out_dir, "kernel_durations_causal_b2h16n8192d128_"
+                           "decode_b8h32k65536.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), one counter per run
+    def counter(sub, cname):
+        rows = _read_csv(_find(run, sub, "counter_collection.csv"))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows
+                if r["Counter_Name"] == cname]
+    copy_f = [v for n, v in counter("FETCH_SIZE_copy", "FETCH_SIZE") if "copyBuffer" in n]
+    copy_w = [v for n, v in counter("WRITE_SIZE_copy", "WRITE_SIZE") if "copyBuffer" in n]
+    gib_kib = float(1 << 20)
+    ff, fw = gib_kib / statistics.median(copy_f), gib_kib / statistics.median(copy_w)
+    fetch, write = counter("FETCH_SIZE", "FETCH_SIZE"), counter("WRITE_SIZE", "WRITE_SIZE")
+    sf = _split_calls([n for n, _ in fetch], pmc_steps, pmc_warmup)
+    sw = _split_calls([n for n, _ in write], pmc_steps, pmc_warmup)
+    cmds = [f"rocprofv3 --pmc {c} --output-format csv -d <out>/{c} -o bench -- python3 bench.py "
+            f"--steps {pmc_steps} --warmup {pmc_warmup} --cpu-heads 0" for c in ("FETCH_SIZE",
+                                                                                 "WRITE_SIZE")]
+    cmds += [f"rocprofv3 --pmc {c} --output-format csv -d <out>/{c}_copy -o copy -- python3 "
+             f"bench.py --calibrate-copy 1024" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    lines = ["# HBM traffic per launch of each bench entry: causal attention fwd+bwd B2 H16 N8192 "
+             "d128, decode B8 H32 KV65536 d128, and the bench's other entries", "",
+             "Commands (repository root, one MI355X), one counter per run:", ""]
+    lines += ["    " + c for c in cmds]
+    lines += ["", f"Calibration: a plain 1 GiB device-to-device copy reads FETCH_SIZE = "
+              f"{statistics.median(copy_f):.0f} KiB and WRITE_SIZE = {statistics.median(copy_w):.0f}"
+              f" KiB per dispatch for 1048576 KiB moved each way, so the scale factors are "
+              f"{ff:.4f} (FETCH_SIZE) and {fw:.4f} (WRITE_SIZE). Each entry's value is the median "
+              f"over its launches of the scaled sum over its kernels. Summarised by `python3 "
+              f"bench.py --summarize-profiles <out> --pmc-steps {pmc_steps} --pmc-warmup "
+              f"{pmc_warmup}`.", "",
+              "| entry | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled traffic (MB per launch) |",
+              "|---|---|---|---|"]
+    entries = {}
+    for entry, kind, reps, pats in PROFILE_ENTRIES:
+        fk = wk = 0.0
+        ok = True
+        for pat in pats:
+            i_f, _ = sf[(entry, pat)]
+            i_w, _ = sw[(entry, pat)]
+            if not i_f or not i_w:
+                ok = False
+                break
+            fk += statistics.median(fetch[i][1] for i in i_f)
+            wk += statistics.median(write[i][1] for i in i_w)
+        if not ok:
+            continue
+        nbytes = (fk * ff + wk * fw) * 1024
+        entries[entry] = {"bytes_per_launch": int(nbytes),
+                          "source_hash": _source_hash(_family(entry))}
+        lines.append(f"| {entry} | {fk:.0f} | {wk:.0f} | {nbytes / 1e6:.1f} |")
+    with open(os.path.join(out_dir, "hbm_traffic_causal_b2h16n8192d128_"
+                           "decode_b8h32k65536.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
+        json.dump({"note": f"(FETCH_SIZE * {ff:.4f} + WRITE_SIZE * {fw:.4f}) KiB per launch, "
+                           "from profiles/hbm_traffic_*.md", "entries": entries}, f, indent=1)
+        f.write("\n")
+
+    # matrix-core, vector-ALU and LDS counters, all in one run
+    sq = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32",
+          "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVES", "GRBM_GUI_ACTIVE"]
+    rows = _read_csv(_find(run, "mfma", "counter_collection.csv"))
+    per = {}
+    for r in rows:
+        per.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], {}])[1][r["Counter_Name"]] = \
+            float(r["Counter_Value"])
+    disp = [per[k] for k in sorted(per)]
+    sm = _split_calls([n for n, _ in disp], pmc_steps, pmc_warmup)
+    lines = ["# Matrix-core, vector-ALU and LDS counters per bench entry: causal attention fwd+bwd "
+             "B2 H16 N8192 d128, decode B8 H32 KV65536 d128, and the bench's other entries", "",
+             "Command (repository root, one MI355X):", "",
+             f"    rocprofv3 --pmc {' '.join(sq)} --output-format csv -d <out>/mfma -o bench -- "
+             f"python3 bench.py --steps {pmc_steps} --warmup {pmc_warmup} --cpu-heads 0", "",
+             "Per launch, the mean over the entry's launches. MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / "
+             "(GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs): the fraction of elapsed cycles the matrix "
+             "cores were busy. The clock column is GRBM_GUI_ACTIVE / 8 over the kernel's average "
+             "duration in the kernel-trace run: the mean shader clock while it ran (left out under "
+             "100 us, where launch gaps dominate the count).", "",
+             "| entry | kernel | MFMA instr | VALU instr | VALU per MFMA | transcendental instr | "
+             "LDS instr | LDS bank-conflict cycles | MfmaUtil | clock (MHz) |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for entry, kind, reps, pats in PROFILE_ENTRIES:
+        for pat in pats:
+            idx, _ = sm[(entry, pat)]
+            if not idx:
+                continue
+            c = {n: statistics.mean(disp[i][1].get(n, 0.0) for i in idx) for n in sq}
+            util = c["SQ_VALU_MFMA_BUSY_CYCLES"] / max(c["GRBM_GUI_ACTIVE"] / 8 * 1024, 1.0)
+            i_t, timed = split[(entry, pat)]
+            us = statistics.mean(dur[i] for i in i_t[-timed:]) if i_t else 0.0
+            mhz = f"{c['GRBM_GUI_ACTIVE'] / 8 / us:.0f}" if us >= 100 else "-"
+            vpm = (f"{c['SQ_INSTS_VALU'] / c['SQ_INSTS_MFMA']:.1f}" if c["SQ_INSTS_MFMA"]
+                   else "-")
+            lines.append(f"| {entry} | `{pat}` | {c['SQ_INSTS_MFMA']:.3g} | {c['SQ_INSTS_VALU']:.3g}"
+                         f" | {vpm} | {c['SQ_INSTS_VALU_TRANS_F32']:.3g} | {c['SQ_INSTS_LDS']:.3g} | "
+                         f"{c['SQ_LDS_BANK_CONFLICT']:.3g} | {util:.2f} | {mhz} |")
+    with open(os.path.join(out_dir, "mfma_valu_lds_counters_causal_b2h16n8192d128_"
+                           "decode_b8h32k65536.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def cpu_baseline(heads: int) -> dict:
@@ -144,10 +395,19 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the oracle CPU baseline sample (0 = skip)")
+    ap.add_argument("--summarize-profiles", default="", metavar="DIR",
+                    help="only turn the rocprofv3 results under DIR into the profiles/ summaries "
+                         "(no GPU needed); --steps/--warmup are those of the kernel-trace run")
+    ap.add_argument("--pmc-steps", type=int, default=2)
+    ap.add_argument("--pmc-warmup", type=int, default=1)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, three times (the "
                          "reference the HBM byte counters are scaled against), and exit")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.steps, args.warmup, args.pmc_steps,
+                           args.pmc_warmup)
+        return 0
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)

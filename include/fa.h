@@ -14,11 +14,15 @@
  *     q, o, dout, dq      [B, H, N_q, d]   bf16
  *     k, v, dk, dv        [B, H, N_k, d]   bf16
  *     lse                 [B, H, N_q]      fp32, natural log: lse_i = ln sum_j exp(S_ij)
- * bf16 values are passed as their 16-bit patterns (fa_bf16). d_v = d.
+ * bf16 values are passed as their 16-bit patterns (fa_bf16). V, O, dO and dV share d with Q
+ * and K everywhere except the fa_fwd_dv / fa_bwd_dv entry points, which give them a width d_v
+ * of their own; K and V have H_kv heads instead of H in the grouped-query entry points; the
+ * entry points with an additive bias, per-sequence lengths, dropout or FP8 say what they add.
  *
  * Ownership. The caller owns every buffer. The library never allocates, frees or synchronises
- * and keeps no mutable global state, so calls are reentrant. Inputs are read only; outputs are
- * fully overwritten; outputs must not alias inputs or each other.
+ * and keeps no mutable global state, so calls are reentrant (the one exception, a per-GPU
+ * device array used by fa_decode_noalloc, is described there). Inputs are read only; outputs
+ * are fully overwritten; outputs must not alias inputs or each other.
  *
  * Streams. Every call only enqueues kernels on `stream` (0 = the null stream) and returns.
  *
@@ -27,7 +31,10 @@
  * execution surface at the caller's next synchronisation of the stream.
  *
  * Common constraints: B, H, N_q, N_k >= 1; d in {64, 128}; B*H*N_q and B*H*N_k below 2^31;
- * pointers 16-byte aligned; scale finite and > 0; causal requires N_q <= N_k (so no row is empty).
+ * one head's rows of any tensor below 2^31 bytes (the kernels address a head through 32-bit
+ * buffer offsets); pointers 16-byte aligned; scale finite and > 0; causal requires N_q <= N_k
+ * (so no row is empty). A violation returns FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_ALIGN,
+ * FA_ERR_SCALE or FA_ERR_CAUSAL before anything is enqueued.
  */
 #ifndef FA_H
 #define FA_H
