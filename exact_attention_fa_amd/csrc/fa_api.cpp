@@ -562,7 +562,12 @@ fa_status fa_fwd_ext(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf
 }
 
 size_t fa_bwd_ext_workspace_bytes(int B, int H, int H_kv, int N_q, int N_k, int d) {
-  return fa_bwd_gqa_workspace_bytes(B, H, H_kv, N_q, N_k, d);
+  const size_t base = fa_bwd_workspace_bytes(B, H, N_q, N_k, d);
+  if (base == 0 || H_kv < 1 || H % H_kv != 0 || N_k < 1 || (d != 64 && d != 128)) return 0;
+  if (H_kv == H) return base;
+  // grouped K/V heads: room for the fp32 partial rows of dK and dV per query head, which the
+  // dK/dV pass uses with per-sequence lengths (unknown here) and on small grids
+  return base + 2 * round_up16((size_t)B * H * N_k * d * sizeof(float));
 }
 
 fa_status fa_bwd_ext(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,

@@ -591,14 +591,16 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
   }
 
   // (in a one-gradient mode the other gradient's products are dead code and compile away)
-  // one query head's partial rows: the plain variant only (the launcher passes pK = nullptr to
-  // every other one)
-  constexpr bool kPartialOk = MODE == kDkDv && !VL && !DROP && !BIAS && D == DV;
+  // one query head's partial rows, zero past the sequence's keys (the launcher passes
+  // pK = nullptr to the variants with a bias or a V head dimension of its own)
+  constexpr bool kPartialOk = !BIAS && D == DV;
   if (kPartialOk && pK != nullptr) {
     if (key < Nk) {
       const bool live = key < nk;
-      store_row_f32<D>(pK + ((size_t)bh * Nk + key) * D, dk, scale, live, hi);
-      store_row_f32<DV>(pV + ((size_t)bh * Nk + key) * DV, dv, 1.f, live, hi);
+      if (MODE != kDvOnly) store_row_f32<D>(pK + ((size_t)bh * Nk + key) * D, dk, scale, live, hi);
+      if (MODE != kDkOnly)
+        store_row_f32<DV>(pV + ((size_t)bh * Nk + key) * DV, dv, DROP ? drop.inv_keep : 1.f,
+                          live, hi);
     }
   } else if (key < nk) {
     if (MODE != kDvOnly) store_row<D>(dK + ((size_t)kvbh * Nk + key) * D, dk, scale, hi);
@@ -926,11 +928,13 @@ hipError_t launch(const BwdArgs& a, unsigned phases) {
     if (e != hipSuccess) return e;
   }
   const int G = a.Hkv ? a.H / a.Hkv : 1;  // query heads per K/V head
-  // grouped query heads with too few K/V workgroups to fill the chip: one workgroup per query
-  // head and fp32 partial rows in the workspace, summed by a second kernel
+  // grouped query heads with too few K/V workgroups to fill the chip, or with per-sequence
+  // lengths (which make the workgroups that visit a whole group of heads very unequal, so that
+  // the longest ones set the time): one workgroup per query head and fp32 partial rows in the
+  // workspace, summed by a second kernel
   constexpr bool split = (DROP || BIAS) && D == 128;
-  const bool partial =
-      !split && !VL && !DROP && !BIAS && D == DV && bwd_gqa_uses_partials(a.B, a.H, a.H / G, a.Nk);
+  const bool partial = G > 1 && !BIAS && D == DV &&
+                       (VL || bwd_gqa_uses_partials(a.B, a.H, a.H / G, a.Nk));
   const int GL = partial ? 1 : G;
   // dK/dV workgroups stream the Q and dO rows of the query heads of their unit (GL of them)
   const int hg_kv = xcd_head_group((size_t)GL * a.Nq * (D + DV) * 2, (long long)BH / GL);

@@ -278,8 +278,11 @@ fa_status fa_bwd_varlen(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, co
  *                           the padded layout, which are the sequence's own indices.
  * Without lengths causal needs N_q <= N_k (FA_ERR_CAUSAL); with them any N_q, N_k. The backward
  * needs the forward's (seq_lens, H_kv, p_drop, seed, offset) and a workspace of at least
- * fa_bwd_ext_workspace_bytes(B, H, H_kv, N_q, N_k, d) bytes (0 for invalid sizes). A bias and
- * d_v != d are not among the options. Other arguments and errors as for fa_fwd / fa_bwd.
+ * fa_bwd_ext_workspace_bytes(B, H, H_kv, N_q, N_k, d) bytes (0 for invalid sizes); with grouped
+ * K/V heads this includes the fp32 partial rows of fa_bwd_gqa's small-grid mode, which the dK/dV
+ * pass also uses whenever lengths are given (a workgroup per whole group would make the longest
+ * sequences' workgroups set the time). A bias and d_v != d are not among the options. Other
+ * arguments and errors as for fa_fwd / fa_bwd.
  */
 fa_status fa_fwd_ext(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
                      const int32_t* seq_lens_q, const int32_t* seq_lens_k, int B, int H, int H_kv,
