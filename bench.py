@@ -132,7 +132,7 @@ PROFILE_ENTRIES = [  # (entry, kind, reps, [kernel patterns])
     ("fwd_b4h16n2048", "shape", 50, [_fwd(128, 128, 8, 0, 0, 0, 0)]),
     ("fwd_b4h16n2048_causal", "shape", 50, [_fwd(128, 128, 8, 1, 0, 0, 0)]),
     ("fwd_b1h32n32768", "shape", 4, [_fwd(128, 128, 8, 1, 0, 0, 0)]),
-    ("fwd_b1h64n32768_d64", "shape", 4, [_fwd(64, 64, 8, 1, 0, 0, 0)]),
+    ("fwd_b1h64n32768_d64", "shape", 4, [_fwd(64, 64, 4, 1, 0, 0, 0)]),
 ]
 # sources each entry's kernels are built from (a change to any of them retires its counters)
 _COMMON_SOURCES = ["fa_device.h", "fa_launch.h", "fa_api.cpp"]

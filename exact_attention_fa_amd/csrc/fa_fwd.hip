@@ -67,8 +67,21 @@ struct FwdLds {
 // DV: head dimension of V and O (the notation's d_v; the same as D unless asked otherwise).
 // G: query heads per K/V head (grouped-query attention; 1 unless asked otherwise): query head bh
 // reads K/V head bh / G, K and V holding BH / G heads.
+// d = d_v = 64 without dropout or a bias: one buffer of scores (the next tile's S^T is formed after
+// this tile's P is packed, over its scores) fits the kernel in 128 VGPRs, so four waves share each
+// SIMD (four 4-wave workgroups per CU) and the softmax of one wave hides under the products of the
+// others. At d = 64 the softmax's share of the work is twice that of d = 128, and four such waves
+// beat two that each overlap the next tile's products with their own softmax (measured causal
+// B1 H64 N32768 d64: 9.36 against 9.95 ms). At d = 128 the same form with three waves per SIMD
+// (12-wave workgroups, 162 VGPRs) is slower than two double-buffered waves (0.560 against
+// 0.514 ms, causal B2 H16 N8192).
+template <int D, int DV, bool DROP, bool BIAS>
+constexpr bool kOneScoreBuffer = D == 64 && DV == 64 && !DROP && !BIAS;
+
 template <int D, int DV, int NW, bool CAUSAL, bool VL, bool DROP, bool BIAS>
-__global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64) void fwd_kernel(
+__global__ __attribute__((amdgpu_waves_per_eu(kOneScoreBuffer<D, DV, DROP, BIAS> ? 4 : 2,
+                                               kOneScoreBuffer<D, DV, DROP, BIAS> ? 4 : 2)))
+__launch_bounds__(NW * 64) void fwd_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int* __restrict__ lens_q,
     const int* __restrict__ lens_k, int BH, int H, int G, int Nq, int Nk, float c,
@@ -76,6 +89,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
 #if defined(__HIP_DEVICE_COMPILE__)
   using L = FwdLds<D, DV>;
   constexpr int BR = NW * 32;  // query rows per workgroup
+  constexpr bool kSB = kOneScoreBuffer<D, DV, DROP, BIAS>;
   constexpr int KIW = (L::KI + NW - 1) / NW, VIW = (L::VI + NW - 1) / NW;
   // one array per buffer: the LDS copies into one buffer then provably do not alias the reads of
   // the other, so the reads wait for nothing but their own data
@@ -274,7 +288,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     }
     // Issued unconditionally so that it shares a basic block with the softmax below; past the
     // last tile it reads stale (in-bounds) LDS and its result is never used.
-    qk(sn0, sn1, P ? kb0 : kb1);
+    if constexpr (!kSB) qk(sn0, sn1, P ? kb0 : kb1);
     // a row that sees no key at all (possible only with per-sequence lengths) keeps m = -inf;
     // reference it to 0 so that its probabilities are exp2(-inf) = 0, not NaN
     const float m_use = (GUARD && m_run == kNegInf) ? 0.f : m_run;
@@ -308,6 +322,8 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
         pf[st] = as_bf16x8(x);
       }
     }
+    // one score buffer: the next tile's S^T over this tile's scores, now packed into pf
+    if constexpr (kSB) qk(sn0, sn1, P ? kb0 : kb1);
     const unsigned char* vt = P ? vb1 : vb0;
 #pragma unroll
     for (int st = 0; st < kBC / 16; ++st)
@@ -330,11 +346,19 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
     qk(sa0, sa1, kb0);
   }
   int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    step(I0(), sa0, sa1, sb0, sb1, t);
-    step(I1(), sb0, sb1, sa0, sa1, t + 1);
+  if constexpr (kSB) {
+    for (; t + 1 < ntiles; t += 2) {
+      step(I0(), sa0, sa1, sa0, sa1, t);
+      step(I1(), sa0, sa1, sa0, sa1, t + 1);
+    }
+    if (t < ntiles) step(I0(), sa0, sa1, sa0, sa1, t);
+  } else {
+    for (; t + 1 < ntiles; t += 2) {
+      step(I0(), sa0, sa1, sb0, sb1, t);
+      step(I1(), sb0, sb1, sa0, sa1, t + 1);
+    }
+    if (t < ntiles) step(I0(), sa0, sa1, sb0, sb1, t);
   }
-  if (t < ntiles) step(I0(), sa0, sa1, sb0, sb1, t);
 
   // ---- epilogue: O = acc / lq, L = ln 2 * (m + log2 l)
   const float l_tot = halves_sum(l_run);
@@ -382,11 +406,16 @@ hipError_t launch(const FwdArgs& a) {
 template <int D, bool VL, bool DROP, bool BIAS, int DV = D>
 hipError_t launch_d(const FwdArgs& a) {
   const long long tiles = (long long)a.B * a.H * ((a.Nq + 255) / 256);
-  if (tiles < 512)
+  if constexpr (kOneScoreBuffer<D, DV, DROP, BIAS>) {  // four 4-wave workgroups per CU
     return a.causal ? launch<D, DV, 4, true, VL, DROP, BIAS>(a)
                     : launch<D, DV, 4, false, VL, DROP, BIAS>(a);
-  return a.causal ? launch<D, DV, 8, true, VL, DROP, BIAS>(a)
-                  : launch<D, DV, 8, false, VL, DROP, BIAS>(a);
+  } else {
+    if (tiles < 512)
+      return a.causal ? launch<D, DV, 4, true, VL, DROP, BIAS>(a)
+                      : launch<D, DV, 4, false, VL, DROP, BIAS>(a);
+    return a.causal ? launch<D, DV, 8, true, VL, DROP, BIAS>(a)
+                    : launch<D, DV, 8, false, VL, DROP, BIAS>(a);
+  }
 }
 
 template <int D>
