@@ -127,7 +127,7 @@ PROFILE_ENTRIES = [  # (entry, kind, reps, [kernel patterns])
     ("bwd_gqa", "other", 1, [_DELTA, _dkdv(128, 1, 0, 0, 0, 0, 128),
                              _k("bwd_gqa_reduce_kernel", 128), _dq(128, 1, 0, 0, 0, 128)]),
     ("fwd_fp8", "other", 1, [_k("fp8_prep_kernel", 128), _k("fp8_prep_v_kernel", 128),
-                             _k("fwd_fp8_kernel", 128, 8, True)]),
+                             _k("fwd_fp8_kernel", 128, 4, True)]),
     ("fwd_b1h1n256d64", "shape", 200, [_fwd(64, 64, 4, 0, 0, 0, 0)]),
     ("fwd_b4h16n2048", "shape", 50, [_fwd(128, 128, 8, 0, 0, 0, 0)]),
     ("fwd_b4h16n2048_causal", "shape", 50, [_fwd(128, 128, 8, 1, 0, 0, 0)]),

@@ -23,9 +23,9 @@
 //     maxima, then the E4M3 codes written transposed, V8^T [d][N_k padded to 64], so that the
 //     second product's A operand (rows = head dimensions, k = keys) is a plain row read; padding
 //     keys are zero.
-//   * fwd_fp8_kernel: the bf16 forward's structure (256 queries per workgroup, 8 waves of 32
-//     queries, 64-key tiles copied HBM -> LDS by buffer_load ... lds and double buffered, causal
-//     longest-first and XCD-aware grid) with FP8 operands:
+//   * fwd_fp8_kernel: the bf16 forward's structure (waves of 32 queries, 64-key tiles copied
+//     HBM -> LDS by buffer_load ... lds and double buffered, causal longest-first and XCD-aware
+//     grid; here 4 waves per workgroup and one score buffer, see the kernel) with FP8 operands:
 //       - operand layout of the 32x32x64 instruction (measured on the MI355X): lane (i, h)
 //         holds row/column i and k = 32 h + 0..31 in its 32 bytes, for A and B alike; output
 //         register r of lane (i, h) is row 8 (r / 4) + 4 h + (r % 4), column i;
@@ -286,8 +286,14 @@ __device__ __forceinline__ int fp8_key_of_row(int i, int b) {
   return 32 * ((i >> 2) & 1) + 16 * b + 4 * (i >> 3) + (i & 3);
 }
 
+// One buffer of scores: the next tile's S^T is formed after this tile's P is packed, over its
+// scores. That keeps the kernel within 168 VGPRs, so three 4-wave workgroups share a CU (three
+// waves per SIMD) and the softmax of one wave hides under the products of the others; with the
+// matrix-core time halved against bf16 the softmax dominates, and this beats two waves per SIMD
+// that each overlap the next tile's products with their own softmax (measured, causal B2 H16
+// N8192 d128: 0.402 against 0.424 ms for the whole call; 12-wave workgroups 0.431 ms).
 template <int D, int NW, bool CAUSAL>
-__global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64) void fwd_fp8_kernel(
+__global__ __attribute__((amdgpu_waves_per_eu(3, 3))) __launch_bounds__(NW * 64) void fwd_fp8_kernel(
     const unsigned char* __restrict__ q8, const unsigned char* __restrict__ k8,
     const unsigned char* __restrict__ v8t, const float* __restrict__ sq,
     const float* __restrict__ sk, const float* __restrict__ sv, bf16* __restrict__ O,
@@ -396,7 +402,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
   };
   const int vr = l32 * L::VST + 32 * hi;  // V^T row (dim 32 db + l32), keys 32 h + 0..31
 
-  auto step = [&](auto PAR, f32x16& sc0, f32x16& sc1, f32x16& sn0, f32x16& sn1, int t) {
+  auto step = [&](auto PAR, f32x16& sc0, f32x16& sc1, int t) {
     constexpr int P = decltype(PAR)::value;
     wait_vmem();
     __syncthreads();
@@ -432,7 +438,6 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
-    qk(sn0, sn1, P ? kb0 : kb1);
     // 2^8 P: below 2^8.5 because no score exceeds m_run by more than the slack
     const float mo = m_run - kPShift;
 #pragma unroll
@@ -456,13 +461,14 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
                                            cvt2_fp8<false>(sc1[4 * w], sc1[4 * w + 1], 0));
     }
     const i32x8 pf = __builtin_bit_cast(i32x8, pw);
+    qk(sc0, sc1, P ? kb0 : kb1);  // the next tile's scores, over this one's
     const unsigned char* vt = P ? vb1 : vb0;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
       oacc[db] = mfma_fp8(ld32(vt + vr + 32 * db * L::VST), pf, oacc[db]);
   };
 
-  f32x16 sa0, sa1, sb0, sb1;
+  f32x16 sa0, sa1;
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   copy_k(0, kb0);
@@ -473,10 +479,10 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(NW * 64)
   qk(sa0, sa1, kb0);
   int t = 0;
   for (; t + 1 < ntiles; t += 2) {
-    step(I0(), sa0, sa1, sb0, sb1, t);
-    step(I1(), sb0, sb1, sa0, sa1, t + 1);
+    step(I0(), sa0, sa1, t);
+    step(I1(), sa0, sa1, t + 1);
   }
-  if (t < ntiles) step(I0(), sa0, sa1, sb0, sb1, t);
+  if (t < ntiles) step(I0(), sa0, sa1, t);
 
   // ---- epilogue: O = s_v acc / l, L = ln 2 (m - 8 + log2 l)
   const float l_tot = halves_sum(l_run);
@@ -512,7 +518,7 @@ hipError_t launch_d(const Fp8Args& a) {
                      a.v, a.ws.vpart, a.ws.v8t, a.ws.sv, a.Nk, nkb64);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int NW = 8, BR = NW * 32;
+  constexpr int NW = 4, BR = NW * 32;  // three workgroups per CU
   const int nqt = (a.Nq + BR - 1) / BR;
   const long long grid = (long long)BH * nqt;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
