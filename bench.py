@@ -112,7 +112,7 @@ PROFILE_ENTRIES = [  # (entry, kind, reps, [kernel patterns])
     ("fwd_varlen_gqa_dropout", "other", 1, [_fwd(128, 128, 8, 1, 1, 1, 0)]),
     ("bwd_varlen_gqa_dropout", "other", 1,
      [_DELTA, _dkdv(128, 1, 1, 1, 1, 0, 128), _dkdv(128, 1, 1, 1, 2, 0, 128),
-      _dq(128, 1, 1, 1, 0, 128)]),
+      _k("bwd_gqa_reduce_kernel", 128), _dq(128, 1, 1, 1, 0, 128)]),
     ("fwd_dropout", "other", 1, [_fwd(128, 128, 8, 1, 0, 1, 0)]),
     ("bwd_dropout", "other", 1,
      [_DELTA, _dkdv(128, 1, 0, 1, 1, 0, 128), _dkdv(128, 1, 0, 1, 2, 0, 128),
