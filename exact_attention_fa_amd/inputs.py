@@ -67,6 +67,25 @@ def tensor_bf16(seed: int, tensor: str, B: int, H: int, n: int, d: int,
     return out
 
 
+def long_head_bf16(seed: int, tensor: str, n: int, d: int, parts: int = 32,
+                   threads: int | None = None) -> np.ndarray:
+    """One very long head [1, 1, n, d] as bf16 bit patterns, drawn in `parts` runs of rows with
+    one stream each, SeedSequence([seed, tensor_id, 0, 0, part]), so that the draw runs on
+    several threads (a single stream of 2^30 values takes half a minute)."""
+    out = np.empty((1, 1, n, d), dtype=np.uint16)
+    step = (n + parts - 1) // parts
+
+    def fill(i: int) -> None:
+        r0, r1 = i * step, min(n, (i + 1) * step)
+        if r0 < r1:
+            g = Generator(PCG64(SeedSequence([seed, TENSOR_ID[tensor], 0, 0, i])))
+            out[0, 0, r0:r1] = bf16_round(g.standard_normal((r1 - r0, d), dtype=np.float32))
+
+    with ThreadPoolExecutor(threads or min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range(parts)))
+    return out
+
+
 def qkv_bf16(seed: int, B: int, H: int, n_q: int, n_k: int, d: int, with_do: bool = False):
     """Q [B,H,n_q,d], K and V [B,H,n_k,d] (and dO [B,H,n_q,d]) as bf16 bit patterns."""
     q = tensor_bf16(seed, "q", B, H, n_q, d)
