@@ -57,7 +57,7 @@ GQA = dict(H_kv=4)  # grouped query heads: the forward+backward workload with 4 
 GEMM = dict(n=8192, seed=0x6E, reps=10)  # plain bf16 GEMM on random data: the sustained MFMA rate
 # matrix-core calibration loop: 2 workgroups of 4 waves per CU, 8 independent 32x32x16 bf16
 # accumulators per wave on random operands; iters per launch (about 30 ms)
-CALIB = dict(blocks=512, iters=100000, seed=0xCA1)
+CALIB = dict(blocks=512, iters=100000, iters_fp8=50000, seed=0xCA1)
 
 
 def log(msg: str) -> None:
@@ -921,7 +921,37 @@ def main() -> int:
             e["frac_of_mfma_ceiling"] = e["achieved"] / c_tf
     roof["frac_of_mfma_ceiling"] = kernels[dominant].get("frac_of_mfma_ceiling")
     out["fwd_frac_of_mfma_ceiling"] = kernels["fwd"]["frac_of_mfma_ceiling"]
-    del c_ops, c_clk, c_sink
+    del c_ops
+    # the same on random E4M3 codes (never the NaN codes 0x7F, 0xFF): the FP8 forward's ceiling
+    calib.fa_calib_mfma_fp8.restype = ctypes.c_int
+    calib.fa_calib_mfma_fp8.argtypes = calib.fa_calib_mfma_bf16.argtypes
+    ci8 = CALIB["iters_fp8"]
+    r8 = torch.randint(0, 254, (cb * 256 * 32 * 16,), generator=gen_c, device=dev,
+                       dtype=torch.int32)
+    c8_ops = (r8 + (r8 >= 127).to(torch.int32)).to(torch.uint8)
+    del r8
+    run_c8 = lambda: calib.fa_calib_mfma_fp8(c8_ops.data_ptr(), cb, ci8, c_clk.data_ptr(),  # noqa: E731
+                                             c_sink.data_ptr(), stream)
+    if run_c8() != 0:
+        raise RuntimeError("fp8 calibration loop failed to launch")
+    torch.cuda.synchronize()
+    c0.record()
+    run_c8()
+    c1.record()
+    torch.cuda.synchronize()
+    c8_ms = c0.elapsed_time(c1)
+    c8_tf = cb * 4 * ci8 * 8 * 2.0 * 32 * 32 * 64 / (c8_ms * 1e-3) / 1e12
+    clk = c_clk.cpu().double()
+    mhz8 = float(((clk[:, 1] - clk[:, 0]) / (clk[:, 3] - clk[:, 2]) * 100.0).median())
+    log(f"MFMA loop on random E4M3: {c8_ms:.2f} ms, {c8_tf:.0f} TFLOP/s at {mhz8:.0f} MHz")
+    peak8 = metrics.MI355X_FP8_DENSE_TFLOPS
+    out["mfma_ceiling_fp8"] = {
+        "what": f"{cb} workgroups x 4 waves, each {ci8} x 8 independent "
+                "v_mfma_scale_f32_32x32x64_f8f6f4 on random E4M3 codes (no memory traffic)",
+        "tflops": c8_tf, "frac_peak": c8_tf / peak8, "clock_mhz": mhz8,
+        "peak_at_clock": peak8 * mhz8 / 2400.0}
+    kernels["fwd_fp8"]["frac_of_mfma_ceiling"] = kernels["fwd_fp8"]["achieved"] / c8_tf
+    del c8_ops, c_clk, c_sink
 
     if args.cpu_heads > 0:
         log(f"oracle CPU baseline on {args.cpu_heads} head(s) ...")
