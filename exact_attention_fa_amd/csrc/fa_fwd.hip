@@ -29,9 +29,13 @@
 //     are free of bank conflicts. K is copied two tiles ahead and V one tile ahead.
 //   * Software pipeline: the QK^T product of tile t+1 is issued while the softmax of tile t runs,
 //     so the matrix cores and the vector ALUs overlap inside a wave; two waves share each SIMD.
-//   * The running maximum only moves when some row of the wave would exceed it by more than
-//     kRescaleSlack (log2 units), so the accumulator rescale is skipped on most tiles. Softmax is
-//     invariant to the reference value; probabilities are then bounded by 2^kRescaleSlack.
+//   * The reference m of the exponentials is a running maximum that only moves when needed, so
+//     the accumulator rescale is skipped on most tiles; softmax is invariant to the reference
+//     value, and every probability stays at most 2^kRescaleSlack. In most forms no row maximum is
+//     taken on the common path: the exponentials are taken against m as it stands, and only when
+//     some lane's sum of the tile exceeds 2^kRescaleSlack (or on the first tile) is the maximum
+//     taken, m moved and the tile redone. The other forms take the maximum first and move m when
+//     a row would exceed it by more than kRescaleSlack (log2 units).
 //   * O is normalised by the sum of the same bf16 probabilities that feed the PV product, so it is
 //     an exact convex combination of V rows under the rounded weights; the log-sum-exp keeps the
 //     fp32 sum.
@@ -45,6 +49,7 @@ namespace {
 
 constexpr int kBC = 64;               // keys per tile
 constexpr float kRescaleSlack = 8.f;  // log2 units
+constexpr float kTileSumMax = 256.f;  // 2^kRescaleSlack
 
 template <int D, int DV>
 struct FwdLds {
@@ -90,6 +95,10 @@ __launch_bounds__(NW * 64) void fwd_kernel(
   using L = FwdLds<D, DV>;
   constexpr int BR = NW * 32;  // query rows per workgroup
   constexpr bool kSB = kOneScoreBuffer<D, DV, DROP, BIAS>;
+  // the row maximum only when the tile's sums call for it: the scores then stay live beside the
+  // probabilities, which the one-score-buffer form has no registers for, and which would push
+  // the bias and the lengths-with-dropout forms into scratch memory
+  constexpr bool kLateMax = !kSB && !BIAS && !(VL && DROP);
   constexpr int KIW = (L::KI + NW - 1) / NW, VIW = (L::VI + NW - 1) / NW;
   // one array per buffer: the LDS copies into one buffer then provably do not alias the reads of
   // the other, so the reads wait for nothing but their own data
@@ -264,15 +273,19 @@ __launch_bounds__(NW * 64) void fwd_kernel(
         if (kbase + 32 + key_of_reg(r, hi) > lim) sc1[r] = kNegInf;
       }
     }
-    // row maximum: two independent v_max3 chains over the 32 scores of the lane
-    float ma = fmaxf(fmaxf(sc0[0], sc0[1]), sc0[2]), mb = fmaxf(fmaxf(sc1[0], sc1[1]), sc1[2]);
+    // Softmax of the tile against the running reference m_run (log2 units of the scaled scores).
+    // row_max: two independent v_max3 chains over the 32 scores of the lane
+    auto row_max = [&]() {
+      float ma = fmaxf(fmaxf(sc0[0], sc0[1]), sc0[2]), mb = fmaxf(fmaxf(sc1[0], sc1[1]), sc1[2]);
 #pragma unroll
-    for (int r = 3; r < 15; r += 2) {
-      ma = fmaxf(fmaxf(ma, sc0[r]), sc0[r + 1]);
-      mb = fmaxf(fmaxf(mb, sc1[r]), sc1[r + 1]);
-    }
-    const float mx = halves_max(fmaxf(fmaxf(ma, sc0[15]), fmaxf(mb, sc1[15]))) * cs;
-    if (__any(mx > m_run + kRescaleSlack)) {
+      for (int r = 3; r < 15; r += 2) {
+        ma = fmaxf(fmaxf(ma, sc0[r]), sc0[r + 1]);
+        mb = fmaxf(fmaxf(mb, sc1[r]), sc1[r + 1]);
+      }
+      return halves_max(fmaxf(fmaxf(ma, sc0[15]), fmaxf(mb, sc1[15]))) * cs;
+    };
+    // move the reference up to mx (a no-op for rows already at or above it)
+    auto rescale_to = [&](float mx) {
       // finite for every row that sees a key: key 0 of tile 0 is visible to all of them
       const float m_new = fmaxf(m_run, mx);
       // a row that has seen no key yet has nothing to rescale; with per-sequence lengths it may
@@ -285,29 +298,58 @@ __launch_bounds__(NW * 64) void fwd_kernel(
       for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    };
+    // probabilities p = exp2(cs s - m) into p0/p1 (may alias sc0/sc1); returns the lane's sum
+    auto probs = [&](f32x16& p0, f32x16& p1) {
+      // a row that sees no key at all (possible only with per-sequence lengths or a bias) keeps
+      // m = -inf; reference it to 0 so that its probabilities are exp2(-inf) = 0, not NaN
+      const float m_use = (GUARD && m_run == kNegInf) ? 0.f : m_run;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p0[r] = exp2_fast(__builtin_fmaf(sc0[r], cs, -m_use));
+        p1[r] = exp2_fast(__builtin_fmaf(sc1[r], cs, -m_use));
+      }
+      float ps[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ps[j] = p0[j] + p1[j];
+#pragma unroll
+      for (int r = 4; r < 16; ++r) ps[r & 3] += p0[r] + p1[r];
+      return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    };
+    f32x16 pa, pb;  // kLateMax: the probabilities (the scores stay for a second pass)
+    f32x16& p0 = kLateMax ? pa : sc0;
+    f32x16& p1 = kLateMax ? pb : sc1;
+    float ts;  // sum of the lane's probabilities of this tile
+    if constexpr (kLateMax) {
+      if constexpr (!kSB) qk(sn0, sn1, P ? kb0 : kb1);
+      // No row maximum on the common path: the exponentials are taken against m_run as it is,
+      // and the tile is redone after a rescale only when some lane's sum leaves [0, 2^slack]
+      // (so no probability exceeds 2^slack) or is not finite (m_run = -inf before the first
+      // visit), or when a row without a reference meets its first finite score. On the first
+      // tile the maximum is taken up front.
+      bool again = t == 0;
+      if (!again) {
+        ts = probs(pa, pb);
+        again = __any(!(ts <= kTileSumMax) || (GUARD && m_run == kNegInf && ts > 0.f));
+      }
+      if (again) {
+        rescale_to(row_max());
+        ts = probs(pa, pb);
+      }
+    } else {
+      const float mx = row_max();
+      if (__any(mx > m_run + kRescaleSlack)) rescale_to(mx);
+      // Issued unconditionally so that it shares a basic block with the softmax below; past the
+      // last tile it reads stale (in-bounds) LDS and its result is never used.
+      if constexpr (!kSB) qk(sn0, sn1, P ? kb0 : kb1);
+      ts = probs(sc0, sc1);
     }
-    // Issued unconditionally so that it shares a basic block with the softmax below; past the
-    // last tile it reads stale (in-bounds) LDS and its result is never used.
-    if constexpr (!kSB) qk(sn0, sn1, P ? kb0 : kb1);
-    // a row that sees no key at all (possible only with per-sequence lengths) keeps m = -inf;
-    // reference it to 0 so that its probabilities are exp2(-inf) = 0, not NaN
-    const float m_use = (GUARD && m_run == kNegInf) ? 0.f : m_run;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc0[r] = exp2_fast(__builtin_fmaf(sc0[r], cs, -m_use));
-      sc1[r] = exp2_fast(__builtin_fmaf(sc1[r], cs, -m_use));
-    }
-    float ps[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ps[j] = sc0[j] + sc1[j];
-#pragma unroll
-    for (int r = 4; r < 16; ++r) ps[r & 3] += sc0[r] + sc1[r];
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    l_run += ts;
     bf16x8 pf[4];
-    pf[0] = pack_bf16x8(sc0[0], sc0[1], sc0[2], sc0[3], sc0[4], sc0[5], sc0[6], sc0[7]);
-    pf[1] = pack_bf16x8(sc0[8], sc0[9], sc0[10], sc0[11], sc0[12], sc0[13], sc0[14], sc0[15]);
-    pf[2] = pack_bf16x8(sc1[0], sc1[1], sc1[2], sc1[3], sc1[4], sc1[5], sc1[6], sc1[7]);
-    pf[3] = pack_bf16x8(sc1[8], sc1[9], sc1[10], sc1[11], sc1[12], sc1[13], sc1[14], sc1[15]);
+    pf[0] = pack_bf16x8(p0[0], p0[1], p0[2], p0[3], p0[4], p0[5], p0[6], p0[7]);
+    pf[1] = pack_bf16x8(p0[8], p0[9], p0[10], p0[11], p0[12], p0[13], p0[14], p0[15]);
+    pf[2] = pack_bf16x8(p1[0], p1[1], p1[2], p1[3], p1[4], p1[5], p1[6], p1[7]);
+    pf[3] = pack_bf16x8(p1[8], p1[9], p1[10], p1[11], p1[12], p1[13], p1[14], p1[15]);
     lq_run = sum_bf16x8(pf[3], sum_bf16x8(pf[2], sum_bf16x8(pf[1], sum_bf16x8(pf[0], lq_run))));
     if constexpr (DROP) {
       // pf[st] holds keys kbase + 16 st + 8 hi + 0..7: one generator call each

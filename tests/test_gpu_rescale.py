@@ -5,7 +5,10 @@ first key block, so these cases force it:
 
 * rising keys (inputs.rising_keys): Q's column 0 is 3 and K's column 0 grows linearly with the key
   index, so every query's scores grow along the keys and its maximum rises on every 64-key block,
-  by 3 or by 12 in log2 units per block (below and above the forward's rescale threshold of 8);
+  by 3 or by 12 in log2 units per block. The forward moves its reference when a lane's
+  probabilities of a block sum past 2^8 (or, in the forms that take the maximum first, when the
+  maximum passes the reference by 8): with 3 per block that happens every second or third block,
+  before any single probability reaches 2^8, with 12 on every block;
 * a peaked softmax: iid inputs at scale 1 with d = 128 (score standard deviation about 11, in
   log2 units about 16), where the maximum jumps by large, irregular amounts. O is then close to
   single V rows, so V is scaled by 1/4 (exactly, in bf16): at |O| >= 2.5 the bf16 step of O alone
