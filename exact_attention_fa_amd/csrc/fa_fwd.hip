@@ -73,19 +73,20 @@ struct FwdLds {
 // G: query heads per K/V head (grouped-query attention; 1 unless asked otherwise): query head bh
 // reads K/V head bh / G, K and V holding BH / G heads.
 // d = d_v = 64 without dropout or a bias: one buffer of scores (the next tile's S^T is formed after
-// this tile's P is packed, over its scores) fits the kernel in 128 VGPRs, so four waves share each
-// SIMD (four 4-wave workgroups per CU) and the softmax of one wave hides under the products of the
-// others. At d = 64 the softmax's share of the work is twice that of d = 128, and four such waves
+// this tile's P is packed, over its scores) fits the kernel in 168 VGPRs, so three waves share each
+// SIMD (three 4-wave workgroups per CU) and the softmax of one wave hides under the products of
+// the others. At d = 64 the softmax's share of the work is twice that of d = 128, and such waves
 // beat two that each overlap the next tile's products with their own softmax (measured causal
-// B1 H64 N32768 d64: 9.36 against 9.95 ms). At d = 128 the same form with three waves per SIMD
-// (12-wave workgroups, 162 VGPRs) is slower than two double-buffered waves (0.560 against
-// 0.514 ms, causal B2 H16 N8192).
+// B1 H64 N32768 d64: 9.36 against 9.95 ms with four waves of 128 VGPRs, which take the row
+// maximum first; three waves that take it late, 9.02 against 9.19 ms for those four). At d = 128
+// the same form with three waves per SIMD (12-wave workgroups, 162 VGPRs) is slower than two
+// double-buffered waves (0.560 against 0.514 ms, causal B2 H16 N8192).
 template <int D, int DV, bool DROP, bool BIAS>
 constexpr bool kOneScoreBuffer = D == 64 && DV == 64 && !DROP && !BIAS;
 
 template <int D, int DV, int NW, bool CAUSAL, bool VL, bool DROP, bool BIAS>
-__global__ __attribute__((amdgpu_waves_per_eu(kOneScoreBuffer<D, DV, DROP, BIAS> ? 4 : 2,
-                                               kOneScoreBuffer<D, DV, DROP, BIAS> ? 4 : 2)))
+__global__ __attribute__((amdgpu_waves_per_eu(kOneScoreBuffer<D, DV, DROP, BIAS> ? 3 : 2,
+                                               kOneScoreBuffer<D, DV, DROP, BIAS> ? 3 : 2)))
 __launch_bounds__(NW * 64) void fwd_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int* __restrict__ lens_q,
@@ -96,9 +97,9 @@ __launch_bounds__(NW * 64) void fwd_kernel(
   constexpr int BR = NW * 32;  // query rows per workgroup
   constexpr bool kSB = kOneScoreBuffer<D, DV, DROP, BIAS>;
   // the row maximum only when the tile's sums call for it: the scores then stay live beside the
-  // probabilities, which the one-score-buffer form has no registers for, and which would push
-  // the bias and the lengths-with-dropout forms into scratch memory
-  constexpr bool kLateMax = !kSB && !BIAS && !(VL && DROP);
+  // probabilities, which would push the bias and the lengths-with-dropout forms into scratch
+  // memory
+  constexpr bool kLateMax = !BIAS && !(VL && DROP);
   constexpr int KIW = (L::KI + NW - 1) / NW, VIW = (L::VI + NW - 1) / NW;
   // one array per buffer: the LDS copies into one buffer then provably do not alias the reads of
   // the other, so the reads wait for nothing but their own data
@@ -448,7 +449,7 @@ hipError_t launch(const FwdArgs& a) {
 template <int D, bool VL, bool DROP, bool BIAS, int DV = D>
 hipError_t launch_d(const FwdArgs& a) {
   const long long tiles = (long long)a.B * a.H * ((a.Nq + 255) / 256);
-  if constexpr (kOneScoreBuffer<D, DV, DROP, BIAS>) {  // four 4-wave workgroups per CU
+  if constexpr (kOneScoreBuffer<D, DV, DROP, BIAS>) {  // three 4-wave workgroups per CU
     return a.causal ? launch<D, DV, 4, true, VL, DROP, BIAS>(a)
                     : launch<D, DV, 4, false, VL, DROP, BIAS>(a);
   } else {
