@@ -16,7 +16,8 @@
 // Kernels.
 //   * fp8_prep_kernel: one workgroup per 64 rows of Q, of K, or of V of one head. For Q and K it
 //     applies the signs and the fast Walsh-Hadamard butterfly in fp32 (spans 1, 2, 4 inside a
-//     lane's 8 values, then lane distances 1 .. d/16 by shuffles), multiplies by 1/sqrt(d),
+//     lane's 8 values, then lane distances 1 .. d/16 by DPP moves inside the row's 16 or 8
+//     lanes), multiplies by 1/sqrt(d),
 //     reduces the block maxima, writes the scales and the E4M3 codes. For V it only writes the
 //     block's max |x| (the head scale needs all of them).
 //   * fp8_prep_v_kernel: one workgroup per 64 keys of one head: the head scale from the partial
@@ -76,6 +77,28 @@ __device__ __forceinline__ void scale_by_reciprocal(const float (&x)[8], float s
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = clamp_fp8(x[e] * r);
   }
+}
+
+// The value of the lane whose index differs from this lane's in bit DIST (1, 2, 4 or 8), inside
+// each row of 16 lanes, by DPP moves (no LDS traffic): quad permutations for 1 and 2; for 4 the
+// mirror inside each 8 lanes (index ^ 7) and then the quad permutation index ^ 3; for 8 the
+// rotation of the row by 8.
+template <int DIST>
+__device__ __forceinline__ float lane_xor(float x) {
+  const int v = __float_as_int(x);
+  int r;
+  if constexpr (DIST == 1) {
+    r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);  // quad_perm [1, 0, 3, 2]
+  } else if constexpr (DIST == 2) {
+    r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);  // quad_perm [2, 3, 0, 1]
+  } else if constexpr (DIST == 4) {
+    const int m = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true);  // row_half_mirror
+    r = __builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true);             // quad_perm [3, 2, 1, 0]
+  } else {
+    static_assert(DIST == 8, "lane distances 1, 2, 4, 8");
+    r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);  // row_ror:8
+  }
+  return __int_as_float(r);
 }
 
 // max over the 256 threads of a workgroup (all threads must call it)
@@ -145,12 +168,17 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(
           }
       // spans 8 .. D/2: lane distance 1 .. TPR/2 inside the row's lane group; the upper lane
       // of a pair takes o - x, the lower x + o, both as one exactly rounded fma(x, +-1, o)
-#pragma unroll
-      for (int dist = 1; dist < TPR; dist *= 2) {
+      auto lane_stage = [&](auto DIST) {
+        constexpr int dist = decltype(DIST)::value;
         const float sg = (chunk & dist) ? -1.f : 1.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[p][e] = fmaf(x[p][e], sg, __shfl_xor(x[p][e], dist));
-      }
+        for (int e = 0; e < 8; ++e) x[p][e] = fmaf(x[p][e], sg, lane_xor<dist>(x[p][e]));
+      };
+      static_assert(TPR == 8 || TPR == 16, "rows of 8 or 16 lanes");
+      lane_stage(std::integral_constant<int, 1>());
+      lane_stage(std::integral_constant<int, 2>());
+      lane_stage(std::integral_constant<int, 4>());
+      if constexpr (TPR == 16) lane_stage(std::integral_constant<int, 8>());
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[p][e] *= inv_sqrt_d;
     }
