@@ -342,7 +342,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
     {
       const bool b = tx & 4;
       const uint32_t s0 = b ? w[0] : w[2], s1 = b ? w[1] : w[3];
-      const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 4), r1 = (uint32_t)__shfl_xor((int)s1, 4);
+      const uint32_t r0 = lane_xor<4>(s0), r1 = lane_xor<4>(s1);
       if (b) { w[0] = r0; w[1] = r1; } else { w[2] = r0; w[3] = r1; }
     }
     // now word 2 a + m holds rows (lane's row with bit 2 = a), columns 4 (tx >> 2) + 2 m, + 1
@@ -350,7 +350,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
     {
       const bool b = tx & 2;
       const uint32_t s0 = b ? w[0] : w[1], s1 = b ? w[2] : w[3];
-      const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 2), r1 = (uint32_t)__shfl_xor((int)s1, 2);
+      const uint32_t r0 = lane_xor<2>(s0), r1 = lane_xor<2>(s1);
       if (b) { w[0] = r0; w[2] = r1; } else { w[1] = r0; w[3] = r1; }
     }
     // now word 2 a + c holds rows (bit 2 = a, bit 1 = c, bit 0 = tx & 1), columns
@@ -362,7 +362,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(kNT) voi
                           : __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);  // hi halves
     const uint32_t s1 = b ? __builtin_amdgcn_perm(w[3], w[2], 0x05040100u)
                           : __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
-    const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 1), r1 = (uint32_t)__shfl_xor((int)s1, 1);
+    const uint32_t r0 = lane_xor<1>(s0), r1 = lane_xor<1>(s1);
     // r0 = (partner's half for word 0, for word 1), r1 likewise for words 2, 3: rows with bit 0
     // = 1 - b. Word m of the result: rows 2 m (low half) and 2 m + 1 (high half).
     u32x4 o;

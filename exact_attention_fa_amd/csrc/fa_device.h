@@ -269,6 +269,32 @@ __device__ __forceinline__ uint32_t bias_ld2(__amdgpu_buffer_rsrc_t r, int byte_
 // above) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// The value of the lane whose index differs from this lane's in bit DIST (1, 2, 4 or 8), inside
+// each row of 16 lanes, by DPP moves (no LDS traffic): quad permutations for 1 and 2; for 4 the
+// mirror inside each 8 lanes (index ^ 7) and then the quad permutation index ^ 3; for 8 the
+// rotation of the row by 8.
+template <int DIST>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+  const int v = (int)x;
+  int r;
+  if constexpr (DIST == 1) {
+    r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);  // quad_perm [1, 0, 3, 2]
+  } else if constexpr (DIST == 2) {
+    r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);  // quad_perm [2, 3, 0, 1]
+  } else if constexpr (DIST == 4) {
+    const int m = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true);  // row_half_mirror
+    r = __builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true);             // quad_perm [3, 2, 1, 0]
+  } else {
+    static_assert(DIST == 8, "lane distances 1, 2, 4, 8");
+    r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);  // row_ror:8
+  }
+  return (uint32_t)r;
+}
+template <int DIST>
+__device__ __forceinline__ float lane_xor(float x) {
+  return __uint_as_float(lane_xor<DIST>(__float_as_uint(x)));
+}
+
 // ---- dropout on the probabilities ------------------------------------------------------------
 // The mask is never stored: every kernel that needs it regenerates it from a counter-based
 // generator (the seed-and-offset scheme of "Maskeleme ve Dropout"). Generator: Philox-4x32-10

@@ -79,28 +79,6 @@ __device__ __forceinline__ void scale_by_reciprocal(const float (&x)[8], float s
   }
 }
 
-// The value of the lane whose index differs from this lane's in bit DIST (1, 2, 4 or 8), inside
-// each row of 16 lanes, by DPP moves (no LDS traffic): quad permutations for 1 and 2; for 4 the
-// mirror inside each 8 lanes (index ^ 7) and then the quad permutation index ^ 3; for 8 the
-// rotation of the row by 8.
-template <int DIST>
-__device__ __forceinline__ float lane_xor(float x) {
-  const int v = __float_as_int(x);
-  int r;
-  if constexpr (DIST == 1) {
-    r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);  // quad_perm [1, 0, 3, 2]
-  } else if constexpr (DIST == 2) {
-    r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);  // quad_perm [2, 3, 0, 1]
-  } else if constexpr (DIST == 4) {
-    const int m = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true);  // row_half_mirror
-    r = __builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true);             // quad_perm [3, 2, 1, 0]
-  } else {
-    static_assert(DIST == 8, "lane distances 1, 2, 4, 8");
-    r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);  // row_ror:8
-  }
-  return __int_as_float(r);
-}
-
 // max over the 256 threads of a workgroup (all threads must call it)
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
