@@ -34,7 +34,7 @@
 //     value, and every probability stays at most 2^kRescaleSlack. In most forms no row maximum is
 //     taken on the common path: the exponentials are taken against m as it stands, and only when
 //     some lane's sum of the tile exceeds 2^kRescaleSlack (or on the first tile) is the maximum
-//     taken, m moved and the tile redone. The other forms take the maximum first and move m when
+//     taken, m moved and the tile redone. The bias form takes the maximum first and moves m when
 //     a row would exceed it by more than kRescaleSlack (log2 units).
 //   * O is normalised by the sum of the same bf16 probabilities that feed the PV product, so it is
 //     an exact convex combination of V rows under the rounded weights; the log-sum-exp keeps the
@@ -97,9 +97,8 @@ __launch_bounds__(NW * 64) void fwd_kernel(
   constexpr int BR = NW * 32;  // query rows per workgroup
   constexpr bool kSB = kOneScoreBuffer<D, DV, DROP, BIAS>;
   // the row maximum only when the tile's sums call for it: the scores then stay live beside the
-  // probabilities, which would push the bias and the lengths-with-dropout forms into scratch
-  // memory
-  constexpr bool kLateMax = !BIAS && !(VL && DROP);
+  // probabilities, which would push the bias form into scratch memory
+  constexpr bool kLateMax = !BIAS;
   constexpr int KIW = (L::KI + NW - 1) / NW, VIW = (L::VI + NW - 1) / NW;
   // one array per buffer: the LDS copies into one buffer then provably do not alias the reads of
   // the other, so the reads wait for nothing but their own data
