@@ -151,3 +151,37 @@ def test_rescale_decode_paged(gpu, kind, heads):
     o_ref, l_ref = oracle.decode_paged(f(q16), f(kc), f(vc), table, sl, scale)
     assert_fwd_close(from_dev(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref,
                      f"paged decode {kind} H{H} H_kv{H_kv}")
+
+
+@pytest.mark.parametrize("kind", ["rise3", "rise12", "peaked"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_rescale_fwd_ext(gpu, kind, d):
+    """The same moving maxima through fwd_ext with per-sequence lengths, 2 query heads per K/V
+    head and dropout p = 0.2 (the lengths-with-dropout form of the forward), causal, against
+    the oracle's forward_combined; padding rows and keys hold NaN. On the rising keys O is
+    close to the last keys' V rows times 1/(1 - p) = 1.25, up to |O| = 4.6, where one bf16 step
+    of O (2^-5) exceeds the O bar, so V is quartered there too (exactly, and V plays no part in
+    the row maximum)."""
+    import torch
+    import oracle.combined as OC
+    B, H, H_kv, n = 2, 4, 2, 700
+    lens = np.array([700, 450], dtype=np.int32)
+    (q16, k16, v16, _), scale = make_case(kind, 470 + d, B, H, n, n, d)
+    k16, v16 = k16[:, :H_kv].copy(), v16[:, :H_kv].copy()
+    if kind != "peaked":  # (make_case quarters V of the peaked case already)
+        v16 = quarter(v16)
+    q16 = inputs.fill_padding(q16, lens)
+    k16, v16 = inputs.fill_padding(k16, lens), inputs.fill_padding(v16, lens)
+    lq = torch.from_numpy(lens).cuda()
+    o, lse = gpu.fwd_ext(to_dev(q16), to_dev(k16), to_dev(v16), lq, lq, 0.2, 0xACE, 3,
+                         causal=True, scale=scale)
+    torch.cuda.synchronize()
+    f = inputs.bf16_to_f64
+    o_ref, l_ref = OC.forward_combined(f(q16), f(k16), f(v16), lens, lens, scale, True, 0.2,
+                                       0xACE, 3)
+    o_h, l_h = from_dev(o), lse.cpu().numpy().astype(np.float64)
+    live = ~np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(l_h), ~live), f"{kind} d{d}: rows with lse = -inf differ"
+    assert np.all(o_h[~live] == 0.0), f"{kind} d{d}: empty rows not zero"
+    assert_fwd_close(o_h[live], l_h[live], o_ref[live], l_ref[live], f"fwd_ext {kind} d{d}")
+
