@@ -185,3 +185,41 @@ def test_rescale_fwd_ext(gpu, kind, d):
     assert np.all(o_h[~live] == 0.0), f"{kind} d{d}: empty rows not zero"
     assert_fwd_close(o_h[live], l_h[live], o_ref[live], l_ref[live], f"fwd_ext {kind} d{d}")
 
+
+@pytest.mark.parametrize("kind", ["rise3", "rise12", "peaked"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rescale_bias(gpu, kind, causal):
+    """The bias form of the forward (the one that takes the row maximum first and moves the
+    reference when a row passes it by more than 8) under moving maxima: on iid inputs a bias that
+    rises along the keys by 3 or 12 log2 units per 64-key block, and a peaked softmax (scale 1,
+    d = 128, V quartered) under an iid 2 N(0, 1) bias; forward and gradients against the oracle
+    (K is not ramped here, so dQ keeps the plain bar)."""
+    import torch
+    B, H, n_q, n_k, d = 1, 2, 500, 700, 128
+    q16, k16, v16, do16 = inputs.qkv_bf16(480, B, H, n_q, n_k, d, with_do=True)
+    if kind == "peaked":
+        scale = 1.0
+        v16 = quarter(v16)
+        g = np.random.default_rng(480)
+        bias = (2 * g.standard_normal((1, H, n_q, n_k))).astype(np.float32)
+    else:
+        scale = default_scale(d)
+        rise = {"rise3": 3.0, "rise12": 12.0}[kind]
+        ramp = np.arange(n_k) * (rise / 64.0) / LOG2E  # natural-log units of the scores
+        bias = np.broadcast_to(ramp, (1, H, n_q, n_k)).astype(np.float32)
+    b16 = inputs.bf16_round(np.ascontiguousarray(bias))
+    q, k, v, do, b = (to_dev(x) for x in (q16, k16, v16, do16, b16))
+    o, lse = gpu.fwd_bias(q, k, v, b, causal=causal, scale=scale)
+    grads = gpu.bwd_bias(q, k, v, o, lse, do, b, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    f = inputs.bf16_to_f64
+    o_ref, l_ref = oracle.forward_bias(f(q16), f(k16), f(v16), f(b16), scale, causal)
+    what = f"bias {kind} causal {causal}"
+    assert_fwd_close(from_dev(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, what)
+    ref = oracle.backward_bias(f(q16), f(k16), f(v16), f(do16), f(b16), scale, causal)
+    for name, g_, r in zip(("dQ", "dK", "dV"), grads, ref):
+        g_ = from_dev(g_)
+        assert np.all(np.isfinite(g_)), f"{what}: non-finite {name}"
+        e = rel_fro(g_, r)
+        assert e <= GRAD_REL_FRO, f"{what}: {name} relative Frobenius error {e:.3e}"
+
